@@ -1,0 +1,365 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle.
+
+Each ``check_*`` raises AssertionError when the oracle disagrees with:
+exact rational arithmetic, brute-force enumeration, closed forms, PyTorch's
+scaled_dot_product_attention (a library routine) or an independent
+token-mask formulation.  The checks look the oracle's functions up on the
+module at call time, so the mutation tests can swap one of them for a
+plausible mistake and see a check fail.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import torch
+import torch.nn.functional as F
+
+import oracle.sparse_attention as ra
+import workloads
+from _exact import exact_block_means, exact_scores
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _np(x):
+    return x.float().numpy()
+
+
+def _sdpa(q, k, v, mask=None, scale=None):
+    """Reference attention over [B, T, H, D] numpy arrays, float64, CPU."""
+    t = lambda x: torch.from_numpy(np.asarray(x, dtype=np.float64)).permute(0, 2, 1, 3)
+    m = None if mask is None else torch.from_numpy(np.asarray(mask, dtype=np.float64))
+    o = F.scaled_dot_product_attention(t(q), t(k), t(v), attn_mask=m,
+                                       scale=scale if scale else 1.0 / math.sqrt(q.shape[-1]))
+    return o.permute(0, 2, 1, 3).numpy()
+
+
+def _bits(a):
+    return np.asarray(a, dtype=np.float32).view(np.uint32)
+
+
+def _varied_bf16(shape, seed):
+    """bf16 values spread over many binades (stresses exact summation)."""
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn(*shape, generator=g) * torch.exp2(torch.randint(-12, 4, shape, generator=g).float())
+    return x.to(torch.bfloat16)
+
+
+# ---------------------------------------------------------------- pooling ---
+
+def check_pool_exact():
+    x = _np(_varied_bf16((1, 256, 2, 128), seed=11))
+    got = ra.pool_means(x, 4)
+    want = exact_block_means(x, 4)
+    assert got.dtype == np.float32 and got.shape == (1, 2, 4, 128)
+    assert np.array_equal(_bits(got), _bits(want)), "pooled means are not the correctly rounded exact means"
+
+
+def check_pool_permutation_invariant():
+    x = _np(_varied_bf16((1, 320, 3, 128), seed=12))
+    rng = np.random.default_rng(5)
+    y = x.copy()
+    for i in range(5):
+        perm = rng.permutation(64) + 64 * i
+        y[:, 64 * i:64 * i + 64] = x[:, perm]
+    assert np.array_equal(_bits(ra.pool_means(x, 5)), _bits(ra.pool_means(y, 5)))
+
+
+# ----------------------------------------------------------------- scores ---
+
+def check_scores_exact():
+    x = _np(_varied_bf16((1, 384, 2, 128), seed=13))
+    z = _np(_varied_bf16((1, 384, 2, 128), seed=14))
+    qbar = exact_block_means(x, 6)
+    kbar = exact_block_means(z, 6)
+    got = ra.route_scores(qbar, kbar)
+    want = exact_scores(qbar, kbar)
+    assert got.dtype == np.float32 and got.shape == (1, 2, 6, 6)
+    assert np.array_equal(_bits(got), _bits(want)), "scores are not fp32 of the exact dot products"
+
+
+# ----------------------------------------------------------------- budget ---
+
+def check_budget():
+    # closed forms of ceil(ratio * NVB) for the workloads' sizes
+    f = ra.topk_budget
+    assert f(16, 0.25) == 4
+    assert f(128, 0.1) == 13
+    assert f(144, 0.1) == 15
+    assert f(512, 0.1) == 52
+    assert f(30, 0.1) == 3          # 0.1*30 is 3.0000000000000004 in double
+    assert f(10, 0.1) == 1
+    assert f(144, 1.0) == 144
+    assert f(7, 1e-4) == 1          # at least one routed block
+    assert f(0, 0.1) == 0
+    for bad in (0.0, -0.5, 1.5):
+        try:
+            f(10, bad)
+        except ValueError:
+            pass
+        else:
+            raise AssertionError("invalid ratio accepted")
+
+
+# -------------------------------------------------------------- selection ---
+
+def _brute_topk(scores, cand, k):
+    """The unique k-subset whose every member beats every non-member under
+    (score descending, index ascending)."""
+    def beats(a, b):
+        return scores[a] > scores[b] or (scores[a] == scores[b] and a < b)
+    found = []
+    for sub in itertools.combinations(cand, k):
+        s = set(sub)
+        rest = [b for b in cand if b not in s]
+        if all(beats(a, b) for a in sub for b in rest):
+            found.append(sorted(sub))
+    assert len(found) == 1, "brute force must find exactly one subset"
+    return found[0]
+
+
+def check_topk_bruteforce():
+    rng = np.random.default_rng(21)
+    for nvb in range(1, 9):
+        for radius in (0, 1, 2):
+            for ratio in (0.1, 0.3, 0.5, 1.0):
+                nb = nvb + int(rng.integers(0, 3))
+                budget = ra.topk_budget(nvb, ratio)
+                # coarse values -> many exact ties; include signed zeros
+                row_vals = rng.integers(-3, 4, size=nvb).astype(np.float32)
+                row_vals[row_vals == 0] = np.where(rng.random((row_vals == 0).sum()) < 0.5, -0.0, 0.0)
+                for i in range(nvb):
+                    sel = ra.select_row(row_vals, i, nvb, nb, budget, radius)
+                    forced = [j for j in range(nvb) if abs(j - i) <= radius]
+                    cand = [j for j in range(nvb) if j not in forced]
+                    k = min(budget, len(cand))
+                    want = _brute_topk({j: float(row_vals[j]) for j in cand}, cand, k) if k else []
+                    assert sel.routed == want, (nvb, radius, ratio, i, sel.routed, want)
+                    assert sel.forced == forced
+                    assert sel.blocks == sorted(set(want) | set(forced) | set(range(nvb, nb)))
+
+
+def check_signed_zero_tie():
+    row = np.array([5.0, -0.0, 0.0, -1.0], dtype=np.float32)
+    # i=0, radius 0: candidates 1,2,3; budget 1 -> -0.0 and +0.0 tie, index 1 wins
+    sel = ra.select_row(row, 0, 4, 4, 1, 0)
+    assert sel.routed == [1]
+    row2 = np.array([5.0, 0.0, -0.0, -1.0], dtype=np.float32)
+    assert ra.select_row(row2, 0, 4, 4, 1, 0).routed == [1]
+
+
+def check_near_tie_flag():
+    budget = ra.topk_budget(6, 1.0 / 3.0)
+    assert budget == 2
+    tied = np.array([9.0, 3.0, 1.0, np.float32(1.0000001), -2.0, 0.5], dtype=np.float32)
+    sel = ra.select_row(tied, 0, 6, 6, budget, 0)
+    assert sel.routed == [1, 3] and sel.near_tie
+    lo, hi = sel.band
+    assert lo <= 1.0 <= hi and lo <= float(np.float32(1.0000001)) <= hi and hi < 1.001
+    apart = np.array([9.0, 3.0, 1.0, 1.5, -2.0, 0.5], dtype=np.float32)
+    sel2 = ra.select_row(apart, 0, 6, 6, budget, 0)
+    assert sel2.routed == [1, 3] and not sel2.near_tie
+
+
+def check_list_structure():
+    rng = np.random.default_rng(22)
+    nvb, nb = 20, 24
+    for radius in (0, 1, 2):
+        for ratio in (0.1, 0.25, 1.0):
+            budget = ra.topk_budget(nvb, ratio)
+            row = rng.standard_normal(nvb).astype(np.float32)
+            for i in range(nvb):
+                sel = ra.select_row(row, i, nvb, nb, budget, radius)
+                S = sel.blocks
+                F_ = [j for j in range(max(0, i - radius), min(nvb, i + radius + 1))]
+                assert set(F_) <= set(S) and set(range(nvb, nb)) <= set(S)
+                assert all(a < b for a, b in zip(S, S[1:]))
+                assert not (set(sel.routed) & set(F_))
+                k = min(budget, nvb - len(F_))
+                assert len(S) == k + len(F_) + (nb - nvb)
+                assert len(S) <= ra.max_selected(nb * 64, nvb * 64, ratio, radius)
+
+
+def check_route_glue():
+    """route() = pool(Q), pool(K), score(qbar, kbar), select - against the
+    exact rational path and the brute-force selection."""
+    q, k, _ = workloads.random_qkv(1, 448, 2, seed=23)
+    q, k = _np(q), _np(k)
+    rt = ra.route(q, k, sink_start=420, ratio=0.34, radius=1)
+    nvb = 6
+    assert (rt.nb, rt.nvb) == (7, nvb)
+    s = exact_scores(exact_block_means(q, nvb), exact_block_means(k, nvb))
+    budget = ra.topk_budget(nvb, 0.34)
+    for h in range(2):
+        for i in range(nvb):
+            forced = [j for j in range(nvb) if abs(j - i) <= 1]
+            cand = [j for j in range(nvb) if j not in forced]
+            want = _brute_topk({j: float(s[0, h, i, j]) for j in cand}, cand, min(budget, len(cand)))
+            assert rt.rows[0][h][i].routed == want
+            assert rt.rows[0][h][i].blocks == sorted(set(want) | set(forced) | {6})
+
+
+# -------------------------------------------------------------- attention ---
+
+def _case(T, H, seed, sink_start):
+    q, k, v = workloads.random_qkv(1, T, H, seed=seed)
+    return _np(q), _np(k), _np(v), sink_start
+
+
+def _sink_bias_mask(T, nvb, bias):
+    m = np.zeros((T, T))
+    if bias is not None:
+        kb = np.asarray(bias, dtype=np.float64).reshape(-1)[:T].copy()
+        kb[: nvb * 64] = 0.0
+        m = m + kb[None, :]
+    return m
+
+
+def check_ratio_one_equals_sdpa():
+    q, k, v, ss = _case(200, 2, 31, 150)          # NVB=2, split video block, partial last block
+    bias = workloads.sink_key_bias(1, 200, ss, seed=32).numpy()
+    out, lse, rt = ra.routed_attention(q, k, v, ss, 1.0, 0, key_bias=bias)
+    want = _sdpa(q, k, v, mask=_sink_bias_mask(200, rt.nvb, bias)[None, None])
+    assert np.abs(out - want).max() < 1e-12
+    # natural-log LSE against torch.logsumexp of the biased, scaled logits
+    qt = torch.from_numpy(q.astype(np.float64))
+    kt = torch.from_numpy(k.astype(np.float64))
+    logits = torch.einsum("bthd,bshd->bhts", qt, kt) / math.sqrt(128) + torch.from_numpy(_sink_bias_mask(200, 2, bias))
+    assert np.abs(lse - torch.logsumexp(logits, dim=-1).numpy()).max() < 1e-10
+
+
+def check_all_dense_when_no_video_block():
+    q, k, v, ss = _case(150, 2, 33, 40)           # sink_start < 64 -> NVB = 0
+    out, _, rt = ra.routed_attention(q, k, v, ss, 0.1, 1)
+    assert rt.nvb == 0
+    assert np.abs(out - _sdpa(q, k, v)).max() < 1e-12
+
+
+def check_token_mask_path():
+    """Block lists expanded to a token mask over the dense score matrix."""
+    T, ss = 1000, 900                              # NVB=14, sinks {14, 15}, last block 40 keys
+    q, k, v, _ = _case(T, 2, 34, ss)
+    bias = workloads.sink_key_bias(1, T, ss, seed=35).numpy()
+    out, _, rt = ra.routed_attention(q, k, v, ss, 0.25, 1, key_bias=bias)
+    nvb = rt.nvb
+    mask = np.full((2, T, T), -np.inf)
+    for h in range(2):
+        for t in range(T):
+            if t < nvb * 64:
+                for j in rt.rows[0][h][t // 64].blocks:
+                    mask[h, t, j * 64:min(T, j * 64 + 64)] = 0.0
+            else:
+                mask[h, t, :] = 0.0
+    mask = mask + _sink_bias_mask(T, nvb, bias)[None]
+    want = _sdpa(q, k, v, mask=mask[None])
+    assert np.abs(out - want).max() < 1e-12
+
+
+def check_zero_bias_is_no_bias():
+    q, k, v, ss = _case(400, 2, 36, 300)
+    a, la, _ = ra.routed_attention(q, k, v, ss, 0.25, 0)
+    b, lb, _ = ra.routed_attention(q, k, v, ss, 0.25, 0, key_bias=np.zeros((1, 400), np.float32))
+    assert np.array_equal(a, b) and np.array_equal(la, lb)
+
+
+def check_bias_ln_m_duplicates_key():
+    """Bias ln(m) on a sink key weighs it like m copies of that key."""
+    T, ss, j0, m = 200, 128, 150, 3
+    q, k, v, _ = _case(T, 2, 37, ss)
+    bias = np.zeros((1, T), np.float32)
+    bias[0, j0] = np.float32(math.log(m))
+    out, _, _ = ra.routed_attention(q, k, v, ss, 1.0, 0, key_bias=bias)
+    extra = [j0] * (m - 1)
+    k2 = np.concatenate([k, k[:, extra]], axis=1)
+    v2 = np.concatenate([v, v[:, extra]], axis=1)
+    # fp32(ln 3) is ln 3 to 1e-8 relative, so the weights agree to ~1e-8
+    want = _sdpa(q, k2, v2)
+    assert np.abs(out - want).max() < 1e-6
+
+
+def check_bias_removes_key():
+    T, ss, j0 = 200, 128, 170
+    q, k, v, _ = _case(T, 2, 38, ss)
+    bias = np.zeros((1, T), np.float32)
+    bias[0, j0] = -1e4
+    out, _, _ = ra.routed_attention(q, k, v, ss, 1.0, 0, key_bias=bias)
+    keep = [j for j in range(T) if j != j0]
+    want = _sdpa(q, k[:, keep], v[:, keep])
+    assert np.abs(out - want).max() < 1e-12
+
+
+def check_bias_changes_output():
+    q, k, v, ss = _case(400, 2, 39, 300)
+    bias = workloads.sink_key_bias(1, 400, ss, seed=40).numpy()
+    a, _, _ = ra.routed_attention(q, k, v, ss, 0.25, 0)
+    b, _, _ = ra.routed_attention(q, k, v, ss, 0.25, 0, key_bias=bias)
+    assert np.abs(a - b).max() > 1e-3
+
+
+def check_bias_ignored_on_video_keys():
+    """Only the exact sink branch consumes the bias: a bias on video keys
+    leaves the output unchanged."""
+    q, k, v, ss = _case(400, 2, 41, 300)
+    bias = np.zeros((1, 400), np.float32)
+    bias[0, :256] = -1.5                               # blocks 0..3 are video blocks
+    a, _, _ = ra.routed_attention(q, k, v, ss, 0.25, 1)
+    b, _, _ = ra.routed_attention(q, k, v, ss, 0.25, 1, key_bias=bias)
+    assert np.array_equal(a, b)
+
+
+def check_constant_v():
+    q, k, v, ss = _case(330, 2, 42, 260)
+    v = np.full_like(v, 0.75)
+    out, _, _ = ra.routed_attention(q, k, v, ss, 0.2, 1)
+    assert np.abs(out - 0.75).max() < 1e-12
+
+
+def check_convex_hull():
+    T, ss = 330, 260
+    q, k, v, _ = _case(T, 2, 43, ss)
+    out, _, rt = ra.routed_attention(q, k, v, ss, 0.2, 1)
+    for h in range(2):
+        for t in range(T):
+            if t < rt.nvb * 64:
+                idx = np.concatenate([np.arange(j * 64, min(T, j * 64 + 64)) for j in rt.rows[0][h][t // 64].blocks])
+            else:
+                idx = np.arange(T)
+            vv = v[0, idx, h].astype(np.float64)
+            assert np.all(out[0, t, h] >= vv.min(0) - 1e-12) and np.all(out[0, t, h] <= vv.max(0) + 1e-12)
+
+
+def check_effective_flops_h3():
+    # H3: 144 video blocks, 5 sink blocks (the last has 33 keys), ratio 0.1 -> 15 routed + self
+    nvb, T, H = 144, 9505, 56
+    lists = [[[list(range(nvb - 1))[:15] + [nvb - 1] + list(range(144, 149))] * nvb for _ in range(H)]]
+    want = 4 * 128 * (H * nvb * 64 * (20 * 64 + 33) + H * (T - nvb * 64) * T)
+    assert want == 425_709_039_616
+    assert ra.effective_flops(T, H, 1, lists, nvb) == want
+
+
+def check_golden_pages_numbers():
+    with open(os.path.join(GOLDEN, "pages_numbers.json")) as f:
+        items = {it["name"]: it["value"] for it in json.load(f)["items"]}
+    assert ra.HEAD_DIM == items["head_dim"] and ra.BLOCK == items["block_tokens"]
+    T, H = items["h3_tokens"], items["h3_heads"]
+    # ~20 GB of scores for the dense matrix: fp32 [1, 56, 9505, 9505]
+    gb = T * T * H * 4 / 1e9
+    assert abs(gb - items["h3_dense_score_gigabytes"]) / items["h3_dense_score_gigabytes"] < 0.05
+    nb, nvb = ra.block_counts(T, 9 * 32 * 32)
+    assert (nb, nvb) == (T // 64 + 1, 144) and T % 64 == 33
+    assert len(ra.forced_blocks(10, nvb, 0)) == items["exact_radius_0_forced_blocks"]
+    assert len(ra.forced_blocks(10, nvb, 1)) == items["exact_radius_1_forced_blocks"]
+    assert ra.topk_budget(nvb, items["default_topk_ratio"]) == 15
+
+
+ALL_CHECKS = [
+    check_pool_exact, check_pool_permutation_invariant, check_scores_exact,
+    check_budget, check_topk_bruteforce, check_signed_zero_tie, check_near_tie_flag,
+    check_list_structure, check_route_glue, check_ratio_one_equals_sdpa,
+    check_all_dense_when_no_video_block, check_token_mask_path,
+    check_zero_bias_is_no_bias, check_bias_ln_m_duplicates_key, check_bias_removes_key,
+    check_bias_changes_output, check_bias_ignored_on_video_keys, check_constant_v,
+    check_convex_hull, check_effective_flops_h3, check_golden_pages_numbers,
+]

@@ -1,0 +1,156 @@
+"""Plant a plausible mistake in the oracle (on the CPU) and require that at
+least one pin fails.  Shows that the pins would catch a dropped term, a wrong
+sign, index or operand in each oracle function."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle.sparse_attention as ra
+import oracle_checks as oc
+
+_orig = {name: getattr(ra, name) for name in (
+    "pool_means", "route_scores", "topk_budget", "select_row", "attend",
+    "key_bias_vector", "sparse_block_output", "dense_rows_output", "forced_blocks",
+    "route")}
+
+
+def pool_63(x, nvb):                       # off-by-one block length
+    out = _orig["pool_means"](x, nvb)
+    x64 = np.asarray(x, np.float64)
+    for i in range(nvb):
+        out[:, :, i] = (x64[:, i * 64:i * 64 + 63].sum(1) / 64).astype(np.float32)
+    return out
+
+
+def pool_f32_sum(x, nvb):                  # accumulates in fp32 in token order
+    B, T, H, D = x.shape
+    out = np.zeros((B, H, nvb, D), np.float32)
+    for i in range(nvb):
+        acc = np.zeros((B, H, D), np.float32)
+        for t in range(i * 64, i * 64 + 64):
+            acc = acc + np.asarray(x[:, t], np.float32)
+        out[:, :, i] = acc / np.float32(64)
+    return out
+
+
+def scores_transposed(qbar, kbar):
+    return np.swapaxes(_orig["route_scores"](qbar, kbar), -1, -2).copy()
+
+
+def scores_bf16(qbar, kbar):
+    import torch
+    r = lambda a: torch.from_numpy(a).to(torch.bfloat16).float().numpy()
+    return _orig["route_scores"](r(qbar), r(kbar))
+
+
+def budget_floor(nvb, ratio):
+    if nvb <= 0:
+        return 0
+    return max(1, int(math.floor(float(np.float32(ratio)) * nvb)))
+
+
+def select_ascending(scores_row, i, nvb, nb, budget, radius):
+    return _orig["select_row"](-np.asarray(scores_row, np.float32), i, nvb, nb, budget, radius)
+
+
+def select_tie_high_index(scores_row, i, nvb, nb, budget, radius):
+    forced = ra.forced_blocks(i, nvb, radius)
+    cand = np.array([j for j in range(nvb) if j not in forced], np.int64)
+    k = min(budget, len(cand))
+    s = np.asarray(scores_row, np.float32)[cand]
+    order = np.lexsort((-cand, -s.astype(np.float64)))
+    routed = sorted(int(j) for j in cand[order[:k]])
+    sel = _orig["select_row"](scores_row, i, nvb, nb, budget, radius)
+    sel.routed = routed
+    sel.blocks = sorted(set(routed) | set(forced) | set(range(nvb, nb)))
+    return sel
+
+
+def select_forced_inside_budget(scores_row, i, nvb, nb, budget, radius):
+    s = np.asarray(scores_row, np.float32)
+    order = np.lexsort((np.arange(nvb), -s.astype(np.float64)))
+    top = sorted(int(j) for j in order[:budget])
+    forced = ra.forced_blocks(i, nvb, radius)
+    sel = _orig["select_row"](scores_row, i, nvb, nb, budget, radius)
+    sel.routed = [j for j in top if j not in forced]
+    sel.blocks = sorted(set(top) | set(forced) | set(range(nvb, nb)))
+    return sel
+
+
+def attend_no_scale(qrows, keys, vals, bias, scale):
+    return _orig["attend"](qrows, keys, vals, bias, 1.0)
+
+
+def attend_bias_sign(qrows, keys, vals, bias, scale):
+    return _orig["attend"](qrows, keys, vals, None if bias is None else -np.asarray(bias), scale)
+
+
+def attend_bias_log2(qrows, keys, vals, bias, scale):     # log2 units fed to a natural exp
+    return _orig["attend"](qrows, keys, vals, None if bias is None else np.asarray(bias) * math.log2(math.e), scale)
+
+
+def attend_values_are_keys(qrows, keys, vals, bias, scale):
+    return _orig["attend"](qrows, keys, keys, bias, scale)
+
+
+def bias_on_all_keys(key_bias, b, T, nvb):
+    if key_bias is None:
+        return None
+    return np.asarray(key_bias, np.float64).reshape(-1, T)[b].copy()
+
+
+def gather_shifted(q, k, v, b, h, i, blocks, key_bias=None, nvb=None, scale=None):
+    nb = -(-q.shape[1] // 64)
+    return _orig["sparse_block_output"](q, k, v, b, h, i, [min(j + 1, nb - 1) for j in blocks],
+                                        key_bias, nvb, scale)
+
+
+def dense_without_sinks(q, k, v, b, h, rows, key_bias=None, nvb=0, scale=None):
+    T = q.shape[1]
+    keys = np.arange(0, max(64 * nvb, 1))
+    kb = ra.key_bias_vector(key_bias, b, T, nvb)
+    return ra.attend(q[b, rows, h], k[b, keys, h], v[b, keys, h],
+                     None if kb is None else kb[keys], 1.0 / math.sqrt(128))
+
+
+def forced_one_sided(i, nvb, radius):
+    return [j for j in range(i, i + radius + 1) if 0 <= j < nvb]
+
+
+def route_qk_swapped(q, k, sink_start, ratio, radius):
+    return _orig["route"](k, q, sink_start, ratio, radius)
+
+
+# (oracle function, mutant, the pin expected to catch it)
+MUTANTS = [
+    ("pool_means", pool_63, oc.check_pool_exact),
+    ("pool_means", pool_f32_sum, oc.check_pool_exact),
+    ("route_scores", scores_transposed, oc.check_scores_exact),
+    ("route_scores", scores_bf16, oc.check_scores_exact),
+    ("topk_budget", budget_floor, oc.check_budget),
+    ("select_row", select_ascending, oc.check_topk_bruteforce),
+    ("select_row", select_tie_high_index, oc.check_topk_bruteforce),
+    ("select_row", select_tie_high_index, oc.check_signed_zero_tie),
+    ("select_row", select_forced_inside_budget, oc.check_topk_bruteforce),
+    ("attend", attend_no_scale, oc.check_ratio_one_equals_sdpa),
+    ("attend", attend_bias_sign, oc.check_bias_ln_m_duplicates_key),
+    ("attend", attend_bias_log2, oc.check_bias_ln_m_duplicates_key),
+    ("attend", attend_values_are_keys, oc.check_ratio_one_equals_sdpa),
+    ("key_bias_vector", bias_on_all_keys, oc.check_bias_ignored_on_video_keys),
+    ("sparse_block_output", gather_shifted, oc.check_token_mask_path),
+    ("dense_rows_output", dense_without_sinks, oc.check_all_dense_when_no_video_block),
+    ("dense_rows_output", dense_without_sinks, oc.check_ratio_one_equals_sdpa),
+    ("forced_blocks", forced_one_sided, oc.check_topk_bruteforce),
+    ("forced_blocks", forced_one_sided, oc.check_golden_pages_numbers),
+    ("route", route_qk_swapped, oc.check_route_glue),
+]
+
+
+@pytest.mark.parametrize("name,mutant,check", MUTANTS,
+                         ids=[f"{m.__name__}-{c.__name__}" for _, m, c in MUTANTS])
+def test_mutant_is_caught(monkeypatch, name, mutant, check):
+    check()                                   # passes on the oracle as written
+    monkeypatch.setattr(ra, name, mutant)
+    with pytest.raises((AssertionError, ValueError, IndexError)):
+        check()
