@@ -1,0 +1,200 @@
+"""Benchmark: one routed block-sparse attention call on the H3-shaped
+workload (B=1, H=56, T=9505 = 9216 video + 289 context tokens, D=128, bf16,
+top-k ratio 0.1, self block forced, context tokens as exact sinks).
+
+A step is one full call on one stream: sparse_attn_route (pool + route
+kernels), sparse_attn_fwd (video query rows) and dense_sink_fwd (context
+rows).  Inputs are resident in HBM before the timed region.  Effective FLOPs
+count 4*128 per (query row, key) pair scored exactly.
+
+Prints one JSON line.  ``--gpus`` above 1 is refused: this path runs on one
+GPU (a multi-GPU run would shard heads, see the design notes).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+HBM_PEAK_GBPS = 8000.0
+METRIC = "ms/call and effective TFLOP/s (frac of bf16 peak), B1 H56 T9505 D128 top-k 0.1"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_sparse_h3_traffic.json")
+ATTN_SRC = os.path.join(ROOT, "block_sparse_attention_05_amd", "csrc", "attn.hip")
+
+
+def effective_flops_from_lists(cnt, idx, T, nvb, H, B):
+    """4*D per exactly-scored (row, key) pair, from the GPU's own lists."""
+    idx = idx.cpu().numpy()
+    cnt = cnt.cpu().numpy()
+    keys_in_block = np.minimum(64, T - 64 * np.arange(-(-T // 64)))
+    sparse_pairs = 0
+    for b in range(B):
+        for h in range(H):
+            for i in range(nvb):
+                sparse_pairs += 64 * int(keys_in_block[idx[b, h, i, :cnt[b, h, i]]].sum())
+    dense_pairs = B * H * (T - 64 * nvb) * T
+    return 4 * 128 * sparse_pairs, 4 * 128 * dense_pairs
+
+
+def traffic_for_current_kernel():
+    """HBM bytes per sparse-attention launch measured with rocprofv3 counters
+    (FETCH_SIZE + WRITE_SIZE, scaled by a copy-kernel calibration), if they
+    were taken on the current kernel source; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        t = json.load(f)
+    src_hash = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
+    if t.get("attn_src_sha256") != src_hash:
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(wl, heads):
+    """Oracle (as written) on a bounded sample: the first `heads` heads of
+    the same workload."""
+    import oracle.sparse_attention as ora
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    f = lambda t: t[:, :, :heads].float().contiguous().numpy()
+    q, k, v = f(wl.q), f(wl.k), f(wl.v)
+    t0 = time.perf_counter()
+    _, _, rt = ora.routed_attention(q, k, v, wl.sink_start, wl.topk_ratio, wl.local_radius,
+                                    key_bias=None if wl.key_bias is None else wl.key_bias.numpy())
+    dt = time.perf_counter() - t0
+    T = q.shape[1]
+    flops = ora.effective_flops(T, heads, 1, rt.lists(), rt.nvb)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"oracle routed_attention (pool+route+sparse+dense, float64) on heads 0..{heads - 1} "
+                      f"of the same workload ({flops / 1e9:.1f} effective GFLOP in {dt:.1f} s)",
+            "seconds": dt}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="h3", choices=["h3", "h3_bias", "mid", "long", "tiny"])
+    ap.add_argument("--cpu-heads", type=int, default=24)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the routed attention "
+              "path shards by head with no collective; run one process per GPU.", file=sys.stderr)
+        sys.exit(2)
+
+    import block_sparse_attention_05_amd as sa
+    import workloads
+
+    wl = workloads.NAMED[args.workload]()
+    dev = torch.device("cuda:0")
+    q, k, v = (x.to(dev) for x in (wl.q, wl.k, wl.v))
+    kb = None if wl.key_bias is None else wl.key_bias.to(dev)
+    B, T, H, D = q.shape
+    ss = wl.sink_start
+    nvb = sa.sa_num_sparse_blocks(T, ss)
+    max_sel = sa.sa_max_selected(T, ss, wl.topk_ratio, wl.local_radius)
+    idx = torch.empty((B, H, nvb, max_sel), dtype=torch.int32, device=dev)
+    cnt = torch.empty((B, H, nvb), dtype=torch.int32, device=dev)
+    ws = torch.empty(max(16, sa.sa_route_workspace_bytes(B, T, H, ss)), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        sa.sparse_attn_route(q, k, ss, wl.topk_ratio, wl.local_radius, block_idx=idx, block_cnt=cnt,
+                             workspace=ws)
+        if ev is not None:
+            ev[1].record(stream)
+        sa.sparse_attn_fwd(q, k, v, ss, idx, cnt, key_bias=kb, out=out)
+        if ev is not None:
+            ev[2].record(stream)
+        sa.dense_sink_fwd(q, k, v, ss, key_bias=kb, out=out)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # whole-step timing: events only at the ends
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+
+    # per-stage timing (events between the launches, same stream)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    st = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(3)] for e in evs])
+    med = np.median(st, axis=0)
+
+    sparse_flops, dense_flops = effective_flops_from_lists(cnt, idx, T, nvb, H, B)
+    total_flops = sparse_flops + dense_flops
+    tflops = total_flops / (ms * 1e-3) / 1e12
+    sparse_ms = float(st[:, 1].mean())
+    achieved = sparse_flops / (sparse_ms * 1e-3) / 1e12
+
+    res = {
+        "metric": METRIC,
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": B, "T": T, "H": H, "D": D, "video_tokens": ss,
+                   "sink_tokens": T - ss, "topk_ratio": wl.topk_ratio, "local_radius": wl.local_radius,
+                   "key_bias": kb is not None, "inputs": "smooth-field+noise Q/K, N(0,1) V, seed 2"},
+        "ms_per_call": round(ms, 4),
+        "frac_of_bf16_peak": round(tflops / BF16_PEAK_TFLOPS, 4),
+        "effective_gflop": round(total_flops / 1e9, 3),
+        "stages_ms_median": {"route": round(float(med[0]), 4), "sparse_fwd": round(float(med[1]), 4),
+                             "dense_fwd": round(float(med[2]), 4)},
+        "stages_ms_p10_p90": {n: [round(float(np.percentile(st[:, j], 10)), 4),
+                                  round(float(np.percentile(st[:, j], 90)), 4)]
+                              for j, n in enumerate(("route", "sparse_fwd", "dense_fwd"))},
+        "attention_only_tflops": round((sparse_flops + dense_flops) / ((med[1] + med[2]) * 1e-3) / 1e12, 3),
+        "roofline": {"kernel": "attn_fwd_kernel<sparse>", "bound": "mfma", "achieved": round(achieved, 3),
+                     "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+                     "algorithmic_gflop_per_launch": round(sparse_flops / 1e9, 3),
+                     "launch_ms_mean": round(sparse_ms, 4),
+                     "traffic": traffic_for_current_kernel()},
+    }
+    if not args.no_cpu_baseline:
+        cb = cpu_baseline(wl, args.cpu_heads)
+        cb.pop("seconds")
+        res["cpu_baseline"] = cb
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

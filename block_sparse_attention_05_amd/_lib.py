@@ -1,0 +1,244 @@
+"""ctypes binding of libsparse_attn.so (include/sparse_attn.h).
+
+Argument marshalling only: tensors supply device pointers and the current
+stream; every step of the computation runs in the library's HIP kernels.
+There is no fallback: if the library is missing or a call fails, an
+exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsparse_attn.so")
+
+SA_OK, SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_WORKSPACE, SA_ERR_HIP = range(5)
+HEAD_DIM = 128
+BLOCK = 64
+
+_lib = None
+
+_c_int32, _c_int64, _c_size, _c_float, _vp = (ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t,
+                                               ctypes.c_float, ctypes.c_void_p)
+
+SIGNATURES = {
+    "sa_num_blocks": (_c_int32, [_c_int32]),
+    "sa_num_sparse_blocks": (_c_int32, [_c_int32, _c_int32]),
+    "sa_topk_budget": (_c_int32, [_c_int32, _c_float]),
+    "sa_max_selected": (_c_int32, [_c_int32, _c_int32, _c_float, _c_int32]),
+    "sa_route_workspace_bytes": (_c_size, [_c_int32, _c_int32, _c_int32, _c_int32]),
+    "sa_last_error": (ctypes.c_char_p, []),
+    "sparse_attn_route": (ctypes.c_int, [
+        _vp, _vp, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32,
+        _c_float, _c_int32, _vp, _c_int32, _vp, _vp, _vp, _c_size, _vp]),
+    "sparse_attn_fwd": (ctypes.c_int, [
+        _vp, _vp, _vp, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32,
+        _vp, _c_int64, _vp, _vp, _c_int32, _c_float, _vp, _vp, _vp]),
+    "dense_sink_fwd": (ctypes.c_int, [
+        _vp, _vp, _vp, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32,
+        _vp, _c_int64, _c_float, _vp, _vp, _vp]),
+}
+
+
+class SparseAttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"[status {status}] {message}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load the HIP library once.  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m block_sparse_attention_05_amd.build` (hipcc, gfx950)")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def _check(status: int):
+    if status != SA_OK:
+        msg = lib().sa_last_error().decode(errors="replace")
+        raise SparseAttnError(status, msg)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check_qkv(*ts: torch.Tensor):
+    ref = ts[0]
+    for t in ts:
+        if t.dtype != torch.bfloat16:
+            raise ValueError("q, k, v must be bfloat16")
+        if not t.is_cuda:
+            raise ValueError("q, k, v must be on a GPU device")
+        if t.dim() != 4 or t.shape[-1] != HEAD_DIM:
+            raise ValueError("q, k, v must be [B, T, H, 128]")
+        if not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous")
+        if t.shape != ref.shape or t.device != ref.device:
+            raise ValueError("q, k, v must share shape and device")
+
+
+def _bias(key_bias: Optional[torch.Tensor], B: int, T: int, device):
+    """Normalize the natural-log key bias to the float32 [B, T] contract;
+    reject a wrong element count before anything runs."""
+    if key_bias is None:
+        return None, 0
+    if key_bias.numel() != B * T:
+        raise ValueError(f"key_bias must hold exactly B*T = {B * T} elements, got {key_bias.numel()}")
+    if key_bias.device != device:
+        raise ValueError("key_bias must be on the same device as q")
+    kb = key_bias.reshape(B, T)
+    if kb.dtype != torch.float32 or not kb.is_contiguous():
+        kb = kb.to(torch.float32).contiguous()
+    return kb, kb.numel()
+
+
+# ---- shape helpers ---------------------------------------------------------
+
+def sa_num_blocks(T: int) -> int:
+    return lib().sa_num_blocks(T)
+
+
+def sa_num_sparse_blocks(T: int, sink_start: int) -> int:
+    return lib().sa_num_sparse_blocks(T, sink_start)
+
+
+def sa_topk_budget(nvb: int, ratio: float) -> int:
+    return lib().sa_topk_budget(nvb, ratio)
+
+
+def sa_max_selected(T: int, sink_start: int, ratio: float, radius: int) -> int:
+    return lib().sa_max_selected(T, sink_start, ratio, radius)
+
+
+def sa_route_workspace_bytes(B: int, T: int, H: int, sink_start: int) -> int:
+    return lib().sa_route_workspace_bytes(B, T, H, sink_start)
+
+
+# ---- entry points ----------------------------------------------------------
+
+def sparse_attn_route(q: torch.Tensor, k: torch.Tensor, sink_start: int,
+                      topk_ratio: float = 0.1, local_radius: int = 0, *,
+                      max_sel: Optional[int] = None, block_idx: Optional[torch.Tensor] = None,
+                      block_cnt: Optional[torch.Tensor] = None,
+                      route_scores: Optional[torch.Tensor] = None,
+                      workspace: Optional[torch.Tensor] = None,
+                      ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Exact block lists of every video query block.  Returns
+    (block_idx int32 [B,H,NVB,max_sel], block_cnt int32 [B,H,NVB]);
+    ``route_scores`` (fp32 [B,H,NVB,NVB]) is filled when given."""
+    _check_qkv(q, k)
+    B, T, H, D = q.shape
+    L = lib()
+    nvb = L.sa_num_sparse_blocks(T, sink_start)
+    if nvb < 0:
+        raise ValueError("sink_start must lie in [0, T]")
+    need = L.sa_max_selected(T, sink_start, topk_ratio, local_radius)
+    if max_sel is None:
+        max_sel = max(need, 1)
+    dev = q.device
+    if block_idx is None:
+        block_idx = torch.empty((B, H, nvb, max_sel), dtype=torch.int32, device=dev)
+    if block_cnt is None:
+        block_cnt = torch.empty((B, H, nvb), dtype=torch.int32, device=dev)
+    ws_bytes = L.sa_route_workspace_bytes(B, T, H, sink_start)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    for name, t, dt in (("block_idx", block_idx, torch.int32), ("block_cnt", block_cnt, torch.int32)):
+        if t.dtype != dt or not t.is_contiguous() or t.device != dev:
+            raise ValueError(f"{name} must be a contiguous int32 tensor on {dev}")
+    if block_idx.numel() < B * H * nvb * max_sel or block_cnt.numel() < B * H * nvb:
+        raise ValueError("block_idx / block_cnt too small")
+    if route_scores is not None and (route_scores.dtype != torch.float32 or not route_scores.is_contiguous()
+                                     or route_scores.numel() < B * H * nvb * nvb):
+        raise ValueError("route_scores must be contiguous float32 [B,H,NVB,NVB]")
+    _check(L.sparse_attn_route(
+        _ptr(q), _ptr(k), B, T, H, D, sink_start, T - sink_start, float(topk_ratio),
+        int(local_radius), _ptr(block_idx), int(max_sel), _ptr(block_cnt), _ptr(route_scores),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(dev)))
+    return block_idx, block_cnt
+
+
+def sparse_attn_fwd(q, k, v, sink_start: int, block_idx: torch.Tensor, block_cnt: torch.Tensor, *,
+                    key_bias: Optional[torch.Tensor] = None, softmax_scale: float = 0.0,
+                    out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
+    """Exact attention of rows [0, 64*NVB) over their block lists; writes
+    those rows of ``out`` (allocated if None) and returns it."""
+    _check_qkv(q, k, v)
+    B, T, H, D = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    _check_qkv(q, out)
+    if block_idx.dtype != torch.int32 or block_cnt.dtype != torch.int32 or \
+            not block_idx.is_contiguous() or not block_cnt.is_contiguous():
+        raise ValueError("block_idx / block_cnt must be contiguous int32")
+    nvb = lib().sa_num_sparse_blocks(T, sink_start)
+    max_sel = block_idx.shape[-1] if block_idx.dim() == 4 else 0
+    if nvb > 0 and (block_idx.dim() != 4 or tuple(block_idx.shape[:3]) != (B, H, nvb)
+                    or block_cnt.numel() != B * H * nvb):
+        raise ValueError("block_idx must be [B,H,NVB,max_sel] and block_cnt [B,H,NVB]")
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != B * H * T):
+        raise ValueError("lse must be contiguous float32 [B,H,T]")
+    kb, kb_n = _bias(key_bias, B, T, q.device)
+    _check(lib().sparse_attn_fwd(
+        _ptr(q), _ptr(k), _ptr(v), B, T, H, D, sink_start, T - sink_start, _ptr(kb), kb_n,
+        _ptr(block_idx), _ptr(block_cnt), int(max_sel), float(softmax_scale), _ptr(out), _ptr(lse),
+        _stream(q.device)))
+    return out
+
+
+def dense_sink_fwd(q, k, v, sink_start: int, *, key_bias: Optional[torch.Tensor] = None,
+                   softmax_scale: float = 0.0, out: Optional[torch.Tensor] = None,
+                   lse: Optional[torch.Tensor] = None):
+    """Dense attention of rows [64*NVB, T) over all keys; writes those rows
+    of ``out`` (allocated if None) and returns it."""
+    _check_qkv(q, k, v)
+    B, T, H, D = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    _check_qkv(q, out)
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != B * H * T):
+        raise ValueError("lse must be contiguous float32 [B,H,T]")
+    kb, kb_n = _bias(key_bias, B, T, q.device)
+    _check(lib().dense_sink_fwd(
+        _ptr(q), _ptr(k), _ptr(v), B, T, H, D, sink_start, T - sink_start, _ptr(kb), kb_n,
+        float(softmax_scale), _ptr(out), _ptr(lse), _stream(q.device)))
+    return out
+
+
+def routed_attention(q, k, v, sink_start: int, topk_ratio: float = 0.1, local_radius: int = 0, *,
+                     key_bias: Optional[torch.Tensor] = None, softmax_scale: float = 0.0,
+                     return_lse: bool = False, return_route: bool = False):
+    """One full call: sparse_attn_route + sparse_attn_fwd + dense_sink_fwd on
+    the current stream."""
+    block_idx, block_cnt = sparse_attn_route(q, k, sink_start, topk_ratio, local_radius)
+    B, T, H, _ = q.shape
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device) if return_lse else None
+    sparse_attn_fwd(q, k, v, sink_start, block_idx, block_cnt, key_bias=key_bias,
+                    softmax_scale=softmax_scale, out=out, lse=lse)
+    dense_sink_fwd(q, k, v, sink_start, key_bias=key_bias, softmax_scale=softmax_scale,
+                   out=out, lse=lse)
+    res = [out]
+    if return_lse:
+        res.append(lse)
+    if return_route:
+        res.append((block_idx, block_cnt))
+    return res[0] if len(res) == 1 else tuple(res)

@@ -1,0 +1,237 @@
+// C ABI of libsparse_attn.so: host-side validation and launch plumbing.
+// Every check runs before anything is enqueued; see include/sparse_attn.h.
+#include "sparse_attn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+sa_status fail(sa_status st, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+sa_status ok() {
+  g_err[0] = '\0';
+  return SA_OK;
+}
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Shape checks shared by the three entry points.
+sa_status check_shape(int32_t B, int32_t T, int32_t H, int32_t D, int32_t sink_start,
+                      int32_t sink_tokens) {
+  if (D != sa::kHeadDim) return fail(SA_ERR_INVALID_ARG, "D must be 128 (got %d)", D);
+  if (B <= 0 || T <= 0 || H <= 0)
+    return fail(SA_ERR_INVALID_ARG, "B, T, H must be positive (got %d, %d, %d)", B, T, H);
+  if (sink_start < 0 || sink_start > T)
+    return fail(SA_ERR_INVALID_ARG, "sink_start must lie in [0, T] (got %d, T=%d)", sink_start,
+                T);
+  if ((int64_t)sink_start + sink_tokens != T)
+    return fail(SA_ERR_INVALID_ARG, "sink_start + sink_tokens must equal T (%d + %d != %d)",
+                sink_start, sink_tokens, T);
+  // every launch indexes workgroups with int and elements with int64
+  const int64_t nb = (T + sa::kBlock - 1) / sa::kBlock;
+  if ((int64_t)B * H * nb > INT32_MAX / 2)
+    return fail(SA_ERR_UNSUPPORTED, "B*H*ceil(T/64) too large");
+  return SA_OK;
+}
+
+sa_status check_bf16(const void *p, const char *name) {
+  if (p == nullptr) return fail(SA_ERR_INVALID_ARG, "%s must not be NULL", name);
+  if (!aligned(p, 16)) return fail(SA_ERR_INVALID_ARG, "%s must be 16-byte aligned", name);
+  return SA_OK;
+}
+
+sa_status check_bias(const float *key_bias, int64_t numel, int32_t B, int32_t T) {
+  if (key_bias == nullptr) return SA_OK;
+  if (!aligned(key_bias, 4)) return fail(SA_ERR_INVALID_ARG, "key_bias must be 4-byte aligned");
+  if (numel != (int64_t)B * T)
+    return fail(SA_ERR_INVALID_ARG, "key_bias must hold exactly B*T = %lld floats (got %lld)",
+                (long long)B * T, (long long)numel);
+  return SA_OK;
+}
+
+sa_status check_scale(float softmax_scale, float *scale_log2) {
+  if (!std::isfinite(softmax_scale) || softmax_scale < 0.f)
+    return fail(SA_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0");
+  const double s = softmax_scale == 0.f ? 1.0 / std::sqrt((double)sa::kHeadDim) : softmax_scale;
+  *scale_log2 = (float)(s * 1.4426950408889634);
+  return SA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t sa_num_blocks(int32_t T) { return T <= 0 ? 0 : (T + sa::kBlock - 1) / sa::kBlock; }
+
+int32_t sa_num_sparse_blocks(int32_t T, int32_t sink_start) {
+  if (sink_start < 0 || sink_start > T) return -1;
+  return sink_start / sa::kBlock;
+}
+
+int32_t sa_topk_budget(int32_t nvb, float ratio) {
+  if (!(ratio > 0.f && ratio <= 1.f)) return -1;
+  if (nvb <= 0) return 0;
+  const double k = std::ceil((double)ratio * (double)nvb - 1e-6);
+  return k < 1.0 ? 1 : (int32_t)k;
+}
+
+int32_t sa_max_selected(int32_t T, int32_t sink_start, float ratio, int32_t radius) {
+  const int32_t nvb = sa_num_sparse_blocks(T, sink_start);
+  if (nvb < 0 || radius < 0) return -1;
+  const int32_t budget = sa_topk_budget(nvb, ratio);
+  if (budget < 0) return -1;
+  if (nvb == 0) return 0;
+  const int64_t local = (int64_t)budget + 2 * (int64_t)radius + 1;
+  const int32_t routed = local < nvb ? (int32_t)local : nvb;
+  return routed + (sa_num_blocks(T) - nvb);
+}
+
+size_t sa_route_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t sink_start) {
+  const int32_t nvb = sa_num_sparse_blocks(T, sink_start);
+  if (B <= 0 || H <= 0 || nvb <= 0) return 0;
+  return 2ull * (size_t)B * (size_t)H * (size_t)nvb * sa::kHeadDim * sizeof(float);
+}
+
+const char *sa_last_error(void) { return g_err; }
+
+sa_status sparse_attn_route(const void *q, const void *k, int32_t B, int32_t T, int32_t H,
+                            int32_t D, int32_t sink_start, int32_t sink_tokens,
+                            float topk_ratio, int32_t local_radius, int32_t *block_idx,
+                            int32_t max_sel, int32_t *block_cnt, float *route_scores,
+                            void *workspace, size_t workspace_bytes, void *stream) {
+  sa_status st = check_shape(B, T, H, D, sink_start, sink_tokens);
+  if (st != SA_OK) return st;
+  if ((st = check_bf16(q, "q")) != SA_OK) return st;
+  if ((st = check_bf16(k, "k")) != SA_OK) return st;
+  if (!(topk_ratio > 0.f && topk_ratio <= 1.f))
+    return fail(SA_ERR_INVALID_ARG, "topk_ratio must lie in (0, 1]");
+  if (local_radius < 0) return fail(SA_ERR_INVALID_ARG, "local_radius must be >= 0");
+  const int32_t nvb = sa_num_sparse_blocks(T, sink_start);
+  const int32_t nb = sa_num_blocks(T);
+  if (nvb > sa::kMaxRouteBlocks)
+    return fail(SA_ERR_UNSUPPORTED, "at most %d video blocks can be routed (got %d)",
+                sa::kMaxRouteBlocks, nvb);
+  const int32_t need_sel = sa_max_selected(T, sink_start, topk_ratio, local_radius);
+  if (max_sel < need_sel)
+    return fail(SA_ERR_INVALID_ARG, "max_sel must be >= %d (got %d)", need_sel, max_sel);
+  if (nvb == 0) return ok();
+  if (block_idx == nullptr || block_cnt == nullptr)
+    return fail(SA_ERR_INVALID_ARG, "block_idx and block_cnt must not be NULL");
+  if (!aligned(block_idx, 4) || !aligned(block_cnt, 4) ||
+      (route_scores != nullptr && !aligned(route_scores, 4)))
+    return fail(SA_ERR_INVALID_ARG, "block_idx, block_cnt, route_scores must be 4-byte aligned");
+  const size_t need_ws = sa_route_workspace_bytes(B, T, H, sink_start);
+  if (workspace_bytes < need_ws)
+    return fail(SA_ERR_WORKSPACE, "workspace must hold %zu bytes (got %zu)", need_ws,
+                workspace_bytes);
+  if (workspace == nullptr || !aligned(workspace, 16))
+    return fail(SA_ERR_WORKSPACE, "workspace must be a 16-byte aligned device pointer");
+
+  const int32_t budget = sa_topk_budget(nvb, topk_ratio);
+  float *qbar = static_cast<float *>(workspace);
+  float *kbar = qbar + (size_t)B * H * nvb * sa::kHeadDim;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = sa::launch_pool(q, k, qbar, kbar, B, T, H, nvb, s);
+  if (e != hipSuccess) return fail(SA_ERR_HIP, "pool launch: %s", hipGetErrorString(e));
+  e = sa::launch_route(qbar, kbar, B, H, nvb, nb, budget, local_radius, max_sel, block_idx,
+                       block_cnt, route_scores, s);
+  if (e != hipSuccess) return fail(SA_ERR_HIP, "route launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+sa_status sparse_attn_fwd(const void *q, const void *k, const void *v, int32_t B, int32_t T,
+                          int32_t H, int32_t D, int32_t sink_start, int32_t sink_tokens,
+                          const float *key_bias, int64_t key_bias_numel,
+                          const int32_t *block_idx, const int32_t *block_cnt, int32_t max_sel,
+                          float softmax_scale, void *out, float *lse, void *stream) {
+  sa_status st = check_shape(B, T, H, D, sink_start, sink_tokens);
+  if (st != SA_OK) return st;
+  if ((st = check_bf16(q, "q")) != SA_OK) return st;
+  if ((st = check_bf16(k, "k")) != SA_OK) return st;
+  if ((st = check_bf16(v, "v")) != SA_OK) return st;
+  if ((st = check_bf16(out, "out")) != SA_OK) return st;
+  if ((st = check_bias(key_bias, key_bias_numel, B, T)) != SA_OK) return st;
+  float scale_log2 = 0.f;
+  if ((st = check_scale(softmax_scale, &scale_log2)) != SA_OK) return st;
+  if (lse != nullptr && !aligned(lse, 4)) return fail(SA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  const int32_t nvb = sa_num_sparse_blocks(T, sink_start);
+  if (nvb == 0) return ok();
+  if (block_idx == nullptr || block_cnt == nullptr)
+    return fail(SA_ERR_INVALID_ARG, "block_idx and block_cnt must not be NULL");
+  if (!aligned(block_idx, 4) || !aligned(block_cnt, 4))
+    return fail(SA_ERR_INVALID_ARG, "block_idx and block_cnt must be 4-byte aligned");
+  if (max_sel <= 0) return fail(SA_ERR_INVALID_ARG, "max_sel must be positive");
+
+  sa::AttnArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.lse = lse;
+  a.key_bias = key_bias;
+  a.block_idx = block_idx;
+  a.block_cnt = block_cnt;
+  a.B = B;
+  a.T = T;
+  a.H = H;
+  a.nb = sa_num_blocks(T);
+  a.nvb = nvb;
+  a.max_sel = max_sel;
+  a.scale_log2 = scale_log2;
+  hipError_t e = sa::launch_attn_sparse(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SA_ERR_HIP, "sparse attention launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+sa_status dense_sink_fwd(const void *q, const void *k, const void *v, int32_t B, int32_t T,
+                         int32_t H, int32_t D, int32_t sink_start, int32_t sink_tokens,
+                         const float *key_bias, int64_t key_bias_numel, float softmax_scale,
+                         void *out, float *lse, void *stream) {
+  sa_status st = check_shape(B, T, H, D, sink_start, sink_tokens);
+  if (st != SA_OK) return st;
+  if ((st = check_bf16(q, "q")) != SA_OK) return st;
+  if ((st = check_bf16(k, "k")) != SA_OK) return st;
+  if ((st = check_bf16(v, "v")) != SA_OK) return st;
+  if ((st = check_bf16(out, "out")) != SA_OK) return st;
+  if ((st = check_bias(key_bias, key_bias_numel, B, T)) != SA_OK) return st;
+  float scale_log2 = 0.f;
+  if ((st = check_scale(softmax_scale, &scale_log2)) != SA_OK) return st;
+  if (lse != nullptr && !aligned(lse, 4)) return fail(SA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  const int32_t nvb = sa_num_sparse_blocks(T, sink_start);
+  if ((int64_t)nvb * sa::kBlock == T) return ok();
+
+  sa::AttnArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.lse = lse;
+  a.key_bias = key_bias;
+  a.B = B;
+  a.T = T;
+  a.H = H;
+  a.nb = sa_num_blocks(T);
+  a.nvb = nvb;
+  a.max_sel = 0;
+  a.scale_log2 = scale_log2;
+  hipError_t e = sa::launch_attn_dense(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SA_ERR_HIP, "dense attention launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

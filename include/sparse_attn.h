@@ -1,0 +1,197 @@
+/*
+ * sparse_attn.h - C ABI of the MI355X (gfx950) routed block-sparse attention
+ * library (libsparse_attn.so).
+ *
+ * Operation (forward only).  Q, K, V are contiguous BF16 [B, T, H, 128]
+ * tensors (page "Sol-Attn and Spark for MiniMax-H3", section Install).  The
+ * first `sink_start` tokens are the target video grid; the remaining
+ * `sink_tokens = T - sink_start` conditioning tokens are packed after it and
+ * act as exact K/V sinks (same page, "H3 pipeline integration" and "Direct
+ * Sol-Attn", where sol_attn takes sink_start=video_tokens and
+ * sink_tokens=T-video_tokens).  Tokens are grouped into 64-token blocks
+ * (same page, "Spark primitives").  With
+ *     NB  = ceil(T / 64)        all blocks (the last may be partial),
+ *     NVB = sink_start / 64     complete video blocks,
+ * blocks [0, NVB) are routed, and every block holding a token >= 64*NVB is a
+ * sink block.  Query rows [0, 64*NVB) take the sparse path; rows
+ * [64*NVB, T) (context rows and a video block split by the boundary) take the
+ * dense path over all keys ("H3 pipeline integration": context query rows
+ * and the mixed final block are computed densely with the complete K/V).
+ *
+ * A full call is sparse_attn_route + sparse_attn_fwd + dense_sink_fwd on one
+ * stream.
+ *
+ * Conventions shared by every entry point:
+ *  - All tensor pointers are DEVICE pointers owned by the caller.  The
+ *    library allocates nothing and keeps no state between calls.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Calls only enqueue work; nothing synchronises the host.
+ *  - Every argument is validated on the host before anything is enqueued.
+ *    A violation returns SA_ERR_INVALID_ARG (or SA_ERR_UNSUPPORTED /
+ *    SA_ERR_WORKSPACE) and enqueues nothing; sa_last_error() then names the
+ *    argument.  A launch failure returns SA_ERR_HIP.  Nothing aborts, retries
+ *    or falls back to another implementation (page "Sol-Attn and Spark for
+ *    MiniMax-H3", "Spark inference integration": kernel failures propagate to
+ *    the caller with no error-triggered fallback).
+ *  - Pointers to BF16 tensors must be 16-byte aligned; int32/fp32 pointers
+ *    4-byte aligned.
+ */
+#ifndef SPARSE_ATTN_H
+#define SPARSE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SA_OK = 0,
+  SA_ERR_INVALID_ARG = 1,
+  SA_ERR_UNSUPPORTED = 2,
+  SA_ERR_WORKSPACE = 3,
+  SA_ERR_HIP = 4
+} sa_status;
+
+/* ---- shape helpers: host-only, pure, no device access ------------------ */
+
+/* NB = ceil(T / 64); 0 if T <= 0. */
+int32_t sa_num_blocks(int32_t T);
+
+/* NVB = sink_start / 64 (complete video blocks); -1 if sink_start is not in
+ * [0, T]. */
+int32_t sa_num_sparse_blocks(int32_t T, int32_t sink_start);
+
+/* Fixed-ratio Top-K budget before clamping: max(1, ceil(ratio * nvb - 1e-6))
+ * with the product in double (page "Sol-Attn and Spark for MiniMax-H3",
+ * "Spark inference integration": native mean Top-K routing with ratio 0.1).
+ * Returns 0 when nvb <= 0 and -1 when ratio is not in (0, 1]. */
+int32_t sa_topk_budget(int32_t nvb, float ratio);
+
+/* Longest exact list any query block can get:
+ * min(NVB, budget + 2*radius + 1) + (NB - NVB); 0 when NVB == 0; -1 on
+ * invalid arguments. */
+int32_t sa_max_selected(int32_t T, int32_t sink_start, float ratio, int32_t radius);
+
+/* Workspace bytes sparse_attn_route needs: the pooled fp32 means of Q and K,
+ * 2 * B * H * NVB * 128 * 4 bytes. */
+size_t sa_route_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t sink_start);
+
+/* Message of the last failed call made by this thread ("" if none). */
+const char *sa_last_error(void);
+
+/* ---- routing ------------------------------------------------------------- */
+
+/*
+ * sparse_attn_route - pool, score and select the exact block list of every
+ * video query block.
+ *
+ * Defined by: page "Sol-Attn and Spark for MiniMax-H3", "Spark inference
+ * integration" (native mean Top-K routing, ratio 0.1, the packed route is
+ * exported once so attention does not recompute route QK; the boundary
+ * selection is an exact FP32 selection) and "H3 pipeline integration" (fixed
+ * Top-K routing: radius 0 forces the self block, radius 1 the self block and
+ * its two neighbours, added outside the Top-K budget); page "Add key bias to
+ * chunked Sol-Attn producers", Tests and source audit (sink blocks are put
+ * straight into the exact list and excluded from the routed candidates).
+ *
+ * Computes, for every batch b, head h and query block i < NVB:
+ *   qbar_i, kbar_j = fp32 mean of the 64 Q (K) rows of block i (j); the sum
+ *                    is exact, so the mean is correctly rounded;
+ *   s_ij           = qbar_i . kbar_j for j < NVB, fp32 of a float64 dot
+ *                    product (unscaled);
+ *   F(i)           = { j : |j - i| <= local_radius } within [0, NVB);
+ *   R(i)           = the first min(budget, NVB - |F(i)|) blocks of
+ *                    [0, NVB) \ F(i) ordered by (s_ij descending, j
+ *                    ascending), -0.0 equal to +0.0;
+ *   list(i)        = ascending R(i) u F(i) u [NVB, NB).
+ *
+ * q, k          bf16 [B, T, H, 128], contiguous.
+ * D             must be 128.
+ * sink_start    video tokens, 0 <= sink_start <= T; sink_tokens must equal
+ *               T - sink_start.
+ * topk_ratio    in (0, 1].  local_radius >= 0.
+ * block_idx     int32 [B, H, NVB, max_sel] out: ascending lists, padded -1.
+ * max_sel       >= sa_max_selected(T, sink_start, topk_ratio, local_radius).
+ * block_cnt     int32 [B, H, NVB] out: list lengths.
+ * route_scores  nullable; fp32 [B, H, NVB, NVB] out: s_ij.
+ * workspace     device scratch of workspace_bytes >=
+ *               sa_route_workspace_bytes(B, T, H, sink_start) (pooled means
+ *               are left there: Q means then K means, each [B, H, NVB, 128]
+ *               fp32).  May be NULL when that size is 0.
+ * Errors: SA_ERR_UNSUPPORTED when NVB > 1024 (per-row sort width).
+ * With NVB == 0 nothing is enqueued and SA_OK is returned.
+ */
+sa_status sparse_attn_route(const void *q, const void *k,
+                            int32_t B, int32_t T, int32_t H, int32_t D,
+                            int32_t sink_start, int32_t sink_tokens,
+                            float topk_ratio, int32_t local_radius,
+                            int32_t *block_idx, int32_t max_sel, int32_t *block_cnt,
+                            float *route_scores,
+                            void *workspace, size_t workspace_bytes,
+                            void *stream);
+
+/* ---- attention ----------------------------------------------------------- */
+
+/*
+ * sparse_attn_fwd - exact attention of the video query rows [0, 64*NVB)
+ * over the keys of their block lists.
+ *
+ * Defined by: page "Sol-Attn and Spark for MiniMax-H3", "Spark inference
+ * integration" (K/V tiles streamed through one FP32 online-softmax/output
+ * accumulator) and page "Add key bias to chunked Sol-Attn producers",
+ * Summary and Contract (natural-log key_bias, float32 [B, T], converted once
+ * to log2 units and consumed only by the exact branch; biased key blocks must
+ * be sink-routed).
+ *
+ * For row t of query block i and key j in a block of list(i), j < T:
+ *   l_tj = softmax_scale * (q_t . k_j) + beta_j,
+ *   beta_j = key_bias[b, j] if j >= 64*NVB (a sink key) else 0,
+ *   out_t = sum_j softmax_j(l_t) v_j  (bf16, round to nearest even),
+ *   lse_t = log sum_j exp(l_tj)       (natural log, fp32).
+ * Evaluated as an online softmax in base 2 with fp32 accumulation on bf16
+ * MFMA; P is rounded to bf16 for the PV product.
+ *
+ * key_bias      nullable fp32 [B, T], key_bias_numel must equal B*T.  Values
+ *               on non-sink keys are ignored (callers must keep biased keys
+ *               in sink blocks).
+ * block_idx, block_cnt, max_sel  as produced by sparse_attn_route with the
+ *               same B, T, H, sink_start.  Entries outside [0, NB) are
+ *               skipped and counts are clamped to max_sel.
+ * softmax_scale 0 selects 1/sqrt(128).
+ * out           bf16 [B, T, H, 128]; only rows [0, 64*NVB) are written.
+ * lse           nullable fp32 [B, H, T]; only rows [0, 64*NVB) are written.
+ */
+sa_status sparse_attn_fwd(const void *q, const void *k, const void *v,
+                          int32_t B, int32_t T, int32_t H, int32_t D,
+                          int32_t sink_start, int32_t sink_tokens,
+                          const float *key_bias, int64_t key_bias_numel,
+                          const int32_t *block_idx, const int32_t *block_cnt, int32_t max_sel,
+                          float softmax_scale,
+                          void *out, float *lse,
+                          void *stream);
+
+/*
+ * dense_sink_fwd - dense attention of query rows [64*NVB, T) (context query
+ * rows and a video block split by the boundary) over all T keys, same
+ * formula, same bias rule and the same kernel as sparse_attn_fwd (page
+ * "Sol-Attn and Spark for MiniMax-H3", "H3 pipeline integration": context
+ * query rows are computed with dense attention over the complete K/V).
+ *
+ * out / lse     only rows [64*NVB, T) are written.  With 64*NVB == T
+ *               nothing is enqueued.
+ */
+sa_status dense_sink_fwd(const void *q, const void *k, const void *v,
+                         int32_t B, int32_t T, int32_t H, int32_t D,
+                         int32_t sink_start, int32_t sink_tokens,
+                         const float *key_bias, int64_t key_bias_numel,
+                         float softmax_scale,
+                         void *out, float *lse,
+                         void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSE_ATTN_H */

@@ -1,0 +1,77 @@
+"""Helpers for the GPU parity tests: run the HIP path through the C-ABI
+binding, run the oracle on the same bf16 inputs, compare."""
+import sys
+
+import numpy as np
+import torch
+
+import oracle.sparse_attention as ora
+
+# Output tolerance against the oracle (fp32/fp64 reference, bf16 output).
+MAX_ABS = 2e-2
+MEAN_ABS = 2e-3
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def to_np(t):
+    return t.detach().float().cpu().numpy()
+
+
+def run_gpu(wl, *, key_bias=None, ratio=None, radius=None, scores=True, lse=True):
+    import block_sparse_attention_05_amd as sa
+    dev = torch.device("cuda:0")
+    q, k, v = (x.to(dev) for x in (wl.q, wl.k, wl.v))
+    B, T, H, _ = q.shape
+    ratio = wl.topk_ratio if ratio is None else ratio
+    radius = wl.local_radius if radius is None else radius
+    kb = key_bias if key_bias is not None else wl.key_bias
+    kb = None if kb is None else kb.to(dev)
+    nb, nvb = ora.block_counts(T, wl.sink_start)
+    sc = torch.full((B, H, nvb, nvb), float("nan"), device=dev) if (scores and nvb) else None
+    idx, cnt = sa.sparse_attn_route(q, k, wl.sink_start, ratio, radius, route_scores=sc)
+    out = torch.full_like(q, float("nan"))
+    ls = torch.full((B, H, T), float("nan"), device=dev) if lse else None
+    sa.sparse_attn_fwd(q, k, v, wl.sink_start, idx, cnt, key_bias=kb, out=out, lse=ls)
+    sa.dense_sink_fwd(q, k, v, wl.sink_start, key_bias=kb, out=out, lse=ls)
+    torch.cuda.synchronize()
+    return dict(out=out.cpu(), lse=None if ls is None else ls.cpu(), idx=idx.cpu(), cnt=cnt.cpu(),
+                scores=None if sc is None else sc.cpu())
+
+
+def compare_lists(idx, cnt, rt):
+    """Lists must equal the oracle's except in near-tie rows, where every
+    differing block must have an oracle score inside the tie band.
+    Returns (rows, mismatched rows, near-tie rows, unexplained rows)."""
+    idx = idx.numpy()
+    cnt = cnt.numpy()
+    B, H, nvb, max_sel = idx.shape
+    rows = mism = ties = unexplained = 0
+    for b in range(B):
+        for h in range(H):
+            for i in range(nvb):
+                rows += 1
+                sel = rt.rows[b][h][i]
+                c = int(cnt[b, h, i])
+                got = idx[b, h, i, :c].tolist()
+                assert all(x == -1 for x in idx[b, h, i, c:]), "padding must be -1"
+                assert got == sorted(set(got)), "lists must be strictly ascending"
+                ties += sel.near_tie
+                if got == sel.blocks:
+                    continue
+                mism += 1
+                diff = set(got) ^ set(sel.blocks)
+                lo, hi = sel.band
+                ok = sel.near_tie and len(got) == len(sel.blocks) and all(
+                    j < rt.nvb and j not in sel.forced and lo <= rt.scores[b, h, i, j] <= hi for j in diff)
+                if not ok:
+                    unexplained += 1
+    return rows, mism, ties, unexplained
+
+
+def err_stats(got, want):
+    d = np.abs(np.asarray(got, np.float64) - np.asarray(want, np.float64))
+    return float(d.max()), float(d.mean())

@@ -1,0 +1,224 @@
+"""HIP path vs the CPU oracle on the same seeded bf16 inputs (needs a GPU).
+
+Selections: bit-exact lists except rows the oracle reports as near-ties.
+Outputs: max-abs <= 2e-2 and mean-abs <= 2e-3 against the oracle.
+Full-size workloads are compared on sampled query blocks / dense rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle.sparse_attention as ora
+import workloads
+from gpu_helpers import MAX_ABS, MEAN_ABS, compare_lists, err_stats, log, run_gpu, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_route(res, rt, wl):
+    B, T, H, _ = wl.q.shape
+    nvb = rt.nvb
+    if nvb == 0:
+        return
+    rows, mism, ties, unexp = compare_lists(res["idx"], res["cnt"], rt)
+    log(f"[{wl.name}] lists: rows={rows} mismatched={mism} near_ties={ties} unexplained={unexp}")
+    assert unexp == 0
+    if res["scores"] is not None:
+        g = res["scores"].numpy()
+        # fp32 of an fp64 dot product on both sides: equal except where the two
+        # fp64 sums straddle an fp32 rounding boundary (1 ulp)
+        gi = g.view(np.int32).astype(np.int64)
+        oi = rt.scores.view(np.int32).astype(np.int64)
+        ulps = np.abs(gi - oi)
+        log(f"[{wl.name}] scores: bit-equal={np.mean(ulps == 0):.6f} max_ulp={ulps.max()}")
+        assert ulps.max() <= 1
+    # forced and sink blocks always present
+    idx, cnt = res["idx"].numpy(), res["cnt"].numpy()
+    nb = rt.nb
+    for b in range(B):
+        for h in range(H):
+            for i in range(nvb):
+                s = set(idx[b, h, i, :cnt[b, h, i]].tolist())
+                assert set(ora.forced_blocks(i, nvb, wl.local_radius)) <= s
+                assert set(range(nvb, nb)) <= s
+
+
+def _adopt_gpu_lists(res, rt):
+    """After the route check, evaluate attention on the GPU's lists: they
+    equal the oracle's except inside reported near-tie bands."""
+    idx, cnt = res["idx"].numpy(), res["cnt"].numpy()
+    for b, brow in enumerate(rt.rows):
+        for h, hrow in enumerate(brow):
+            for i, sel in enumerate(hrow):
+                sel.blocks = idx[b, h, i, :cnt[b, h, i]].tolist()
+
+
+def _full_parity(wl, key_bias=None):
+    q, k, v = (to_np(x) for x in (wl.q, wl.k, wl.v))
+    kb = key_bias if key_bias is not None else wl.key_bias
+    kbn = None if kb is None else kb.numpy()
+    log(f"[{wl.name}] GPU run")
+    res = run_gpu(wl, key_bias=kb)
+    log(f"[{wl.name}] oracle run")
+    rt = ora.route(q, k, wl.sink_start, wl.topk_ratio, wl.local_radius)
+    _check_route(res, rt, wl)
+    _adopt_gpu_lists(res, rt)
+    want, want_lse, _ = ora.routed_attention(q, k, v, wl.sink_start, wl.topk_ratio,
+                                             wl.local_radius, key_bias=kbn, rt=rt)
+    got = to_np(res["out"])
+    assert np.isfinite(got).all()
+    mx, mean = err_stats(got, want)
+    lmx, _ = err_stats(res["lse"].numpy(), want_lse)
+    log(f"[{wl.name}] out max_abs={mx:.3e} mean_abs={mean:.3e} |out|max={np.abs(want).max():.3f} lse max_abs={lmx:.3e}")
+    assert mx <= MAX_ABS and mean <= MEAN_ABS
+    assert lmx <= 1e-2
+    return res, rt
+
+
+def test_tiny_full():
+    _full_parity(workloads.tiny())
+
+
+def test_tiny_batch2_radius2():
+    q, k, v = workloads.tiny_qkv(B=2, H=3, T=1024, seed=5)
+    wl = workloads.Workload("tiny_B2_H3_r2", q, k, v, sink_start=1024, topk_ratio=0.3, local_radius=2)
+    _full_parity(wl)
+
+
+def test_mid_full():
+    _full_parity(workloads.mid())
+
+
+def test_split_video_block_and_bias():
+    # video boundary inside a 64-token block: that block is a sink block and
+    # its rows take the dense path; last block partial
+    q, k, v, tv = workloads.video_qkv(B=1, H=3, frames=2, ctx_tokens=150, seed=7, height=16, width=32)
+    tv2 = tv - 17                          # 1024 - 17: boundary splits block 15
+    bias = workloads.sink_key_bias(1, q.shape[1], tv2, seed=8)
+    wl = workloads.Workload("split_block", q, k, v, sink_start=tv2, topk_ratio=0.2, local_radius=1,
+                            key_bias=bias)
+    _full_parity(wl)
+
+
+def test_no_video_blocks_all_dense():
+    q, k, v = workloads.random_qkv(1, 700, 2, seed=9)
+    wl = workloads.Workload("all_dense", q, k, v, sink_start=40, topk_ratio=0.1, local_radius=1)
+    _full_parity(wl)
+
+
+def test_single_video_block():
+    q, k, v = workloads.random_qkv(1, 200, 2, seed=10)
+    wl = workloads.Workload("one_block", q, k, v, sink_start=100, topk_ratio=0.1, local_radius=0)
+    _full_parity(wl)
+
+
+def test_ratio_one_is_dense_and_matches_oracle():
+    q, k, v = workloads.random_qkv(1, 1000, 2, seed=11)
+    wl = workloads.Workload("ratio_one", q, k, v, sink_start=900, topk_ratio=1.0, local_radius=0)
+    _full_parity(wl)
+
+
+def test_ratio_one_sparse_bit_identical_to_dense_kernel():
+    """At ratio 1.0 every list is all blocks in ascending order: the sparse
+    path must reproduce the dense path bit for bit (same kernel, same tile
+    order)."""
+    import block_sparse_attention_05_amd as sa
+    q, k, v = (x.cuda() for x in workloads.random_qkv(1, 1088, 2, seed=12))
+    T = q.shape[1]
+    idx, cnt = sa.sparse_attn_route(q, k, T, 1.0, 0)
+    a = sa.sparse_attn_fwd(q, k, v, T, idx, cnt)
+    b = sa.dense_sink_fwd(q, k, v, 0)          # NVB = 0: all rows dense
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_zero_bias_bit_identical_to_no_bias():
+    wl = workloads.mid()
+    a = run_gpu(wl, scores=False)
+    b = run_gpu(wl, key_bias=torch.zeros(1, wl.q.shape[1]), scores=False)
+    assert torch.equal(a["out"], b["out"]) and torch.equal(a["lse"], b["lse"])
+
+
+def test_bias_changes_output_and_only_on_sinks():
+    wl = workloads.mid()
+    T = wl.q.shape[1]
+    a = run_gpu(wl, scores=False)
+    bias = workloads.sink_key_bias(1, T, wl.sink_start, seed=3)
+    b = run_gpu(wl, key_bias=bias, scores=False)
+    assert (a["out"].float() - b["out"].float()).abs().max() > 1e-3
+    # a bias on video keys is ignored: only the exact sink branch consumes it
+    video_bias = bias.clone()
+    video_bias[:, :wl.sink_start] = -1.0
+    c = run_gpu(wl, key_bias=video_bias, scores=False)
+    assert torch.equal(b["out"], c["out"])
+
+
+def test_deterministic_repeat():
+    wl = workloads.mid()
+    a = run_gpu(wl)
+    b = run_gpu(wl)
+    for key in ("out", "lse", "idx", "cnt", "scores"):
+        assert torch.equal(a[key], b[key]), key
+
+
+def test_pooled_means_bit_exact():
+    import block_sparse_attention_05_amd as sa
+    wl = workloads.mid()
+    q, k = wl.q.cuda(), wl.k.cuda()
+    B, T, H, _ = q.shape
+    ws = torch.zeros(sa.sa_route_workspace_bytes(B, T, H, wl.sink_start), dtype=torch.uint8, device="cuda")
+    sa.sparse_attn_route(q, k, wl.sink_start, 0.1, 1, workspace=ws)
+    torch.cuda.synchronize()
+    nvb = wl.sink_start // 64
+    means = ws.view(torch.float32).cpu().numpy().reshape(2, B, H, nvb, 128)
+    assert np.array_equal(means[0].view(np.uint32), ora.pool_means(to_np(wl.q), nvb).view(np.uint32))
+    assert np.array_equal(means[1].view(np.uint32), ora.pool_means(to_np(wl.k), nvb).view(np.uint32))
+
+
+# ---- full-size workloads: full route, sampled attention -------------------
+
+def _sampled_parity(wl, n_blocks=48, dense_heads=3, seed=0):
+    B, T, H, _ = wl.q.shape
+    q, k, v = (to_np(x) for x in (wl.q, wl.k, wl.v))
+    kbn = None if wl.key_bias is None else wl.key_bias.numpy()
+    log(f"[{wl.name}] GPU run")
+    res = run_gpu(wl)
+    log(f"[{wl.name}] oracle route")
+    rt = ora.route(q, k, wl.sink_start, wl.topk_ratio, wl.local_radius)
+    _check_route(res, rt, wl)
+    got = to_np(res["out"])
+    assert np.isfinite(got).all()
+    glse = res["lse"].numpy()
+    rng = np.random.default_rng(seed)
+    errs, lerrs = [], []
+    nvb = rt.nvb
+    for _ in range(n_blocks):
+        h, i = int(rng.integers(H)), int(rng.integers(nvb))
+        # the GPU's own list (equal to the oracle's, or a near-tie variant)
+        c = int(res["cnt"][0, h, i])
+        blocks = res["idx"][0, h, i, :c].tolist()
+        o, l = ora.sparse_block_output(q, k, v, 0, h, i, blocks, kbn, nvb)
+        errs.append(np.abs(got[0, 64 * i:64 * i + 64, h] - o))
+        lerrs.append(np.abs(glse[0, h, 64 * i:64 * i + 64] - l))
+    rows = np.arange(64 * nvb, T)
+    for h in rng.choice(H, size=min(dense_heads, H), replace=False):
+        o, l = ora.dense_rows_output(q, k, v, 0, int(h), rows, kbn, nvb)
+        errs.append(np.abs(got[0, rows, int(h)] - o))
+        lerrs.append(np.abs(glse[0, int(h), rows] - l))
+    e = np.concatenate([x.ravel() for x in errs])
+    le = np.concatenate([x.ravel() for x in lerrs])
+    log(f"[{wl.name}] sampled out max_abs={e.max():.3e} mean_abs={e.mean():.3e} lse max_abs={le.max():.3e}")
+    assert e.max() <= MAX_ABS and e.mean() <= MEAN_ABS
+    assert le.max() <= 1e-2
+
+
+def test_h3_sampled():
+    _sampled_parity(workloads.h3())
+
+
+def test_h3_keybias_sampled():
+    _sampled_parity(workloads.h3(with_bias=True), seed=1)
+
+
+def test_long_sampled():
+    _sampled_parity(workloads.long(), n_blocks=32, dense_heads=2, seed=2)
