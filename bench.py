@@ -112,6 +112,8 @@ def main():
     idx = torch.empty((B, H, nvb, max_sel), dtype=torch.int32, device=dev)
     cnt = torch.empty((B, H, nvb), dtype=torch.int32, device=dev)
     ws = torch.empty(max(16, sa.sa_route_workspace_bytes(B, T, H, ss)), dtype=torch.uint8, device=dev)
+    dws_n = sa.sa_dense_workspace_bytes(B, T, H, ss)
+    dws = torch.empty(dws_n, dtype=torch.uint8, device=dev) if dws_n > 0 else None
     out = torch.empty_like(q)
     stream = torch.cuda.current_stream(dev)
 
@@ -125,7 +127,7 @@ def main():
         sa.sparse_attn_fwd(q, k, v, ss, idx, cnt, key_bias=kb, out=out)
         if ev is not None:
             ev[2].record(stream)
-        sa.dense_sink_fwd(q, k, v, ss, key_bias=kb, out=out)
+        sa.dense_sink_fwd(q, k, v, ss, key_bias=kb, out=out, workspace=dws)
         if ev is not None:
             ev[3].record(stream)
 

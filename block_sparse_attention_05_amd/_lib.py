@@ -30,6 +30,7 @@ SIGNATURES = {
     "sa_topk_budget": (_c_int32, [_c_int32, _c_float]),
     "sa_max_selected": (_c_int32, [_c_int32, _c_int32, _c_float, _c_int32]),
     "sa_route_workspace_bytes": (_c_size, [_c_int32, _c_int32, _c_int32, _c_int32]),
+    "sa_dense_workspace_bytes": (_c_size, [_c_int32, _c_int32, _c_int32, _c_int32]),
     "sa_last_error": (ctypes.c_char_p, []),
     "sparse_attn_route": (ctypes.c_int, [
         _vp, _vp, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32,
@@ -39,7 +40,7 @@ SIGNATURES = {
         _vp, _c_int64, _vp, _vp, _c_int32, _c_float, _vp, _vp, _vp]),
     "dense_sink_fwd": (ctypes.c_int, [
         _vp, _vp, _vp, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32,
-        _vp, _c_int64, _c_float, _vp, _vp, _vp]),
+        _vp, _c_int64, _c_float, _vp, _vp, _vp, _c_size, _vp]),
 }
 
 
@@ -132,6 +133,10 @@ def sa_route_workspace_bytes(B: int, T: int, H: int, sink_start: int) -> int:
     return lib().sa_route_workspace_bytes(B, T, H, sink_start)
 
 
+def sa_dense_workspace_bytes(B: int, T: int, H: int, sink_start: int) -> int:
+    return lib().sa_dense_workspace_bytes(B, T, H, sink_start)
+
+
 # ---- entry points ----------------------------------------------------------
 
 def sparse_attn_route(q: torch.Tensor, k: torch.Tensor, sink_start: int,
@@ -206,9 +211,11 @@ def sparse_attn_fwd(q, k, v, sink_start: int, block_idx: torch.Tensor, block_cnt
 
 def dense_sink_fwd(q, k, v, sink_start: int, *, key_bias: Optional[torch.Tensor] = None,
                    softmax_scale: float = 0.0, out: Optional[torch.Tensor] = None,
-                   lse: Optional[torch.Tensor] = None):
+                   lse: Optional[torch.Tensor] = None, workspace="auto"):
     """Dense attention of rows [64*NVB, T) over all keys; writes those rows
-    of ``out`` (allocated if None) and returns it."""
+    of ``out`` (allocated if None) and returns it.  ``workspace``: a uint8
+    device tensor, None (no key split), or "auto" (allocate what the split
+    needs)."""
     _check_qkv(q, k, v)
     B, T, H, D = q.shape
     if out is None:
@@ -217,9 +224,13 @@ def dense_sink_fwd(q, k, v, sink_start: int, *, key_bias: Optional[torch.Tensor]
     if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != B * H * T):
         raise ValueError("lse must be contiguous float32 [B,H,T]")
     kb, kb_n = _bias(key_bias, B, T, q.device)
+    if isinstance(workspace, str):
+        n = lib().sa_dense_workspace_bytes(B, T, H, sink_start)
+        workspace = torch.empty(n, dtype=torch.uint8, device=q.device) if n > 0 else None
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().dense_sink_fwd(
         _ptr(q), _ptr(k), _ptr(v), B, T, H, D, sink_start, T - sink_start, _ptr(kb), kb_n,
-        float(softmax_scale), _ptr(out), _ptr(lse), _stream(q.device)))
+        float(softmax_scale), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, _stream(q.device)))
     return out
 
 

@@ -46,6 +46,9 @@ sa_status check_shape(int32_t B, int32_t T, int32_t H, int32_t D, int32_t sink_s
   const int64_t nb = (T + sa::kBlock - 1) / sa::kBlock;
   if ((int64_t)B * H * nb > INT32_MAX / 2)
     return fail(SA_ERR_UNSUPPORTED, "B*H*ceil(T/64) too large");
+  // K/V tiles are addressed with 32-bit byte offsets inside one batch
+  if ((int64_t)(T + sa::kBlock) * H * sa::kHeadDim * 2 > INT32_MAX)
+    return fail(SA_ERR_UNSUPPORTED, "T*H*256 bytes per batch must stay below 2 GiB");
   return SA_OK;
 }
 
@@ -105,6 +108,12 @@ size_t sa_route_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t sink_st
   const int32_t nvb = sa_num_sparse_blocks(T, sink_start);
   if (B <= 0 || H <= 0 || nvb <= 0) return 0;
   return 2ull * (size_t)B * (size_t)H * (size_t)nvb * sa::kHeadDim * sizeof(float);
+}
+
+size_t sa_dense_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t sink_start) {
+  const int32_t nvb = sa_num_sparse_blocks(T, sink_start);
+  if (B <= 0 || H <= 0 || T <= 0 || nvb < 0) return 0;
+  return sa::dense_workspace_bytes(B, H, sa_num_blocks(T), nvb);
 }
 
 const char *sa_last_error(void) { return g_err; }
@@ -201,7 +210,8 @@ sa_status sparse_attn_fwd(const void *q, const void *k, const void *v, int32_t B
 sa_status dense_sink_fwd(const void *q, const void *k, const void *v, int32_t B, int32_t T,
                          int32_t H, int32_t D, int32_t sink_start, int32_t sink_tokens,
                          const float *key_bias, int64_t key_bias_numel, float softmax_scale,
-                         void *out, float *lse, void *stream) {
+                         void *out, float *lse, void *workspace, size_t workspace_bytes,
+                         void *stream) {
   sa_status st = check_shape(B, T, H, D, sink_start, sink_tokens);
   if (st != SA_OK) return st;
   if ((st = check_bf16(q, "q")) != SA_OK) return st;
@@ -214,6 +224,8 @@ sa_status dense_sink_fwd(const void *q, const void *k, const void *v, int32_t B,
   if (lse != nullptr && !aligned(lse, 4)) return fail(SA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
   const int32_t nvb = sa_num_sparse_blocks(T, sink_start);
   if ((int64_t)nvb * sa::kBlock == T) return ok();
+  if (workspace_bytes > 0 && (workspace == nullptr || !aligned(workspace, 16)))
+    return fail(SA_ERR_WORKSPACE, "workspace must be a 16-byte aligned device pointer");
 
   sa::AttnArgs a{};
   a.q = q;
@@ -229,7 +241,7 @@ sa_status dense_sink_fwd(const void *q, const void *k, const void *v, int32_t B,
   a.nvb = nvb;
   a.max_sel = 0;
   a.scale_log2 = scale_log2;
-  hipError_t e = sa::launch_attn_dense(a, static_cast<hipStream_t>(stream));
+  hipError_t e = sa::launch_attn_dense(a, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(SA_ERR_HIP, "dense attention launch: %s", hipGetErrorString(e));
   return ok();
 }

@@ -35,7 +35,13 @@ struct AttnArgs {
 
 // Sparse rows [0, 64*nvb) over their block lists.
 hipError_t launch_attn_sparse(const AttnArgs &a, hipStream_t stream);
-// Dense rows [64*nvb, T) over all keys.
-hipError_t launch_attn_dense(const AttnArgs &a, hipStream_t stream);
+// Dense rows [64*nvb, T) over all keys.  With a workspace of at least
+// dense_workspace_bytes() the key range of each query block is split over
+// dense_splits() workgroups whose partial results are merged by a second
+// kernel; otherwise one workgroup walks all keys.
+hipError_t launch_attn_dense(const AttnArgs &a, void *workspace, size_t workspace_bytes,
+                             hipStream_t stream);
+int dense_splits(int B, int H, int nb, int nvb);
+size_t dense_workspace_bytes(int B, int H, int nb, int nvb);
 
 }  // namespace sa

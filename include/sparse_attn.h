@@ -78,6 +78,10 @@ int32_t sa_max_selected(int32_t T, int32_t sink_start, float ratio, int32_t radi
  * 2 * B * H * NVB * 128 * 4 bytes. */
 size_t sa_route_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t sink_start);
 
+/* Workspace bytes with which dense_sink_fwd splits the key range of each
+ * dense query block over several workgroups (0 when it would not split). */
+size_t sa_dense_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t sink_start);
+
 /* Message of the last failed call made by this thread ("" if none). */
 const char *sa_last_error(void);
 
@@ -181,6 +185,12 @@ sa_status sparse_attn_fwd(const void *q, const void *k, const void *v,
  *
  * out / lse     only rows [64*NVB, T) are written.  With 64*NVB == T
  *               nothing is enqueued.
+ * workspace     optional device scratch.  With workspace_bytes >=
+ *               sa_dense_workspace_bytes(B, T, H, sink_start) > 0 the keys of
+ *               each dense query block are split over several workgroups
+ *               and their partial softmax states merged by a second kernel
+ *               (same result up to fp32 summation order); with less (or 0,
+ *               workspace NULL) one workgroup walks all keys of a block.
  */
 sa_status dense_sink_fwd(const void *q, const void *k, const void *v,
                          int32_t B, int32_t T, int32_t H, int32_t D,
@@ -188,6 +198,7 @@ sa_status dense_sink_fwd(const void *q, const void *k, const void *v,
                          const float *key_bias, int64_t key_bias_numel,
                          float softmax_scale,
                          void *out, float *lse,
+                         void *workspace, size_t workspace_bytes,
                          void *stream);
 
 #ifdef __cplusplus

@@ -62,6 +62,8 @@ def test_shape_helpers_match_oracle(L):
     assert L.sa_topk_budget(10, float("nan")) == -1
     assert L.sa_route_workspace_bytes(1, 9505, 56, 9216) == 2 * 56 * 144 * 128 * 4
     assert L.sa_route_workspace_bytes(1, 9505, 56, 10) == 0
+    assert L.sa_dense_workspace_bytes(1, 9216, 56, 9216) == 0          # no dense rows
+    assert L.sa_dense_workspace_bytes(1, 9505, 56, 9216) % (64 * 130 * 4) == 0
 
 
 FAKE = ctypes.c_void_p(1 << 20)     # aligned, never dereferenced: validation fails first
@@ -87,11 +89,11 @@ def _fwd(L, **kw):
 
 def _dense(L, **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, B=1, T=1000, H=2, D=128, ss=900, st=100, bias=None,
-             bias_n=0, scale=0.0, out=FAKE, lse=None, stream=None)
+             bias_n=0, scale=0.0, out=FAKE, lse=None, ws=None, ws_bytes=0, stream=None)
     a.update(kw)
     return L.dense_sink_fwd(a["q"], a["k"], a["v"], a["B"], a["T"], a["H"], a["D"], a["ss"],
                             a["st"], a["bias"], a["bias_n"], a["scale"], a["out"], a["lse"],
-                            a["stream"])
+                            a["ws"], a["ws_bytes"], a["stream"])
 
 
 INVALID, UNSUPPORTED, WORKSPACE = 1, 2, 3
@@ -149,6 +151,9 @@ DENSE_CASES = [
     (dict(bias=FAKE, bias_n=999), INVALID, "exactly B*T"),
     (dict(st=99), INVALID, "sink_tokens"),
     (dict(lse=ctypes.c_void_p((1 << 20) + 1)), INVALID, "lse"),
+    (dict(ws=None, ws_bytes=1024), WORKSPACE, "workspace"),
+    (dict(ws=ctypes.c_void_p((1 << 20) + 4), ws_bytes=1024), WORKSPACE, "workspace"),
+    (dict(T=1 << 24, ss=(1 << 24) - 64, st=64, H=128), UNSUPPORTED, "2 GiB"),
 ]
 
 

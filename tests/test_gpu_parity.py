@@ -127,9 +127,30 @@ def test_ratio_one_sparse_bit_identical_to_dense_kernel():
     T = q.shape[1]
     idx, cnt = sa.sparse_attn_route(q, k, T, 1.0, 0)
     a = sa.sparse_attn_fwd(q, k, v, T, idx, cnt)
-    b = sa.dense_sink_fwd(q, k, v, 0)          # NVB = 0: all rows dense
+    b = sa.dense_sink_fwd(q, k, v, 0, workspace=None)   # NVB = 0: all rows dense, no key split
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+def test_dense_split_and_unsplit_agree_with_oracle():
+    """The dense rows with and without the split-KV workspace."""
+    import block_sparse_attention_05_amd as sa
+    wl = workloads.mid()
+    q, k, v = (x.cuda() for x in (wl.q, wl.k, wl.v))
+    T = q.shape[1]
+    bias = workloads.sink_key_bias(1, T, wl.sink_start, seed=3)
+    assert sa.sa_dense_workspace_bytes(1, T, 8, wl.sink_start) > 0
+    a = sa.dense_sink_fwd(q, k, v, wl.sink_start, key_bias=bias.cuda())
+    b = sa.dense_sink_fwd(q, k, v, wl.sink_start, key_bias=bias.cuda(), workspace=None)
+    torch.cuda.synchronize()
+    rows = np.arange(wl.sink_start, T)
+    qn, kn, vn = (to_np(x) for x in (wl.q, wl.k, wl.v))
+    for h in (0, 5):
+        want, _ = ora.dense_rows_output(qn, kn, vn, 0, h, rows, bias.numpy(), wl.sink_start // 64)
+        for got in (a, b):
+            mx, mean = err_stats(to_np(got[0, wl.sink_start:, h]), want)
+            log(f"[dense split/unsplit] h={h} max_abs={mx:.3e} mean_abs={mean:.3e}")
+            assert mx <= MAX_ABS and mean <= MEAN_ABS
 
 
 def test_zero_bias_bit_identical_to_no_bias():
