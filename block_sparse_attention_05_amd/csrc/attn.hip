@@ -9,27 +9,40 @@
 //
 // Workgroup = one 64-row query block of one (b, h) (or, on the dense path,
 // one key range of such a block: split-KV), four wavefronts: wave w owns query
-// rows 32*(w&1)..+31 and keys 32*(w>>1)..+31 of every tile, with its own
-// online-softmax state; the two key halves of each row are merged at the end.
-// Per 64-key tile of the block's list:
-//   * K and V tiles (64 keys x 256 B each) arrive with buffer loads: the
-//     tile's base goes into the per-lane offset, so keys past T fall outside
-//     the buffer's range and read as zero; they are staged in registers one
-//     tile ahead and written row-major to LDS with 16-byte chunks
-//     XOR-swizzled per row (conflict-free reads below);
+// rows 32*(w&1)..+31 and keys 32*(w>>1)..+31 of every 64-key tile, with its
+// own online-softmax state; the two key halves of each row are merged at the
+// end.
+//
+// Data movement.  K and V tiles (64 keys x 256 B) go from HBM/L2 straight to
+// LDS with buffer_load ... lds (no register staging): the tile's base is in
+// the per-lane offset, so keys past T fall outside the buffer range and read
+// as zero.  The LDS layout (see below) makes every operand read a constant
+// offset from one base and free of bank conflicts.
+//
+// Math per tile (per wave, 32 rows x 32 keys):
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16, K fragments from LDS, Q^T
 //     fragments resident in registers.  Each lane then owns one query row and
-//     16 keys per 32x32 tile, so the softmax row reductions stay in-lane
-//     apart from one exchange with lane ^ 32;
-//   * online softmax in base 2 (scale * log2 e folded into one FMA), lazy
+//     16 keys, so the row reductions are in-lane plus one v_permlane32_swap;
+//   * online softmax in base 2 (scale * log2 e folded into one FMA) with lazy
 //     rescaling: the running max moves only when a row's max grows by more
-//     than 8 (P <= 2^8 stays exact in range), the row sum is accumulated from
-//     the bf16-rounded P with v_dot2;
-//   * O^T += V^T P^T on the same MFMA: P^T fragments come straight from the
-//     S^T registers; V^T fragments come from the row-major V tile through
-//     ds_read_b64_tr_b16, which hands each lane one column of a 4-row block.
-//     Keys inside each 16-key group are contracted in the order
-//     {4g..4g+3, 8+4g..8+4g+3} (g = lane / 32) on both operands.
+//     than 8 (P <= 2^8), the row sum accumulates the bf16-rounded P with
+//     v_dot2;
+//   * O^T += V^T P^T: P^T fragments come straight from the S^T registers, V^T
+//     fragments from the row-major V tile through ds_read_b64_tr_b16 (each
+//     16-lane group reads a 4-row block, lane c receives column c).  Keys in a
+//     16-key group are contracted in the order {4g..4g+3, 8+4g..8+4g+3}
+//     (g = lane / 32) on both operands.
+//
+// Schedule.  K tiles are fetched two tiles ahead and V tiles one ahead (two
+// LDS slots each), so step j issues the MFMAs of S(j+1) = K(j+1) Q^T together
+// with the softmax VALU work of tile j, interleaved by sched_group_barrier,
+// then O += V(j) P(j).  The exponentials of tile j are
+// taken after the (rare, lazily triggered) rescale that follows the tile max.
+// Sink tiles (the only biased ones) always form a suffix of the tile
+// sequence and the only partial tile is the last one, so every steady-state
+// step is straight-line code.
+#include <type_traits>
+
 #include "device_util.h"
 #include "kernels.h"
 
@@ -40,14 +53,68 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4s __attribute__((ext_vector_type(4)));
 #define LDS_PTR(T, p) ((__attribute__((address_space(3))) T *)(p))
+
+template <int N>
+using Int = std::integral_constant<int, N>;
+template <bool B>
+using Bool = std::integral_constant<bool, B>;
 
 constexpr int kThreads = 256;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.0f;       // log2 units
 constexpr int kBufferFlags = 0x00020000;    // raw buffer, 32-bit data format
+constexpr int kVmcntZero = 0x0F70;          // s_waitcnt vmcnt(0), other counters untouched
+constexpr int kKOff = 0;                    // K ring: 2 x 16 KiB
+constexpr int kVOff = 32768;                // V ring: 2 x 16 KiB
+constexpr int kBOff = 65536;                // bias ring: 2 x 256 B
+constexpr int kLdsBytes = 65536 + 512;
+
+// sched_group_barrier instruction classes
+constexpr int kSchedVALU = 0x002;
+constexpr int kSchedMFMA = 0x008;
+constexpr int kSchedDSRead = 0x100;
+
+// Raw buffer resource: base, no stride, num_records bytes, raw 32-bit format.
+__device__ __forceinline__ i32x4s buffer_rsrc(const void *base, uint32_t num_bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4s r;
+  r[0] = (int)(uint32_t)a;
+  r[1] = (int)(uint32_t)(a >> 32) & 0xffff;
+  r[2] = (int)num_bytes;
+  r[3] = kBufferFlags;
+  return r;
+}
+
+// Global -> LDS copy of 16 (or 4) bytes per lane: lane l writes LDS byte
+// lds_base + 16*l (4*l).  Offsets at or past num_records read as zero.
+// Issued as inline asm so the compiler does not order later LDS reads of the
+// other ring slot behind it; the caller waits (vmcnt) before the barrier that
+// publishes the data.
+__device__ __forceinline__ void lds_dma_b128(const i32x4s &rsrc, uint32_t voffset, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voffset), "s"(rsrc), "s"(lds_base)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void lds_dma_b32(const i32x4s &rsrc, uint32_t voffset, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, 0 offen lds"
+               :
+               : "v"(voffset), "s"(rsrc), "s"(lds_base)
+               : "memory", "m0");
+}
+
+// x combined with the same register of lane ^ 32 (v_permlane32_swap).
+__device__ __forceinline__ float max_with_partner(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float add_with_partner(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 struct Params {
   const uint16_t *q, *k, *v;
@@ -63,15 +130,6 @@ struct Params {
   float scale_log2;
 };
 
-// Byte offset of (key row, 16-byte chunk) in the K tile.
-__device__ __forceinline__ int k_off(int row, int chunk) {
-  return row * 256 + ((chunk ^ (row & 15)) << 4);
-}
-// Byte offset of (key row, 16-byte chunk) in the V tile.
-__device__ __forceinline__ int v_off(int row, int chunk) {
-  return row * 256 + ((chunk ^ ((row & 3) << 2)) << 4);
-}
-
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   const bf16x2 v = {(__bf16)a, (__bf16)b};
   return __builtin_bit_cast(uint32_t, v);
@@ -80,10 +138,8 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 template <bool kDense>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_kernel(Params p) {
-  __shared__ __align__(16) unsigned char smem[32768 + 512];
-  unsigned char *ks = smem;            // K tile
-  unsigned char *vs = smem + 16384;    // V tile
-  float *bs = reinterpret_cast<float *>(smem + 32768);  // key bias of the tile, log2 units
+  // K ring (2 tiles) | V ring (2 tiles) | natural-log key bias ring (2 tiles)
+  __shared__ __align__(16) unsigned char smem[kLdsBytes];
 
   const int total = p.B * p.H * p.nqb * p.nsplit;
   const int w = xcd_remap(blockIdx.x, total);
@@ -120,72 +176,97 @@ void attn_fwd_kernel(Params p) {
     }
   }
 
-  // Tiles of this workgroup
+  // ---- tile sequence ------------------------------------------------------
+  // Sparse: the block list is held in VGPR lanes (lane j = entry cb + j of
+  // the current 64-entry chunk) and read with v_readlane, so no memory round
+  // trip sits between tiles.  Lists are ascending, so sink blocks (>= nvb)
+  // form a suffix.
+  const float *kbias = p.key_bias ? p.key_bias + (int64_t)b * T : nullptr;
   int t_begin = 0, t_end;
+  int n_plain;                  // tiles before the first biased (sink) tile
   const int32_t *list = nullptr;
+  int list_cb = 0;
+  int list_v = 0;
   if (kDense) {
     t_begin = split * p.tiles_per_split;
     t_end = t_begin + p.tiles_per_split;
     t_end = t_end < p.nb ? t_end : p.nb;
+    const int pe = p.nvb < t_end ? p.nvb : t_end;
+    n_plain = pe > t_begin ? pe - t_begin : 0;
   } else {
     const int64_t li = (int64_t)bh * p.nvb + qb;
     int n = p.block_cnt[li];
     t_end = n < 0 ? 0 : (n > p.max_sel ? p.max_sel : n);
     list = p.block_idx + li * p.max_sel;
+    list_v = lane < t_end ? list[lane] : 0;
+    // entries below nvb come first; count them over all 64-entry chunks
+    n_plain = 0;
+    for (int cb = 0; cb < t_end; cb += 64) {
+      const int e = cb + lane < t_end ? list[cb + lane] : p.nb;
+      n_plain += __popcll(__ballot(e < p.nvb));
+    }
   }
-  // First token of tile `it`; an invalid list entry maps to T (reads as zero,
-  // fully masked).
-  auto tile_key0 = [&](int it) -> int {
+  const int n = t_end - t_begin;
+  if (kbias == nullptr) n_plain = n;
+  // First token of tile t_begin + j (j non-decreasing between calls); an
+  // invalid list entry maps to T (reads as zero, fully masked).
+  auto tile_key0 = [&](int j) -> int {
+    const int it = t_begin + j;
     if (kDense) return it * kBlock;
-    const int kb = list[it];
+    if (it - list_cb >= 64) {
+      list_cb = it & ~63;
+      list_v = list_cb + lane < t_end ? list[list_cb + lane] : 0;
+    }
+    const int kb = __builtin_amdgcn_readlane(list_v, it - list_cb);
     return (kb >= 0 && kb < p.nb) ? kb * kBlock : T;
   };
 
-  // Buffer resources over this batch's K and V: offsets past T*row_bytes read 0.
+  // ---- loads --------------------------------------------------------------
   const uint32_t slab = (uint32_t)T * (uint32_t)row_bytes;
-  const __amdgpu_buffer_rsrc_t rk =
-      __builtin_amdgcn_make_buffer_rsrc((void *)(p.k + bbase), (short)0, (int)slab, kBufferFlags);
-  const __amdgpu_buffer_rsrc_t rv =
-      __builtin_amdgcn_make_buffer_rsrc((void *)(p.v + bbase), (short)0, (int)slab, kBufferFlags);
-  const float *kbias = p.key_bias ? p.key_bias + (int64_t)b * T : nullptr;
+  const i32x4s rk = buffer_rsrc(p.k + bbase, slab);
+  const i32x4s rv = buffer_rsrc(p.v + bbase, slab);
+  const i32x4s rb = buffer_rsrc(kbias ? (const void *)kbias : (const void *)p.k, kbias ? T * 4u : 0u);
   const int sink0 = p.nvb * kBlock;
 
-  // Register staging: thread loads rows st_row + 16*s, chunk st_chunk.
-  const int st_row = tid >> 4;
-  const int st_chunk = tid & 15;
-  const uint32_t lane_off = (uint32_t)(st_row * row_bytes + h * 256 + st_chunk * 16);
-  i32x4 kr[4], vr[4];
-  float br = 0.f;
-  auto load_tile = [&](int key0, bool biased) {
-    const uint32_t off0 = lane_off + (uint32_t)key0 * (uint32_t)row_bytes;
+  // LDS tile layout.  A tile slot (K or V) is 16 blocks of 1 KiB; block
+  // (rg, dr) = 4*rg + dr holds keys 16*rg .. +15 and channels 32*dr .. +31
+  // (64 B per key):
+  //   K block: chunk-major, 16-byte piece (key k, chunk c) at 16*(16*c + k%16);
+  //   V block: row-major,   16-byte piece (key k, chunk c) at 16*(4*(k%16) + c).
+  // With these, the K fragment of MFMA lane l (key 32kh + l%32, channels
+  // 16dc + 8(l/32) .. +7) sits at  k_rd + 512*dc  and the ds_read_b64_tr_b16
+  // source of lane l (key 32kh + 16kc + 8u + 4g + r, channels 32dt + 16dh + 4j
+  // .. +3; g = l/32, dh = (l/16)%2, r = (l%16)/4, j = l%4) at
+  // v_rd + 4096*kc + 1024*dt + 512*u: constant offsets from one base, and each
+  // group of 16 lanes touches 256 contiguous bytes (no bank conflicts).
+  // One buffer_load ... lds instruction writes 1 KiB (16 B per lane, in lane
+  // order): wave w loads blocks (rg = w, dr = s) for s = 0..3, each lane
+  // fetching the 16 global bytes of its piece (16 keys x 64 contiguous bytes
+  // per instruction).
+  const uint32_t k_lane = (uint32_t)((16 * wave + (lane & 15)) * row_bytes + h * 256 + (lane >> 4) * 16);
+  const uint32_t v_lane = (uint32_t)((16 * wave + (lane >> 2)) * row_bytes + h * 256 + (lane & 3) * 16);
+  const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>(LDS_PTR(unsigned char, smem));
+  const uint32_t wave_lds = (uint32_t)__builtin_amdgcn_readfirstlane(4096 * wave);
+  auto issue_k = [&](int key0, int slot) {
+    const uint32_t base = (uint32_t)key0 * (uint32_t)row_bytes + k_lane;
+    const uint32_t lb = lds0 + kKOff + (uint32_t)(slot * 16384) + wave_lds;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const uint32_t off = off0 + (uint32_t)(16 * s) * (uint32_t)row_bytes;
-      kr[s] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
-      vr[s] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
-    }
-    if (biased && tid < kBlock) {
-      const int key = key0 + tid;
-      br = key < T ? kbias[key] * kLog2e : 0.f;
-    }
+    for (int s4 = 0; s4 < 4; ++s4) lds_dma_b128(rk, base + 64 * s4, lb + 1024 * s4);
   };
-  auto store_tile = [&](bool biased) {
+  auto issue_v = [&](int key0, int slot) {
+    const uint32_t base = (uint32_t)key0 * (uint32_t)row_bytes + v_lane;
+    const uint32_t lb = lds0 + kVOff + (uint32_t)(slot * 16384) + wave_lds;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int row = st_row + 16 * s;
-      *reinterpret_cast<i32x4 *>(ks + k_off(row, st_chunk)) = kr[s];
-      *reinterpret_cast<i32x4 *>(vs + v_off(row, st_chunk)) = vr[s];
-    }
-    if (biased && tid < kBlock) bs[tid] = br;
+    for (int s4 = 0; s4 < 4; ++s4) lds_dma_b128(rv, base + 64 * s4, lb + 1024 * s4);
+    if (kbias != nullptr && key0 >= sink0 && key0 < T && wave == 0)
+      lds_dma_b32(rb, (uint32_t)(key0 + lane) * 4u, lds0 + kBOff + (uint32_t)(slot * 256));
   };
-  auto tile_biased = [&](int key0) { return kbias != nullptr && key0 >= sink0 && key0 < T; };
+  // operand read bases (bytes within a slot)
+  const uint32_t k_rd = (uint32_t)((2 * kh + (c32 >> 4)) * 4096 + g * 256 + (c32 & 15) * 16);
+  const uint32_t v_rd = (uint32_t)(2 * kh * 4096 + 64 * (4 * g + ((lane & 15) >> 2)) +
+                                   32 * ((lane >> 4) & 1) + 8 * (lane & 3));
 
-  // ds_read_b64_tr_b16 addressing for the V^T fragments
-  const int tr_i = lane & 15;
-  const int tr_r = tr_i >> 2;
-  const int tr_j = tr_i & 3;
-  const int tr_dh = (lane >> 4) & 1;
-
+  // ---- state --------------------------------------------------------------
   float m_used = -INFINITY;   // running max (log2 units) used for P
   float l_run = 0.f;          // this lane's share of the row sum
   f32x16 o[4];
@@ -196,67 +277,78 @@ void attn_fwd_kernel(Params p) {
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
   const float c = p.scale_log2;
 
-  if (t_begin < t_end) {
-    const int k0 = tile_key0(t_begin);
-    load_tile(k0, tile_biased(k0));
-  }
-  for (int it = t_begin; it < t_end; ++it) {
-    const int key0 = tile_key0(it);
-    const bool biased = tile_biased(key0);
-    __syncthreads();  // previous tile fully consumed
-    store_tile(biased);
-    __syncthreads();
-    if (it + 1 < t_end) {
-      const int k1 = tile_key0(it + 1);
-      load_tile(k1, tile_biased(k1));
-    }
+  // One pipeline step on tile j (scores in s_cur, V in slot VS) that also
+  // computes S(j+1) into s_nxt from K slot VS^1 when DO_QK.
+  auto step = [&](auto vs_c, auto biased_c, auto masked_c, auto do_qk_c, f32x16 &s_cur,
+                  f32x16 &s_nxt, int key0) {
+    constexpr int VS = decltype(vs_c)::value;
+    constexpr bool BIASED = decltype(biased_c)::value;
+    constexpr bool MASKED = decltype(masked_c)::value;
+    constexpr bool DO_QK = decltype(do_qk_c)::value;
+    const unsigned char *vbuf = smem + kVOff + VS * 16384;
+    const unsigned char *kbuf = smem + kKOff + (VS ^ 1) * 16384;
+    const float *bs = reinterpret_cast<const float *>(smem + kBOff + VS * 256);
 
-    // S^T = K Q^T over this wave's 32 keys
-    f32x16 s;
+    // S(j+1) MFMAs, issued in two groups so that they overlap the max phase
+    // and the exponential phase of tile j.
+    auto qk_part = [&](auto lo_c, auto hi_c) {
+      constexpr int LO = decltype(lo_c)::value;
+      constexpr int HI = decltype(hi_c)::value;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s[r] = 0.f;
-    {
-      const int row = 32 * kh + c32;
-#pragma unroll
-      for (int dc = 0; dc < 8; ++dc) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(ks + k_off(row, 2 * dc + g));
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[dc], s, 0, 0, 0);
+      for (int dc = LO; dc < HI; ++dc) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(kbuf + k_rd + 512 * dc);
+        s_nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[dc], s_nxt, 0, 0, 0);
       }
-    }
-    const int kbase = key0 + 32 * kh + 4 * g;   // key of s[r] = kbase + 8*(r/4) + r%4
+    };
 
-    // Keys past T (only in the last, partial block) are masked.
-    if (key0 + kBlock > T) {
+    // -- block A: max of tile j (+ first S(j+1) MFMAs) --
+    if (DO_QK) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s_nxt[r] = 0.f;
+      qk_part(Int<0>{}, Int<3>{});
+    }
+    if (MASKED) {
+      const int kbase = key0 + 32 * kh + 4 * g;   // key of s[r] = kbase + 8*(r/4) + r%4
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        if (kbase + 8 * (r >> 2) + (r & 3) >= T) s[r] = -INFINITY;
+        if (kbase + 8 * (r >> 2) + (r & 3) >= T) s_cur[r] = -INFINITY;
     }
-    // Logit in log2 units: s*c (+ beta2 on sink tiles).  With a bias the
-    // exponent is formed as fma(s, c, beta2 - m), so beta2 = 0 reproduces the
-    // unbiased fma(s, c, -m) bit for bit.
-    float bv[16];
+    // Logits in log2 units: s*c (+ beta2 on sink tiles).  The bias is read
+    // from LDS in both phases (instead of being held in registers) and the
+    // exponent is formed as fma(s, c, beta2 - m), so that beta2 = 0 reproduces
+    // the unbiased fma(s, c, -m) bit for bit.
+    auto bias4 = [&](int q4) {
+      const float4 b4 = *reinterpret_cast<const float4 *>(bs + 32 * kh + 8 * q4 + 4 * g);
+      return make_float4(b4.x * kLog2e, b4.y * kLog2e, b4.z * kLog2e, b4.w * kLog2e);
+    };
     float mt;  // tile max of this lane's logits, log2 units
-    if (biased) {
+    if (BIASED) {
+      mt = -INFINITY;
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const float4 b4 = *reinterpret_cast<const float4 *>(bs + 32 * kh + 8 * q4 + 4 * g);
-        bv[4 * q4 + 0] = b4.x;
-        bv[4 * q4 + 1] = b4.y;
-        bv[4 * q4 + 2] = b4.z;
-        bv[4 * q4 + 3] = b4.w;
+        const float4 bq = bias4(q4);
+        mt = fmaxf(mt, __builtin_fmaf(s_cur[4 * q4 + 0], c, bq.x));
+        mt = fmaxf(mt, __builtin_fmaf(s_cur[4 * q4 + 1], c, bq.y));
+        mt = fmaxf(mt, __builtin_fmaf(s_cur[4 * q4 + 2], c, bq.z));
+        mt = fmaxf(mt, __builtin_fmaf(s_cur[4 * q4 + 3], c, bq.w));
       }
-      mt = __builtin_fmaf(s[0], c, bv[0]);
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mt = fmaxf(mt, __builtin_fmaf(s[r], c, bv[r]));
     } else {
-      float mx = s[0];
+      float mx = s_cur[0];
 #pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s_cur[r]);
       mt = mx * c;
     }
-    mt = fmaxf(mt, shfl_xor_f32(mt, 32));
+    mt = max_with_partner(mt);
+    if (DO_QK) {
+#pragma unroll
+      for (int i = 0; i < 3; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedVALU, 4, 0);
+      }
+    }
 
-    // Lazy rescale: move the running max only when it grows by > slack.
+    // -- rare: a row max grew past the slack: rescale --
     if (__any(mt > m_used + kRescaleSlack)) {
       const float m_new = fmaxf(m_used, mt);
       const float alpha = __builtin_amdgcn_exp2f(m_used - m_new);  // 0 when m_used = -inf
@@ -269,44 +361,129 @@ void attn_fwd_kernel(Params p) {
     }
     const float m_sub = (m_used == -INFINITY) ? 0.f : m_used;
 
-    // P = 2^(logit - m) in bf16; row sum from the rounded values.
+    // -- block B: P of tile j (+ remaining S(j+1) MFMAs) --
+    if (DO_QK) qk_part(Int<3>{}, Int<8>{});
     bf16x8 pf[2];
 #pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-      float x0, x1;
-      if (biased) {
-        x0 = __builtin_fmaf(s[r], c, bv[r] - m_sub);
-        x1 = __builtin_fmaf(s[r + 1], c, bv[r + 1] - m_sub);
+    for (int q4 = 0; q4 < 4; ++q4) {
+      float e[4];
+      if (BIASED) {
+        const float4 bq = bias4(q4);
+        e[0] = __builtin_fmaf(s_cur[4 * q4 + 0], c, bq.x - m_sub);
+        e[1] = __builtin_fmaf(s_cur[4 * q4 + 1], c, bq.y - m_sub);
+        e[2] = __builtin_fmaf(s_cur[4 * q4 + 2], c, bq.z - m_sub);
+        e[3] = __builtin_fmaf(s_cur[4 * q4 + 3], c, bq.w - m_sub);
       } else {
-        x0 = __builtin_fmaf(s[r], c, -m_sub);
-        x1 = __builtin_fmaf(s[r + 1], c, -m_sub);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) e[u] = __builtin_fmaf(s_cur[4 * q4 + u], c, -m_sub);
       }
-      const bf16x2 pk = {(__bf16)__builtin_amdgcn_exp2f(x0), (__bf16)__builtin_amdgcn_exp2f(x1)};
-      l_run = __builtin_amdgcn_fdot2_f32_bf16(pk, ones, l_run, false);
-      pf[r >> 3][r & 7] = pk[0];
-      pf[r >> 3][(r & 7) + 1] = pk[1];
+#pragma unroll
+      for (int u = 0; u < 4; u += 2) {
+        const int r = 4 * q4 + u;
+        const bf16x2 pk = {(__bf16)__builtin_amdgcn_exp2f(e[u]), (__bf16)__builtin_amdgcn_exp2f(e[u + 1])};
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(pk, ones, l_run, false);
+        pf[r >> 3][r & 7] = pk[0];
+        pf[r >> 3][(r & 7) + 1] = pk[1];
+      }
+    }
+    if (DO_QK) {
+#pragma unroll
+      for (int i = 0; i < 5; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedVALU, 8, 0);
+      }
     }
 
-    // O^T += V^T P^T over this wave's 32 keys
+    // -- block C: O^T += V^T P^T over this wave's 32 keys --
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) {
-      const int row0 = 32 * kh + 16 * kc + 4 * g + tr_r;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
-        const int chunk = 4 * dt + 2 * tr_dh + (tr_j >> 1);
-        const int sub = (tr_j & 1) * 8;
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, vs + v_off(row0, chunk) + sub));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, vs + v_off(row0 + 8, chunk) + sub));
+        const unsigned char *src = vbuf + v_rd + 4096 * kc + 1024 * dt;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, src));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, src + 512));
         const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kc], o[dt], 0, 0, 0);
       }
     }
+  };
+
+  // ---- pipeline -----------------------------------------------------------
+  // K(j) lives in K slot j%2 and V(j) in V slot j%2; K is fetched two tiles
+  // ahead, V one ahead.  Step j issues V(j+1) and K(j+2) into the slots that
+  // step j-1 finished reading, and ends with the barrier that publishes them.
+  f32x16 s0, s1;
+  int k_cur = 0, k_nxt = 0;
+  if (n > 0) {
+    k_cur = tile_key0(0);
+    issue_k(k_cur, 0);
+    issue_v(k_cur, 0);
+    if (n > 1) {
+      k_nxt = tile_key0(1);
+      issue_k(k_nxt, 1);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(kVmcntZero);
+  __syncthreads();
+  if (n > 0) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s0[r] = 0.f;
+#pragma unroll
+    for (int dc = 0; dc < 8; ++dc) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8 *>(smem + kKOff + k_rd + 512 * dc);
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[dc], s0, 0, 0, 0);
+    }
+  }
+  // Step 0 refills K slot 0: every wave must be done reading it.
+  __syncthreads();
+
+  // Steady-state step j < n-1 (S(j+1) computed); the last step is peeled and
+  // is the only one that masks keys past T.
+  auto run_step = [&](auto vs_c, f32x16 &s_cur, f32x16 &s_nxt, int j) {
+    const int key_j = k_cur;
+    issue_v(k_nxt, decltype(vs_c)::value ^ 1);
+    int k_nn = 0;
+    if (j + 2 < n) {
+      k_nn = tile_key0(j + 2);
+      issue_k(k_nn, decltype(vs_c)::value);
+    }
+    if (j >= n_plain)
+      step(vs_c, Bool<true>{}, Bool<false>{}, Bool<true>{}, s_cur, s_nxt, key_j);
+    else
+      step(vs_c, Bool<false>{}, Bool<false>{}, Bool<true>{}, s_cur, s_nxt, key_j);
+    k_cur = k_nxt;
+    k_nxt = k_nn;
+    __builtin_amdgcn_s_waitcnt(kVmcntZero);
+    __syncthreads();
+  };
+  auto last_step = [&](auto vs_c, f32x16 &s_cur, f32x16 &s_nxt) {
+    const int key_j = k_cur;
+    const bool masked = key_j + kBlock > T;
+    if (n - 1 >= n_plain) {
+      if (masked) step(vs_c, Bool<true>{}, Bool<true>{}, Bool<false>{}, s_cur, s_nxt, key_j);
+      else step(vs_c, Bool<true>{}, Bool<false>{}, Bool<false>{}, s_cur, s_nxt, key_j);
+    } else {
+      if (masked) step(vs_c, Bool<false>{}, Bool<true>{}, Bool<false>{}, s_cur, s_nxt, key_j);
+      else step(vs_c, Bool<false>{}, Bool<false>{}, Bool<false>{}, s_cur, s_nxt, key_j);
+    }
+    __syncthreads();
+  };
+  int j = 0;
+  for (; j + 2 < n; j += 2) {
+    run_step(Int<0>{}, s0, s1, j);
+    run_step(Int<1>{}, s1, s0, j + 1);
+  }
+  if (j + 1 < n) {
+    run_step(Int<0>{}, s0, s1, j);
+    last_step(Int<1>{}, s1, s0);
+  } else if (j < n) {
+    last_step(Int<0>{}, s0, s1);
   }
 
-  // Merge the two key halves of every row: waves 2,3 hand (m, l, O^T) to
-  // waves 0,1 through LDS.
-  float l_tot = l_run + shfl_xor_f32(l_run, 32);
-  __syncthreads();
+  // ---- merge the two key halves of every row ------------------------------
+  // waves 2,3 hand (m, l, O^T) to waves 0,1 through LDS.
+  float l_tot = add_with_partner(l_run);
   float4 *xo = reinterpret_cast<float4 *>(smem);              // [rw][16 quads][64 lanes]
   float2 *xml = reinterpret_cast<float2 *>(smem + 32768);     // [rw][32 rows]
   if (kh == 1) {

@@ -243,3 +243,13 @@ def test_h3_keybias_sampled():
 
 def test_long_sampled():
     _sampled_parity(workloads.long(), n_blocks=32, dense_heads=2, seed=2)
+
+
+def test_h3_deterministic_repeat():
+    """Full-size call repeated: outputs, LSE and lists must be bit-identical
+    (catches races between tile loads and LDS reads)."""
+    wl = workloads.h3(with_bias=True)
+    runs = [run_gpu(wl, scores=False) for _ in range(3)]
+    for r in runs[1:]:
+        for key in ("out", "lse", "idx", "cnt"):
+            assert torch.equal(runs[0][key], r[key]), key
