@@ -92,11 +92,26 @@ def main():
     ap.add_argument("--workload", default="h3", choices=["h3", "h3_bias", "mid", "long", "tiny"])
     ap.add_argument("--cpu-heads", type=int, default=24)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB three times (the known-size "
+                         "kernel that scales the FETCH_SIZE / WRITE_SIZE counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the routed attention "
               "path shards by head with no collective; run one process per GPU.", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_calibration:
+        # an elementwise kernel (y = 1 * x over fp32) rather than copy_, which
+        # may be served by a DMA engine that the shader counters do not see
+        n = args.copy_calibration << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
+        return
 
     import block_sparse_attention_05_amd as sa
     import workloads

@@ -186,7 +186,8 @@ void attn_fwd_kernel(Params p) {
   int n_plain;                  // tiles before the first biased (sink) tile
   const int32_t *list = nullptr;
   int list_cb = 0;
-  int list_v = 0;
+  int list_v = 0;   // entries list_cb .. +63
+  int list_nv = 0;  // entries list_cb + 64 .. +63, loaded one tile early
   if (kDense) {
     t_begin = split * p.tiles_per_split;
     t_end = t_begin + p.tiles_per_split;
@@ -208,16 +209,23 @@ void attn_fwd_kernel(Params p) {
   }
   const int n = t_end - t_begin;
   if (kbias == nullptr) n_plain = n;
-  // First token of tile t_begin + j (j non-decreasing between calls); an
-  // invalid list entry maps to T (reads as zero, fully masked).
+  // First token of tile t_begin + j; calls come with j = 0, 1, 2, ... in
+  // order.  An invalid list entry maps to T (reads as zero, fully masked).
+  // The next 64-entry chunk is loaded one call before it is needed, so that
+  // the end-of-step wait already covers it: a wait placed by the compiler at
+  // the use would also drain the K/V tile loads in flight.
   auto tile_key0 = [&](int j) -> int {
     const int it = t_begin + j;
     if (kDense) return it * kBlock;
     if (it - list_cb >= 64) {
-      list_cb = it & ~63;
-      list_v = list_cb + lane < t_end ? list[list_cb + lane] : 0;
+      list_cb += 64;
+      list_v = list_nv;
     }
     const int kb = __builtin_amdgcn_readlane(list_v, it - list_cb);
+    if (it - list_cb == 63 && list_cb + 64 < t_end) {
+      const int e = list_cb + 64 + lane;
+      list_nv = e < t_end ? list[e] : 0;
+    }
     return (kb >= 0 && kb < p.nb) ? kb * kBlock : T;
   };
 
@@ -230,20 +238,22 @@ void attn_fwd_kernel(Params p) {
 
   // LDS tile layout.  A tile slot (K or V) is 16 blocks of 1 KiB; block
   // (rg, dr) = 4*rg + dr holds keys 16*rg .. +15 and channels 32*dr .. +31
-  // (64 B per key):
-  //   K block: chunk-major, 16-byte piece (key k, chunk c) at 16*(16*c + k%16);
-  //   V block: row-major,   16-byte piece (key k, chunk c) at 16*(4*(k%16) + c).
-  // With these, the K fragment of MFMA lane l (key 32kh + l%32, channels
-  // 16dc + 8(l/32) .. +7) sits at  k_rd + 512*dc  and the ds_read_b64_tr_b16
-  // source of lane l (key 32kh + 16kc + 8u + 4g + r, channels 32dt + 16dh + 4j
-  // .. +3; g = l/32, dh = (l/16)%2, r = (l%16)/4, j = l%4) at
-  // v_rd + 4096*kc + 1024*dt + 512*u: constant offsets from one base, and each
-  // group of 16 lanes touches 256 contiguous bytes (no bank conflicts).
-  // One buffer_load ... lds instruction writes 1 KiB (16 B per lane, in lane
-  // order): wave w loads blocks (rg = w, dr = s) for s = 0..3, each lane
-  // fetching the 16 global bytes of its piece (16 keys x 64 contiguous bytes
-  // per instruction).
-  const uint32_t k_lane = (uint32_t)((16 * wave + (lane & 15)) * row_bytes + h * 256 + (lane >> 4) * 16);
+  // (64 B per key), row-major with 16-byte pieces (key k, chunk c):
+  //   K block: piece (k, c) at 16*(4*k' + (c ^ ((k' >> 1) & 3))), k' = k%16;
+  //   V block: piece (k, c) at 16*(4*k' + c).
+  // Every 4 consecutive lanes of one buffer_load ... lds instruction (which
+  // writes 16 B per lane in lane order) then fetch the 64 contiguous global
+  // bytes of one key, so an instruction touches 16 half cache lines.  The K
+  // swizzle spreads each group of 8 lanes of the MFMA fragment read (keys
+  // k'..k'+7, one chunk) over all 32 banks.  With these, the K fragment of
+  // MFMA lane l (key 32kh + l%32, channels 16dc + 8(l/32) .. +7) sits at
+  // k_rd[dc%2] + 1024*(dc/2), and the ds_read_b64_tr_b16 source of lane l
+  // (key 32kh + 16kc + 8u + 4g + r, channels 32dt + 16dh + 4j .. +3; g = l/32,
+  // dh = (l/16)%2, r = (l%16)/4, j = l%4) at v_rd + 4096*kc + 1024*dt + 512*u:
+  // constant offsets from a few bases, free of bank conflicts.  Wave w loads
+  // blocks (rg = w, dr = s) for s = 0..3.
+  const uint32_t k_lane = (uint32_t)((16 * wave + (lane >> 2)) * row_bytes + h * 256 +
+                                     16 * ((lane & 3) ^ ((lane >> 3) & 3)));
   const uint32_t v_lane = (uint32_t)((16 * wave + (lane >> 2)) * row_bytes + h * 256 + (lane & 3) * 16);
   const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>(LDS_PTR(unsigned char, smem));
   const uint32_t wave_lds = (uint32_t)__builtin_amdgcn_readfirstlane(4096 * wave);
@@ -262,7 +272,10 @@ void attn_fwd_kernel(Params p) {
       lds_dma_b32(rb, (uint32_t)(key0 + lane) * 4u, lds0 + kBOff + (uint32_t)(slot * 256));
   };
   // operand read bases (bytes within a slot)
-  const uint32_t k_rd = (uint32_t)((2 * kh + (c32 >> 4)) * 4096 + g * 256 + (c32 & 15) * 16);
+  const uint32_t k_row = (uint32_t)((2 * kh + (c32 >> 4)) * 4096 + 64 * (c32 & 15));
+  const uint32_t k_sw = (uint32_t)((c32 >> 1) & 3);
+  const uint32_t k_rd0 = k_row + 16 * ((uint32_t)g ^ k_sw);         // dc even: chunk g
+  const uint32_t k_rd1 = k_row + 16 * ((uint32_t)(2 + g) ^ k_sw);   // dc odd: chunk 2 + g
   const uint32_t v_rd = (uint32_t)(2 * kh * 4096 + 64 * (4 * g + ((lane & 15) >> 2)) +
                                    32 * ((lane >> 4) & 1) + 8 * (lane & 3));
 
@@ -296,7 +309,7 @@ void attn_fwd_kernel(Params p) {
       constexpr int HI = decltype(hi_c)::value;
 #pragma unroll
       for (int dc = LO; dc < HI; ++dc) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(kbuf + k_rd + 512 * dc);
+        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(kbuf + ((dc & 1) ? k_rd1 : k_rd0) + 1024 * (dc >> 1));
         s_nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[dc], s_nxt, 0, 0, 0);
       }
     };
@@ -431,7 +444,7 @@ void attn_fwd_kernel(Params p) {
     for (int r = 0; r < 16; ++r) s0[r] = 0.f;
 #pragma unroll
     for (int dc = 0; dc < 8; ++dc) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8 *>(smem + kKOff + k_rd + 512 * dc);
+      const bf16x8 a = *reinterpret_cast<const bf16x8 *>(smem + kKOff + ((dc & 1) ? k_rd1 : k_rd0) + 1024 * (dc >> 1));
       s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[dc], s0, 0, 0, 0);
     }
   }
@@ -440,7 +453,7 @@ void attn_fwd_kernel(Params p) {
 
   // Steady-state step j < n-1 (S(j+1) computed); the last step is peeled and
   // is the only one that masks keys past T.
-  auto run_step = [&](auto vs_c, f32x16 &s_cur, f32x16 &s_nxt, int j) {
+  auto run_step = [&](auto vs_c, auto biased, f32x16 &s_cur, f32x16 &s_nxt, int j) {
     const int key_j = k_cur;
     issue_v(k_nxt, decltype(vs_c)::value ^ 1);
     int k_nn = 0;
@@ -448,10 +461,7 @@ void attn_fwd_kernel(Params p) {
       k_nn = tile_key0(j + 2);
       issue_k(k_nn, decltype(vs_c)::value);
     }
-    if (j >= n_plain)
-      step(vs_c, Bool<true>{}, Bool<false>{}, Bool<true>{}, s_cur, s_nxt, key_j);
-    else
-      step(vs_c, Bool<false>{}, Bool<false>{}, Bool<true>{}, s_cur, s_nxt, key_j);
+    step(vs_c, biased, Bool<false>{}, Bool<true>{}, s_cur, s_nxt, key_j);
     k_cur = k_nxt;
     k_nxt = k_nn;
     __builtin_amdgcn_s_waitcnt(kVmcntZero);
@@ -469,13 +479,28 @@ void attn_fwd_kernel(Params p) {
     }
     __syncthreads();
   };
+  // Steps j < n_plain are unbiased and the rest biased.  Each loop body holds
+  // one step variant only: a runtime choice between the two inside a loop
+  // makes the compiler route the O accumulators through copies every step.
   int j = 0;
+  for (; j + 2 < n && j + 2 <= n_plain; j += 2) {
+    run_step(Int<0>{}, Bool<false>{}, s0, s1, j);
+    run_step(Int<1>{}, Bool<false>{}, s1, s0, j + 1);
+  }
+  if (j + 2 < n && j < n_plain) {  // j + 1 == n_plain
+    run_step(Int<0>{}, Bool<false>{}, s0, s1, j);
+    run_step(Int<1>{}, Bool<true>{}, s1, s0, j + 1);
+    j += 2;
+  }
   for (; j + 2 < n; j += 2) {
-    run_step(Int<0>{}, s0, s1, j);
-    run_step(Int<1>{}, s1, s0, j + 1);
+    run_step(Int<0>{}, Bool<true>{}, s0, s1, j);
+    run_step(Int<1>{}, Bool<true>{}, s1, s0, j + 1);
   }
   if (j + 1 < n) {
-    run_step(Int<0>{}, s0, s1, j);
+    if (j >= n_plain)
+      run_step(Int<0>{}, Bool<true>{}, s0, s1, j);
+    else
+      run_step(Int<0>{}, Bool<false>{}, s0, s1, j);
     last_step(Int<1>{}, s1, s0);
   } else if (j < n) {
     last_step(Int<0>{}, s0, s1);
