@@ -107,7 +107,10 @@ int32_t sa_max_selected(int32_t T, int32_t sink_start, float ratio, int32_t radi
 size_t sa_route_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t sink_start) {
   const int32_t nvb = sa_num_sparse_blocks(T, sink_start);
   if (B <= 0 || H <= 0 || nvb <= 0) return 0;
-  return 2ull * (size_t)B * (size_t)H * (size_t)nvb * sa::kHeadDim * sizeof(float);
+  // query means in fp64, then key means in fp32, each over NVB rounded up to
+  // a multiple of 16 blocks
+  const size_t nvb16 = ((size_t)nvb + 15) / 16 * 16;
+  return (size_t)B * (size_t)H * nvb16 * sa::kHeadDim * (sizeof(double) + sizeof(float));
 }
 
 size_t sa_dense_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t sink_start) {
@@ -132,6 +135,9 @@ sa_status sparse_attn_route(const void *q, const void *k, int32_t B, int32_t T, 
   if (local_radius < 0) return fail(SA_ERR_INVALID_ARG, "local_radius must be >= 0");
   const int32_t nvb = sa_num_sparse_blocks(T, sink_start);
   const int32_t nb = sa_num_blocks(T);
+  if ((int64_t)B * H > 65535)
+    return fail(SA_ERR_UNSUPPORTED, "routing supports B*H up to 65535 (got %lld)",
+                (long long)B * H);
   if (nvb > sa::kMaxRouteBlocks)
     return fail(SA_ERR_UNSUPPORTED, "at most %d video blocks can be routed (got %d)",
                 sa::kMaxRouteBlocks, nvb);
@@ -152,8 +158,8 @@ sa_status sparse_attn_route(const void *q, const void *k, int32_t B, int32_t T, 
     return fail(SA_ERR_WORKSPACE, "workspace must be a 16-byte aligned device pointer");
 
   const int32_t budget = sa_topk_budget(nvb, topk_ratio);
-  float *qbar = static_cast<float *>(workspace);
-  float *kbar = qbar + (size_t)B * H * nvb * sa::kHeadDim;
+  double *qbar = static_cast<double *>(workspace);
+  float *kbar = reinterpret_cast<float *>(qbar + (size_t)B * H * (((size_t)nvb + 15) / 16 * 16) * sa::kHeadDim);
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = sa::launch_pool(q, k, qbar, kbar, B, T, H, nvb, s);
   if (e != hipSuccess) return fail(SA_ERR_HIP, "pool launch: %s", hipGetErrorString(e));

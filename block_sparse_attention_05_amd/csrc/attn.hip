@@ -196,13 +196,16 @@ void attn_fwd_kernel(Params p) {
     n_plain = pe > t_begin ? pe - t_begin : 0;
   } else {
     const int64_t li = (int64_t)bh * p.nvb + qb;
-    int n = p.block_cnt[li];
-    t_end = n < 0 ? 0 : (n > p.max_sel ? p.max_sel : n);
     list = p.block_idx + li * p.max_sel;
-    list_v = lane < t_end ? list[lane] : 0;
+    // The first 64 entries are read together with the count (the two loads
+    // do not depend on each other).
+    const int first = lane < p.max_sel ? list[lane] : 0;
+    const int n = p.block_cnt[li];
+    t_end = n < 0 ? 0 : (n > p.max_sel ? p.max_sel : n);
+    list_v = lane < t_end ? first : 0;
     // entries below nvb come first; count them over all 64-entry chunks
-    n_plain = 0;
-    for (int cb = 0; cb < t_end; cb += 64) {
+    n_plain = __popcll(__ballot(lane < t_end && list_v < p.nvb));
+    for (int cb = 64; cb < t_end; cb += 64) {
       const int e = cb + lane < t_end ? list[cb + lane] : p.nb;
       n_plain += __popcll(__ballot(e < p.nvb));
     }
@@ -236,48 +239,56 @@ void attn_fwd_kernel(Params p) {
   const i32x4s rb = buffer_rsrc(kbias ? (const void *)kbias : (const void *)p.k, kbias ? T * 4u : 0u);
   const int sink0 = p.nvb * kBlock;
 
-  // LDS tile layout.  A tile slot (K or V) is 16 blocks of 1 KiB; block
-  // (rg, dr) = 4*rg + dr holds keys 16*rg .. +15 and channels 32*dr .. +31
-  // (64 B per key), row-major with 16-byte pieces (key k, chunk c):
-  //   K block: piece (k, c) at 16*(4*k' + (c ^ ((k' >> 1) & 3))), k' = k%16;
-  //   V block: piece (k, c) at 16*(4*k' + c).
-  // Every 4 consecutive lanes of one buffer_load ... lds instruction (which
-  // writes 16 B per lane in lane order) then fetch the 64 contiguous global
-  // bytes of one key, so an instruction touches 16 half cache lines.  The K
-  // swizzle spreads each group of 8 lanes of the MFMA fragment read (keys
-  // k'..k'+7, one chunk) over all 32 banks.  With these, the K fragment of
-  // MFMA lane l (key 32kh + l%32, channels 16dc + 8(l/32) .. +7) sits at
-  // k_rd[dc%2] + 1024*(dc/2), and the ds_read_b64_tr_b16 source of lane l
-  // (key 32kh + 16kc + 8u + 4g + r, channels 32dt + 16dh + 4j .. +3; g = l/32,
-  // dh = (l/16)%2, r = (l%16)/4, j = l%4) at v_rd + 4096*kc + 1024*dt + 512*u:
-  // constant offsets from a few bases, free of bank conflicts.  Wave w loads
-  // blocks (rg = w, dr = s) for s = 0..3.
-  const uint32_t k_lane = (uint32_t)((16 * wave + (lane >> 2)) * row_bytes + h * 256 +
-                                     16 * ((lane & 3) ^ ((lane >> 3) & 3)));
-  const uint32_t v_lane = (uint32_t)((16 * wave + (lane >> 2)) * row_bytes + h * 256 + (lane & 3) * 16);
+  // LDS tile layout.  A tile slot (K or V, 64 keys x 256 B) is 16 blocks of
+  // 1 KiB; block 2*kg + hf holds keys 8*kg .. +7 and bytes 128*hf .. +127 of
+  // each key row, one 128-byte row per key, in 16-byte pieces (key k' = key%8,
+  // chunk c = 0..7) placed with an XOR swizzle:
+  //   K: piece (k', c) at 128*k' + 16*(c ^ k');
+  //   V: piece (k', c) at 128*k' + 16*(c ^ 2*(k' & 3)).
+  // One buffer_load ... lds instruction writes 1 KiB (16 B per lane, in lane
+  // order), so each group of 8 lanes fetches the full 128-byte cache line
+  // half of one key row (8 lines per instruction).  The swizzles make the
+  // MFMA operand reads conflict-free: each group of 8 lanes of the K
+  // fragment read (8 keys, one chunk) covers all 32 banks, and each 16-lane
+  // group of ds_read_b64_tr_b16 on V (4 keys x 32 B) covers them too.  With
+  // these, the K fragment of MFMA lane l (key 32kh + l%32, channels
+  // 16dc + 8(l/32) .. +7) sits at (k_rd0 ^ 32*(dc%4)) + 1024*(dc/4), and the
+  // ds_read_b64_tr_b16 source of lane l (key 32kh + 16kc + 8u + 4g + r,
+  // channels 32dt + 16dh + 4j .. +3; g = l/32, dh = (l/16)%2, r = (l%16)/4,
+  // j = l%4) at (v_rd0 ^ 64*(dt%2)) + 4096*kc + 2048*u + 1024*(dt/2).  Wave w loads
+  // blocks 4w .. 4w+3 (keys 16w .. +15).
+  const uint32_t k_lane = (uint32_t)((16 * wave + (lane >> 3)) * row_bytes + h * 256 +
+                                     16 * ((lane & 7) ^ (lane >> 3)));
+  const uint32_t v_lane = (uint32_t)((16 * wave + (lane >> 3)) * row_bytes + h * 256 +
+                                     16 * ((lane & 7) ^ (2 * ((lane >> 3) & 3))));
+  const uint32_t rows8 = (uint32_t)(8 * row_bytes);
   const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>(LDS_PTR(unsigned char, smem));
   const uint32_t wave_lds = (uint32_t)__builtin_amdgcn_readfirstlane(4096 * wave);
   auto issue_k = [&](int key0, int slot) {
     const uint32_t base = (uint32_t)key0 * (uint32_t)row_bytes + k_lane;
     const uint32_t lb = lds0 + kKOff + (uint32_t)(slot * 16384) + wave_lds;
 #pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) lds_dma_b128(rk, base + 64 * s4, lb + 1024 * s4);
+    for (int s4 = 0; s4 < 4; ++s4) lds_dma_b128(rk, base + (s4 >> 1) * rows8 + 128 * (s4 & 1), lb + 1024 * s4);
   };
   auto issue_v = [&](int key0, int slot) {
     const uint32_t base = (uint32_t)key0 * (uint32_t)row_bytes + v_lane;
     const uint32_t lb = lds0 + kVOff + (uint32_t)(slot * 16384) + wave_lds;
 #pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) lds_dma_b128(rv, base + 64 * s4, lb + 1024 * s4);
+    for (int s4 = 0; s4 < 4; ++s4) lds_dma_b128(rv, base + (s4 >> 1) * rows8 + 128 * (s4 & 1), lb + 1024 * s4);
     if (kbias != nullptr && key0 >= sink0 && key0 < T && wave == 0)
       lds_dma_b32(rb, (uint32_t)(key0 + lane) * 4u, lds0 + kBOff + (uint32_t)(slot * 256));
   };
   // operand read bases (bytes within a slot)
-  const uint32_t k_row = (uint32_t)((2 * kh + (c32 >> 4)) * 4096 + 64 * (c32 & 15));
-  const uint32_t k_sw = (uint32_t)((c32 >> 1) & 3);
-  const uint32_t k_rd0 = k_row + 16 * ((uint32_t)g ^ k_sw);         // dc even: chunk g
-  const uint32_t k_rd1 = k_row + 16 * ((uint32_t)(2 + g) ^ k_sw);   // dc odd: chunk 2 + g
-  const uint32_t v_rd = (uint32_t)(2 * kh * 4096 + 64 * (4 * g + ((lane & 15) >> 2)) +
-                                   32 * ((lane >> 4) & 1) + 8 * (lane & 3));
+  // The other operand bases differ by an XOR of the swizzled chunk bits:
+  // K chunk 2*(dc%4) + g lands at k_rd0 ^ (32*(dc%4)); V for odd dt at
+  // v_rd0 ^ 64.
+  uint32_t k_rd0, v_rd0;
+  {
+    const uint32_t kp = (uint32_t)(c32 & 7);
+    k_rd0 = (uint32_t)(2048 * (4 * kh + (c32 >> 3))) + 128 * kp + 16 * ((uint32_t)g ^ kp);
+    const uint32_t r = (uint32_t)((lane & 15) >> 2), dh = (uint32_t)((lane >> 4) & 1), j = (uint32_t)(lane & 3);
+    v_rd0 = (uint32_t)(8192 * kh + 512 * g) + 128 * r + 8 * (j & 1) + 16 * ((2 * dh + (j >> 1)) ^ (2 * r));
+  }
 
   // ---- state --------------------------------------------------------------
   float m_used = -INFINITY;   // running max (log2 units) used for P
@@ -309,7 +320,7 @@ void attn_fwd_kernel(Params p) {
       constexpr int HI = decltype(hi_c)::value;
 #pragma unroll
       for (int dc = LO; dc < HI; ++dc) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(kbuf + ((dc & 1) ? k_rd1 : k_rd0) + 1024 * (dc >> 1));
+        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(kbuf + (k_rd0 ^ (32u * (dc & 3))) + 1024 * (dc >> 2));
         s_nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[dc], s_nxt, 0, 0, 0);
       }
     };
@@ -413,9 +424,9 @@ void attn_fwd_kernel(Params p) {
     for (int kc = 0; kc < 2; ++kc) {
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
-        const unsigned char *src = vbuf + v_rd + 4096 * kc + 1024 * dt;
+        const unsigned char *src = vbuf + ((dt & 1) ? (v_rd0 ^ 64u) : v_rd0) + 4096 * kc + 1024 * (dt >> 1);
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, src));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, src + 512));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, src + 2048));
         const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kc], o[dt], 0, 0, 0);
       }
@@ -444,7 +455,7 @@ void attn_fwd_kernel(Params p) {
     for (int r = 0; r < 16; ++r) s0[r] = 0.f;
 #pragma unroll
     for (int dc = 0; dc < 8; ++dc) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8 *>(smem + kKOff + ((dc & 1) ? k_rd1 : k_rd0) + 1024 * (dc >> 1));
+      const bf16x8 a = *reinterpret_cast<const bf16x8 *>(smem + kKOff + (k_rd0 ^ (32u * (dc & 3))) + 1024 * (dc >> 2));
       s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[dc], s0, 0, 0, 0);
     }
   }

@@ -14,11 +14,11 @@ constexpr int kMaxRouteBlocks = 1024;  // widest per-row sort in the route kerne
 
 // Mean of every complete 64-token video block of Q and K:
 // qbar/kbar fp32 [B, H, nvb, 128].
-hipError_t launch_pool(const void *q, const void *k, float *qbar, float *kbar,
+hipError_t launch_pool(const void *q, const void *k, double *qbar, float *kbar,
                        int B, int T, int H, int nvb, hipStream_t stream);
 
 // Route scores, Top-K and list emission for every (b, h, query block < nvb).
-hipError_t launch_route(const float *qbar, const float *kbar, int B, int H, int nvb,
+hipError_t launch_route(const double *qbar, const float *kbar, int B, int H, int nvb,
                         int nb, int budget, int radius, int max_sel, int32_t *block_idx,
                         int32_t *block_cnt, float *scores, hipStream_t stream);
 

@@ -5,11 +5,13 @@
 // Sol-Attn producers", Summary).
 //
 // HBM-bound: every bf16 element of Q and K in video blocks is read once.
-// One thread owns one 16-byte chunk (8 channels) of one (batch, head) row and
-// walks the 64 tokens of its block; a wavefront reads 1 KiB of contiguous
-// row per token, so every load is fully coalesced.  Sums are kept in fp64:
-// adding 64 bf16 values is exact there, so the mean (a division by 64) is the
-// correctly rounded fp32 value whatever the summation order.
+// A workgroup owns 16 consecutive blocks (one tile of the route kernel) of
+// one (batch, head, Q|K); thread (blk, c8) walks the 64 tokens of block blk,
+// reading 16 bytes (8 channels) per token, so each group of 16 threads reads
+// one contiguous 256-byte head row.  Sums are kept in fp64: adding 64 bf16
+// values is exact there, so the mean (a division by 64) is the correctly
+// rounded fp32 value whatever the summation order.  The workgroup writes its
+// tile of means whole, in the route kernel's operand order.
 #include "device_util.h"
 #include "kernels.h"
 
@@ -19,16 +21,19 @@ namespace {
 constexpr int kPoolThreads = 256;
 
 __global__ __launch_bounds__(kPoolThreads) void pool_means_kernel(
-    const uint4 *__restrict__ q, const uint4 *__restrict__ k, float *__restrict__ qbar,
+    const uint4 *__restrict__ q, const uint4 *__restrict__ k, double *__restrict__ qbar,
     float *__restrict__ kbar, int T, int H, int nvb) {
-  const int chunks = H * (kHeadDim / 8);  // 16-byte chunks per token row
-  const int c = blockIdx.x * kPoolThreads + threadIdx.x;
-  const int i = blockIdx.y;               // video block
+  const int tile = blockIdx.x;
+  const int h = blockIdx.y;
   const int b = blockIdx.z >> 1;
   const bool is_k = (blockIdx.z & 1) != 0;
-  if (c >= chunks) return;
+  const int blk = threadIdx.x >> 4;       // block within the tile
+  const int c8 = threadIdx.x & 15;        // 16-byte chunk of the head row
+  const int i = 16 * tile + blk;          // video block
+  if (i >= nvb) return;
 
-  const uint4 *src = (is_k ? k : q) + ((int64_t)b * T + (int64_t)i * kBlock) * chunks + c;
+  const int chunks = H * (kHeadDim / 8);  // 16-byte chunks per token row
+  const uint4 *src = (is_k ? k : q) + ((int64_t)b * T + (int64_t)i * kBlock) * chunks + h * (kHeadDim / 8) + c8;
   double acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.0;
@@ -46,30 +51,37 @@ __global__ __launch_bounds__(kPoolThreads) void pool_means_kernel(
     acc[7] += (double)bf16_hi(w.w);
   }
 
-  const int h = c / (kHeadDim / 8);
-  const int d0 = (c % (kHeadDim / 8)) * 8;
-  float *dst = (is_k ? kbar : qbar) + (((int64_t)b * H + h) * nvb + i) * kHeadDim + d0;
+  const int d0 = 8 * c8;
   const double inv = 1.0 / kBlock;  // exact power of two
-  float4 lo, hi;
-  lo.x = (float)(acc[0] * inv);
-  lo.y = (float)(acc[1] * inv);
-  lo.z = (float)(acc[2] * inv);
-  lo.w = (float)(acc[3] * inv);
-  hi.x = (float)(acc[4] * inv);
-  hi.y = (float)(acc[5] * inv);
-  hi.z = (float)(acc[6] * inv);
-  hi.w = (float)(acc[7] * inv);
-  reinterpret_cast<float4 *>(dst)[0] = lo;
-  reinterpret_cast<float4 *>(dst)[1] = hi;
+  float m[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) m[e] = (float)(acc[e] * inv);
+  // Means are stored in the operand order of the route kernel's fp64 MFMA
+  // (16 blocks per tile; contraction step st = d % 32 for lane 16*(d/32) +
+  // block % 16): 16-byte pieces that a wavefront then reads contiguously.
+  const int nt = (nvb + 15) >> 4;
+  const int64_t tile_id = ((int64_t)b * H + h) * nt + tile;
+  const int lane = 16 * (d0 >> 5) + blk;
+  const int st0 = d0 & 31;
+  if (is_k) {  // fp32, 4 steps per piece: [tile][st / 4][lane][st % 4]
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+      reinterpret_cast<float4 *>(kbar)[(tile_id * 8 + (st0 >> 2) + x) * 64 + lane] =
+          make_float4(m[4 * x], m[4 * x + 1], m[4 * x + 2], m[4 * x + 3]);
+  } else {  // fp64 copies, 2 steps per piece: [tile][st / 2][lane][st % 2]
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+      reinterpret_cast<double2 *>(qbar)[(tile_id * 16 + (st0 >> 1) + x) * 64 + lane] =
+          make_double2((double)m[2 * x], (double)m[2 * x + 1]);
+  }
 }
 
 }  // namespace
 
-hipError_t launch_pool(const void *q, const void *k, float *qbar, float *kbar, int B, int T,
+hipError_t launch_pool(const void *q, const void *k, double *qbar, float *kbar, int B, int T,
                        int H, int nvb, hipStream_t stream) {
   if (nvb <= 0) return hipSuccess;
-  const int chunks = H * (kHeadDim / 8);
-  dim3 grid((chunks + kPoolThreads - 1) / kPoolThreads, nvb, 2 * B);
+  dim3 grid((nvb + 15) / 16, H, 2 * B);
   hipLaunchKernelGGL(pool_means_kernel, grid, dim3(kPoolThreads), 0, stream,
                      static_cast<const uint4 *>(q), static_cast<const uint4 *>(k), qbar, kbar, T,
                      H, nvb);

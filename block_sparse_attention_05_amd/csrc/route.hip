@@ -7,190 +7,257 @@
 // chunked Sol-Attn producers", Tests and source audit: sink blocks go straight
 // into the exact list and are never routed candidates.
 //
-// One workgroup (4 wavefronts) serves kRows query blocks of one (b, h):
-//  1. scores s_ij for its rows against every key block j < nvb.  fp32 x fp32
-//     products are exact in fp64, so the fp64 dot product rounded once to fp32
-//     is the fp32 score of the exact value (up to fp64 rounding of the sum).
-//  2. per row, one wavefront sorts 64-bit keys (descending-score bits, block
-//     index) with a bitonic network held in registers (E keys per lane,
-//     64*E >= nvb); forced blocks get the largest key so they never compete.
-//  3. the first k keys flag their blocks; forced blocks are flagged too; a
-//     ballot/popcount scan emits the flagged blocks in ascending order, then
-//     the sink blocks [nvb, nb), then -1 padding.
+// One workgroup (8 wavefronts) serves 16 query blocks of one (b, h):
+//  1. scores s_ij for its 16 rows against every key block j < nvb on fp64
+//     MFMA (v_mfma_f64_16x16x4f64), one 16-key tile per accumulator.
+//     fp32 x fp32 products are exact in fp64, so the fp64 dot product
+//     rounded once to fp32 is the fp32 score of the exact value (up to fp64
+//     rounding of the sum, whose order differs from a plain loop).  Scores go
+//     to LDS.
+//  2. per row (two per wavefront), the k best candidates under (score desc,
+//     index asc) by a most-significant-bit-first radix select on
+//     order-preserving 32-bit score keys: one ballot count per bit halves the
+//     bucket that holds the k-th key, starting below the bits shared by all
+//     candidates and stopping as soon as the bucket is taken whole; ties left
+//     at the last bit go to the lowest block indices.
+//  3. a ballot/popcount scan emits selected and forced blocks in ascending
+//     order, then the sink blocks [nvb, nb), then -1 padding.
 #include "device_util.h"
 #include "kernels.h"
 
 namespace sa {
 namespace {
 
-constexpr int kRouteThreads = 256;
-constexpr int kRows = 8;  // query blocks per workgroup
+constexpr int kRouteThreads = 512;
+constexpr int kRouteWaves = kRouteThreads / 64;
+constexpr int kRouteRows = 16;  // query blocks per workgroup (one MFMA tile)
+constexpr int kTournamentMax = 32;  // largest budget selected by repeated argmax
 
-// fp32 bits -> unsigned key that sorts ascending as the float sorts
-// descending.  -0.0 is mapped like +0.0.
-__device__ __forceinline__ uint32_t desc_key(float s) {
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
+// fp32 -> unsigned key with the same order (larger score, larger key); -0.0
+// is mapped like +0.0.  Every finite score maps above 0.
+__device__ __forceinline__ uint32_t order_key(float s) {
   uint32_t b = __float_as_uint(s);
   if (b == 0x80000000u) b = 0u;
-  const uint32_t asc = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-  return ~asc;
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-// Ascending bitonic sort of the 64*E keys of one wavefront; element x lives
-// in lane x % 64, slot x / 64.
-template <int E>
-__device__ __forceinline__ void wave_bitonic_sort(uint64_t (&key)[E], int lane) {
-  constexpr int kLogP = (E == 1) ? 6 : (E == 2) ? 7 : (E == 4) ? 8 : (E == 8) ? 9 : 10;
+__device__ __forceinline__ int popc(uint64_t m) { return __popcll(m); }
+
+// Mask of the bits above `bit` (bit in [-1, 32]: all bits for -1, none for
+// 31 and up).
+__device__ __forceinline__ uint32_t high_bits(int bit) {
+  return bit >= 31 ? 0u : (bit < 0 ? 0xffffffffu : ~((2u << bit) - 1u));
+}
+
+// Wave-wide max / min of unsigned values (DPP scan inside rows of 16 lanes,
+// then row broadcasts; lane 63 ends with the result).
+template <bool kMax>
+__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t x) {
+  auto op = [](uint32_t a, uint32_t b) { return kMax ? (a > b ? a : b) : (a < b ? a : b); };
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x111, 0xf, 0xf, false));  // row_shr:1
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x112, 0xf, 0xf, false));  // row_shr:2
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x114, 0xf, 0xf, false));  // row_shr:4
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x118, 0xf, 0xf, false));  // row_shr:8
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x142, 0xa, 0xf, false));  // row_bcast:15
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x143, 0xc, 0xf, false));  // row_bcast:31
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+}
+
+// Score tiles: query rows 16*rb .. +15 against key tiles t = wave, wave +
+// kRouteWaves, ...  MFMA lane l holds A[l%16][l/16] = q[16rb + l%16][d] and
+// B[l/16][l%16] = k[16t + l%16][d] with d = 32*(l/16) + step (the 128-term
+// contraction is summed in that order); D register r of lane l is the score
+// of row 4r + l/16 and key 16t + l%16.  The means arrive in exactly this
+// operand order (see the pooling kernel), so every load is contiguous across
+// the wavefront.  Rows and keys past nvb hold unused values that only reach
+// unused rows and columns of D.
+__device__ __forceinline__ void route_scores_tile(const double2 *__restrict__ qt,
+                                                  const float4 *__restrict__ kt, int nt,
+                                                  float *sc, int ld, int lane, int wave) {
+  const int g = lane >> 4, c = lane & 15;
+  for (int t = wave; t < nt; t += kRouteWaves) {
+    f64x4 acc0 = {0.0, 0.0, 0.0, 0.0}, acc1 = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-  for (int ls = 1; ls <= kLogP; ++ls) {
-    const int size = 1 << ls;
+    for (int half = 0; half < 2; ++half) {  // 16 contraction steps at a time
+      double a[16];
+      float bk[16];
 #pragma unroll
-    for (int lt = ls - 1; lt >= 0; --lt) {
-      const int stride = 1 << lt;
-      if (stride >= 64) {
-        const int es = stride >> 6;
+      for (int x = 0; x < 8; ++x) {
+        const double2 v = qt[(8 * half + x) * 64 + lane];
+        a[2 * x] = v.x;
+        a[2 * x + 1] = v.y;
+      }
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-          const int e2 = e ^ es;
-          if (e2 > e) {
-            const int x = e * 64 + lane;
-            const bool asc = (x & size) == 0;
-            const uint64_t a = key[e], c = key[e2];
-            const bool swap = asc ? (a > c) : (a < c);
-            key[e] = swap ? c : a;
-            key[e2] = swap ? a : c;
-          }
-        }
-      } else {
+      for (int x = 0; x < 4; ++x) {
+        const float4 v = kt[((int64_t)t * 8 + 4 * half + x) * 64 + lane];
+        bk[4 * x] = v.x;
+        bk[4 * x + 1] = v.y;
+        bk[4 * x + 2] = v.z;
+        bk[4 * x + 3] = v.w;
+      }
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-          const int x = e * 64 + lane;
-          const uint64_t other = shfl_xor_u64(key[e], stride);
-          const bool asc = (x & size) == 0;
-          const bool lower = (lane & stride) == 0;
-          const bool keep_min = (asc == lower);
-          const uint64_t mn = key[e] < other ? key[e] : other;
-          const uint64_t mx = key[e] < other ? other : key[e];
-          key[e] = keep_min ? mn : mx;
-        }
+      for (int st = 0; st < 16; st += 2) {  // two independent chains
+        acc0 = __builtin_amdgcn_mfma_f64_16x16x4f64(a[st], (double)bk[st], acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f64_16x16x4f64(a[st + 1], (double)bk[st + 1], acc1, 0, 0, 0);
       }
     }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sc[(4 * r + g) * ld + 16 * t + c] = (float)(acc0[r] + acc1[r]);
   }
+}
+
+// Small budgets: kk rounds of a wave-wide argmax over the keys not yet
+// taken (ties on the score key go to the lower block index j = 64e + lane).
+// Returns the taken slots as a bit mask per lane.
+template <int E>
+__device__ __forceinline__ uint32_t tournament_select(const uint32_t (&u)[E], int kk, int lane) {
+  uint32_t taken = 0;
+  for (int round = 0; round < kk; ++round) {
+    uint32_t cur = 0;
+    int ebest = 0;
+#pragma unroll
+    for (int e = E - 1; e >= 0; --e) {  // lowest e wins a tie inside the lane
+      const uint32_t x = ((taken >> e) & 1u) ? 0u : u[e];
+      if (x >= cur) { cur = x; ebest = e; }
+    }
+    const uint32_t m = wave_reduce_u32<true>(cur);
+    const uint64_t eq = __ballot(cur == m);
+    int win_lane, win_e;
+    if (popc(eq) == 1) {
+      win_lane = __builtin_ctzll(eq);
+      win_e = __builtin_amdgcn_readlane(ebest, win_lane);
+    } else {
+      const uint32_t jm = wave_reduce_u32<false>(cur == m ? (uint32_t)(64 * ebest + lane) : 0xffffffffu);
+      win_lane = (int)(jm & 63u);
+      win_e = (int)(jm >> 6);
+    }
+    if (lane == win_lane) taken |= 1u << win_e;
+  }
+  return taken;
 }
 
 template <int E>
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(
-    const float *__restrict__ qbar, const float *__restrict__ kbar, int H, int nvb, int nb,
+    const double *__restrict__ qbar, const float *__restrict__ kbar, int H, int nvb, int nb,
     int budget, int radius, int max_sel, int32_t *__restrict__ block_idx,
     int32_t *__restrict__ block_cnt, float *__restrict__ scores_out) {
-  constexpr int P = 64 * E;  // padded row width
-  extern __shared__ __align__(16) unsigned char smem[];
-  double *qs = reinterpret_cast<double *>(smem);                 // [kRows][128]
-  float *sc = reinterpret_cast<float *>(qs + kRows * kHeadDim);  // [kRows][P]
-  uint8_t *flags = reinterpret_cast<uint8_t *>(sc + kRows * P);  // [4 waves][P]
+  constexpr int ld = 64 * E;  // LDS score row stride (floats)
+  extern __shared__ __align__(16) float sc[];  // [kRouteRows][ld]
 
   const int bh = blockIdx.y;
-  const int i0 = blockIdx.x * kRows;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const float *qb = qbar + (int64_t)bh * nvb * kHeadDim;
-  const float *kb = kbar + (int64_t)bh * nvb * kHeadDim;
+  const int i0 = blockIdx.x * kRouteRows;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
-  for (int x = tid; x < kRows * kHeadDim; x += kRouteThreads) {
-    const int r = x / kHeadDim;
-    qs[x] = (i0 + r < nvb) ? (double)qb[(int64_t)(i0 + r) * kHeadDim + (x % kHeadDim)] : 0.0;
-  }
+  const int nt = (nvb + 15) >> 4;
+  route_scores_tile(reinterpret_cast<const double2 *>(qbar) + ((int64_t)bh * nt + blockIdx.x) * 16 * 64,
+                    reinterpret_cast<const float4 *>(kbar) + (int64_t)bh * nt * 8 * 64, nt, sc, ld,
+                    lane, wave);
   __syncthreads();
 
-  // 1. scores
-  for (int j = tid; j < nvb; j += kRouteThreads) {
-    double acc[kRows];
-#pragma unroll
-    for (int r = 0; r < kRows; ++r) acc[r] = 0.0;
-    const float4 *kr = reinterpret_cast<const float4 *>(kb + (int64_t)j * kHeadDim);
-#pragma unroll 4
-    for (int d4 = 0; d4 < kHeadDim / 4; ++d4) {
-      const float4 kv = kr[d4];
-#pragma unroll
-      for (int r = 0; r < kRows; ++r) {
-        const double *qr = qs + r * kHeadDim + 4 * d4;
-        acc[r] = fma(qr[0], (double)kv.x, acc[r]);
-        acc[r] = fma(qr[1], (double)kv.y, acc[r]);
-        acc[r] = fma(qr[2], (double)kv.z, acc[r]);
-        acc[r] = fma(qr[3], (double)kv.w, acc[r]);
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < kRows; ++r) {
-      const float s = (float)acc[r];
-      sc[r * P + j] = s;
-      if (scores_out != nullptr && i0 + r < nvb)
-        scores_out[((int64_t)bh * nvb + i0 + r) * nvb + j] = s;
-    }
-  }
-  __syncthreads();
-
-  // 2-3. one wavefront per row
-  uint8_t *fl = flags + wave * P;
-  for (int rr = wave; rr < kRows; rr += 4) {
+  for (int rr = wave; rr < kRouteRows; rr += kRouteWaves) {
     const int i = i0 + rr;
-    if (i >= nvb) break;  // wave-uniform; no workgroup barrier below
+    if (i >= nvb) break;  // wave-uniform
     const int f_lo = i - radius < 0 ? 0 : i - radius;
     const int f_hi = i + radius > nvb - 1 ? nvb - 1 : i + radius;
     const int n_cand = nvb - (f_hi - f_lo + 1);
     const int kk = budget < n_cand ? budget : n_cand;
 
-    uint64_t key[E];
+    // order keys; 0 (below every finite score) for non-candidates
+    uint32_t u[E];
+    uint32_t mn = 0xffffffffu, mx = 0u;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      const int j = e * 64 + lane;
-      const bool cand = j < nvb && (j < f_lo || j > f_hi);
-      key[e] = cand ? ((uint64_t)desc_key(sc[rr * P + j]) << 32) | (uint32_t)j : ~0ull;
+      const int j = 64 * e + lane;
+      const float s = sc[rr * ld + j];
+      if (scores_out != nullptr && j < nvb) scores_out[((int64_t)bh * nvb + i) * nvb + j] = s;
+      const bool v = j < nvb && (j < f_lo || j > f_hi);
+      u[e] = v ? order_key(s) : 0u;
+      mn = v && u[e] < mn ? u[e] : mn;
+      mx = u[e] > mx ? u[e] : mx;
     }
-    wave_bitonic_sort<E>(key, lane);
 
-    for (int x = lane; x < P; x += 64) fl[x] = 0;
-    wave_lds_sync();
+    // 2. radix select: `pre` holds the decided high bits of the kk-th key,
+    // `rem` how many keys are still to be taken from the bucket of keys that
+    // match `pre` on those bits; keys above the bucket are taken.
+    const int n_off = 64 * E - n_cand;  // non-candidates (key 0)
+    int rem = kk;
+    int stop = 32;  // 32: nothing to take; else the bit the search stopped at
+    uint32_t pre = 0u;
+    uint32_t taken = 0;  // tournament result (bit e: slot e)
+    const bool tour = kk > 0 && kk <= kTournamentMax && kk < n_cand;
+    if (tour) {
+      taken = tournament_select<E>(u, kk, lane);
+    } else if (kk > 0) {
+      mn = wave_reduce_u32<false>(mn);
+      mx = wave_reduce_u32<true>(mx);
+      const int fb = mn >= mx ? -1 : 31 - __builtin_clz(mn ^ mx);
+      pre = fb < 0 ? mx : (mx & high_bits(fb));
+      for (int bit = fb;; --bit) {
+        const uint32_t hm = high_bits(bit);
+        int bucket = 0, c = 0;
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      if (e * 64 + lane < kk) fl[(uint32_t)key[e]] = 1;
+        for (int e = 0; e < E; ++e) {
+          const bool in_b = ((u[e] ^ pre) & hm) == 0u;
+          bucket += popc(__ballot(in_b));
+          c += popc(__ballot(in_b && bit >= 0 && ((u[e] >> (bit & 31)) & 1u)));
+        }
+        if ((pre & hm) == 0u) bucket -= n_off;
+        if (bucket == rem || bit < 0) {
+          stop = bit;
+          break;
+        }
+        if (c >= rem) pre |= 1u << bit;
+        else rem -= c;
+      }
     }
-    for (int j = f_lo + lane; j <= f_hi; j += 64) fl[j] = 1;
-    wave_lds_sync();
 
+    // 3. emission: keys above the bucket, the bucket whole when the search
+    // stopped on it, or (stop = -1) its first rem keys by block index
+    const uint32_t hm = high_bits(stop);
+    const uint32_t ph = pre & hm;
     int32_t *out = block_idx + ((int64_t)bh * nvb + i) * max_sel;
-    int base = 0;
-    for (int c = 0; c < nvb; c += 64) {
-      const int j = c + lane;
-      const bool f = j < nvb && fl[j] != 0;
-      const uint64_t mask = __ballot(f);
-      const int pos = base + __popcll(mask & ((1ull << lane) - 1ull));
-      if (f) out[pos] = j;
-      base += __popcll(mask);
+    int base = 0, ties = rem;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int j = 64 * e + lane;
+      const uint32_t uh = u[e] & hm;
+      bool take = tour ? ((taken >> e) & 1u) != 0u && u[e] != 0u
+                       : stop != 32 && u[e] != 0u && (uh > ph || (stop >= 0 && uh == ph));
+      if (stop == -1) {
+        const bool eq = u[e] != 0u && u[e] == pre;
+        const uint64_t m = __ballot(eq);
+        if (eq && popc(m & ((1ull << lane) - 1ull)) < ties) take = true;
+        ties -= popc(m) < ties ? popc(m) : ties;
+      }
+      const bool f = j < nvb && (take || (j >= f_lo && j <= f_hi));
+      const uint64_t m = __ballot(f);
+      if (f) out[base + popc(m & ((1ull << lane) - 1ull))] = j;
+      base += popc(m);
     }
     for (int j = nvb + lane; j < nb; j += 64) out[base + (j - nvb)] = j;
     const int cnt = base + (nb - nvb);
     for (int x = cnt + lane; x < max_sel; x += 64) out[x] = -1;
     if (lane == 0) block_cnt[(int64_t)bh * nvb + i] = cnt;
-    wave_lds_sync();  // flags are reused by this wave's next row
   }
 }
 
 template <int E>
-hipError_t launch_route_e(const float *qbar, const float *kbar, int B, int H, int nvb, int nb,
+hipError_t launch_route_e(const double *qbar, const float *kbar, int B, int H, int nvb, int nb,
                           int budget, int radius, int max_sel, int32_t *block_idx,
                           int32_t *block_cnt, float *scores, hipStream_t stream) {
-  constexpr int P = 64 * E;
-  const size_t lds = kRows * kHeadDim * sizeof(double) + kRows * P * sizeof(float) + 4 * P;
-  dim3 grid((nvb + kRows - 1) / kRows, B * H);
-  hipLaunchKernelGGL(route_kernel<E>, grid, dim3(kRouteThreads), lds, stream, qbar, kbar, H, nvb,
-                     nb, budget, radius, max_sel, block_idx, block_cnt, scores);
+  dim3 grid((nvb + kRouteRows - 1) / kRouteRows, B * H);
+  const size_t lds = (size_t)kRouteRows * 64 * E * sizeof(float);
+  hipLaunchKernelGGL((route_kernel<E>), grid, dim3(kRouteThreads), lds, stream, qbar, kbar, H,
+                     nvb, nb, budget, radius, max_sel, block_idx, block_cnt, scores);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_route(const float *qbar, const float *kbar, int B, int H, int nvb, int nb,
+hipError_t launch_route(const double *qbar, const float *kbar, int B, int H, int nvb, int nb,
                         int budget, int radius, int max_sel, int32_t *block_idx,
                         int32_t *block_cnt, float *scores, hipStream_t stream) {
   if (nvb <= 0) return hipSuccess;
@@ -200,9 +267,12 @@ hipError_t launch_route(const float *qbar, const float *kbar, int B, int H, int 
   if (nvb <= 128)
     return launch_route_e<2>(qbar, kbar, B, H, nvb, nb, budget, radius, max_sel, block_idx,
                              block_cnt, scores, stream);
+  if (nvb <= 192)
+    return launch_route_e<3>(qbar, kbar, B, H, nvb, nb, budget, radius, max_sel, block_idx,
+                             block_cnt, scores, stream);
   if (nvb <= 256)
     return launch_route_e<4>(qbar, kbar, B, H, nvb, nb, budget, radius, max_sel, block_idx,
-                             block_cnt, scores, stream);
+                                block_cnt, scores, stream);
   if (nvb <= 512)
     return launch_route_e<8>(qbar, kbar, B, H, nvb, nb, budget, radius, max_sel, block_idx,
                              block_cnt, scores, stream);

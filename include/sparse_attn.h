@@ -121,10 +121,17 @@ const char *sa_last_error(void);
  * block_cnt     int32 [B, H, NVB] out: list lengths.
  * route_scores  nullable; fp32 [B, H, NVB, NVB] out: s_ij.
  * workspace     device scratch of workspace_bytes >=
- *               sa_route_workspace_bytes(B, T, H, sink_start) (pooled means
- *               are left there: Q means then K means, each [B, H, NVB, 128]
- *               fp32).  May be NULL when that size is 0.
- * Errors: SA_ERR_UNSUPPORTED when NVB > 1024 (per-row sort width).
+ *               sa_route_workspace_bytes(B, T, H, sink_start), 16-byte
+ *               aligned.  The pooled means are left there, over NVB16 = NVB
+ *               rounded up to a multiple of 16 blocks: first the Q means
+ *               (fp64 copies of the fp32 means), then the K means (fp32),
+ *               each in the operand order of the route kernel's fp64 MFMA:
+ *               mean (b, h, block i, channel d) sits at piece
+ *               [b][h][i / 16][s][16 * (d / 32) + i % 16], element d % 32 - w*s,
+ *               where a piece holds w = 2 (Q) or 4 (K) consecutive steps and
+ *               s = (d % 32) / w.  May be NULL when that size is 0.
+ * Errors: SA_ERR_UNSUPPORTED when NVB > 1024 (per-row selection width) or
+ * B*H > 65535 (launch grid).
  * With NVB == 0 nothing is enqueued and SA_OK is returned.
  */
 sa_status sparse_attn_route(const void *q, const void *k,

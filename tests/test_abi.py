@@ -60,7 +60,7 @@ def test_shape_helpers_match_oracle(L):
             assert L.sa_topk_budget(nvb, ratio) == ora.topk_budget(nvb, ratio), (nvb, ratio)
     assert L.sa_topk_budget(10, 0.0) == -1 and L.sa_topk_budget(10, 1.5) == -1
     assert L.sa_topk_budget(10, float("nan")) == -1
-    assert L.sa_route_workspace_bytes(1, 9505, 56, 9216) == 2 * 56 * 144 * 128 * 4
+    assert L.sa_route_workspace_bytes(1, 9505, 56, 9216) == 56 * 144 * 128 * (8 + 4)
     assert L.sa_route_workspace_bytes(1, 9505, 56, 10) == 0
     assert L.sa_dense_workspace_bytes(1, 9216, 56, 9216) == 0          # no dense rows
     assert L.sa_dense_workspace_bytes(1, 9505, 56, 9216) % (64 * 130 * 4) == 0
@@ -116,6 +116,7 @@ ROUTE_CASES = [
     (dict(ws_bytes=100), WORKSPACE, "workspace"),
     (dict(ws=None), WORKSPACE, "workspace"),
     (dict(T=65600, ss=65600, max_sel=200, ratio=0.1), UNSUPPORTED, "video blocks"),
+    (dict(B=2, H=40000, T=64, ss=64, max_sel=1), UNSUPPORTED, "B*H"),
 ]
 
 

@@ -100,6 +100,36 @@ def test_split_video_block_and_bias():
     _full_parity(wl)
 
 
+def _tied_keys(nvb, copies, seed):
+    """K whose blocks in `copies` repeat block 0 token for token: their pooled
+    means, hence their scores against every query block, are bit-identical."""
+    q, k, v = workloads.random_qkv(1, 64 * nvb, 2, seed=seed)
+    k = k.clone()
+    for j in copies:
+        k[:, 64 * j:64 * j + 64] = k[:, 0:64]
+    return q, k, v
+
+
+@pytest.mark.parametrize("nvb,ratio,radius,copies", [
+    (20, 0.25, 0, range(20)),             # all scores equal, small budget
+    (20, 0.6, 1, range(0, 20, 2)),        # half the blocks tied
+    (80, 0.5, 0, range(80)),              # budget 40: the large-budget selection path
+    (80, 0.6, 1, range(3, 80, 3)),
+])
+def test_exact_ties_break_to_lower_index(nvb, ratio, radius, copies):
+    """Exactly equal scores: the lower block index wins, on both selection
+    paths (small and large budgets).  No near-tie leniency here."""
+    import block_sparse_attention_05_amd as sa
+    q, k, v = _tied_keys(nvb, copies, seed=30 + nvb)
+    qn, kn = to_np(q), to_np(k)
+    rt = ora.route(qn, kn, 64 * nvb, ratio, radius)
+    idx, cnt = sa.sparse_attn_route(q.cuda(), k.cuda(), 64 * nvb, ratio, radius)
+    idx, cnt = idx.cpu().numpy(), cnt.cpu().numpy()
+    for h in range(2):
+        for i in range(nvb):
+            assert idx[0, h, i, :cnt[0, h, i]].tolist() == rt.rows[0][h][i].blocks, (h, i)
+
+
 def test_no_video_blocks_all_dense():
     q, k, v = workloads.random_qkv(1, 700, 2, seed=9)
     wl = workloads.Workload("all_dense", q, k, v, sink_start=40, topk_ratio=0.1, local_radius=1)
@@ -191,9 +221,22 @@ def test_pooled_means_bit_exact():
     sa.sparse_attn_route(q, k, wl.sink_start, 0.1, 1, workspace=ws)
     torch.cuda.synchronize()
     nvb = wl.sink_start // 64
-    means = ws.view(torch.float32).cpu().numpy().reshape(2, B, H, nvb, 128)
-    assert np.array_equal(means[0].view(np.uint32), ora.pool_means(to_np(wl.q), nvb).view(np.uint32))
-    assert np.array_equal(means[1].view(np.uint32), ora.pool_means(to_np(wl.k), nvb).view(np.uint32))
+    nt = -(-nvb // 16)
+    n = B * H * nt * 16 * 128
+    raw = ws.cpu()
+    # operand order of the route kernel: tile of 16 blocks, step st = d % 32,
+    # lane 16*(d // 32) + block % 16; q pieces hold 2 steps, k pieces 4
+    qt = raw[: 8 * n].view(torch.float64).numpy().reshape(B, H, nt, 16, 64, 2)
+    kt = raw[8 * n: 12 * n].view(torch.float32).numpy().reshape(B, H, nt, 8, 64, 4)
+    i = np.arange(nvb)[:, None]
+    d = np.arange(128)[None, :]
+    lane = 16 * (d // 32) + i % 16
+    qm = qt[:, :, i // 16, (d % 32) // 2, lane, d % 2]
+    km = kt[:, :, i // 16, (d % 32) // 4, lane, d % 4]
+    qo = ora.pool_means(to_np(wl.q), nvb)
+    assert np.array_equal(qm, qo.astype(np.float64))       # fp64 copies of the fp32 means
+    assert np.array_equal(qm.astype(np.float32).view(np.uint32), qo.view(np.uint32))
+    assert np.array_equal(km.view(np.uint32), ora.pool_means(to_np(wl.k), nvb).view(np.uint32))
 
 
 # ---- full-size workloads: full route, sampled attention -------------------
