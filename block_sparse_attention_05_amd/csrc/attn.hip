@@ -93,11 +93,14 @@ __device__ __forceinline__ i32x4s buffer_rsrc(const void *base, uint32_t num_byt
 // Issued as inline asm so the compiler does not order later LDS reads of the
 // other ring slot behind it; the caller waits (vmcnt) before the barrier that
 // publishes the data.
+// The LDS address is lds_base + kOff (kOff folded into the M0 write, so the
+// caller keeps one base register per ring slot).
+template <int kOff>
 __device__ __forceinline__ void lds_dma_b128(const i32x4s &rsrc, uint32_t voffset, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+  asm volatile("s_add_u32 m0, %2, %3\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                :
-               : "v"(voffset), "s"(rsrc), "s"(lds_base)
-               : "memory", "m0");
+               : "v"(voffset), "s"(rsrc), "s"(lds_base), "i"(kOff)
+               : "memory", "m0", "scc");
 }
 __device__ __forceinline__ void lds_dma_b32(const i32x4s &rsrc, uint32_t voffset, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, 0 offen lds"
@@ -163,19 +166,6 @@ void attn_fwd_kernel(Params p) {
   const int row_bytes = p.H * kHeadDim * 2;
   const int64_t bbase = (int64_t)b * T * rs;
 
-  // Q^T fragments for this lane's query row: d = 16*dc + 8*g + [0, 8)
-  const int tq = qb * kBlock + rw * 32 + c32;
-  bf16x8 qf[8];
-  {
-    const uint4 *qp = reinterpret_cast<const uint4 *>(p.q + bbase + (int64_t)tq * rs + h * kHeadDim);
-#pragma unroll
-    for (int dc = 0; dc < 8; ++dc) {
-      uint4 x = make_uint4(0, 0, 0, 0);
-      if (tq < T) x = qp[2 * dc + g];
-      qf[dc] = __builtin_bit_cast(bf16x8, x);
-    }
-  }
-
   // ---- tile sequence ------------------------------------------------------
   // Sparse: the block list is held in VGPR lanes (lane j = entry cb + j of
   // the current 64-entry chunk) and read with v_readlane, so no memory round
@@ -212,6 +202,21 @@ void attn_fwd_kernel(Params p) {
   }
   const int n = t_end - t_begin;
   if (kbias == nullptr) n_plain = n;
+
+  // Q^T fragments for this lane's query row: d = 16*dc + 8*g + [0, 8).
+  // Loaded after the list so that the first tile copies do not wait for them.
+  const int tq = qb * kBlock + rw * 32 + c32;
+  bf16x8 qf[8];
+  {
+    const uint4 *qp = reinterpret_cast<const uint4 *>(p.q + bbase + (int64_t)tq * rs + h * kHeadDim);
+#pragma unroll
+    for (int dc = 0; dc < 8; ++dc) {
+      uint4 x = make_uint4(0, 0, 0, 0);
+      if (tq < T) x = qp[2 * dc + g];
+      qf[dc] = __builtin_bit_cast(bf16x8, x);
+    }
+  }
+
   // First token of tile t_begin + j; calls come with j = 0, 1, 2, ... in
   // order.  An invalid list entry maps to T (reads as zero, fully masked).
   // The next 64-entry chunk is loaded one call before it is needed, so that
@@ -267,14 +272,18 @@ void attn_fwd_kernel(Params p) {
   auto issue_k = [&](int key0, int slot) {
     const uint32_t base = (uint32_t)key0 * (uint32_t)row_bytes + k_lane;
     const uint32_t lb = lds0 + kKOff + (uint32_t)(slot * 16384) + wave_lds;
-#pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) lds_dma_b128(rk, base + (s4 >> 1) * rows8 + 128 * (s4 & 1), lb + 1024 * s4);
+    lds_dma_b128<0>(rk, base, lb);
+    lds_dma_b128<1024>(rk, base + 128, lb);
+    lds_dma_b128<2048>(rk, base + rows8, lb);
+    lds_dma_b128<3072>(rk, base + rows8 + 128, lb);
   };
   auto issue_v = [&](int key0, int slot) {
     const uint32_t base = (uint32_t)key0 * (uint32_t)row_bytes + v_lane;
     const uint32_t lb = lds0 + kVOff + (uint32_t)(slot * 16384) + wave_lds;
-#pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) lds_dma_b128(rv, base + (s4 >> 1) * rows8 + 128 * (s4 & 1), lb + 1024 * s4);
+    lds_dma_b128<0>(rv, base, lb);
+    lds_dma_b128<1024>(rv, base + 128, lb);
+    lds_dma_b128<2048>(rv, base + rows8, lb);
+    lds_dma_b128<3072>(rv, base + rows8 + 128, lb);
     if (kbias != nullptr && key0 >= sink0 && key0 < T && wave == 0)
       lds_dma_b32(rb, (uint32_t)(key0 + lane) * 4u, lds0 + kBOff + (uint32_t)(slot * 256));
   };
@@ -587,46 +596,47 @@ void attn_fwd_kernel(Params p) {
 }
 
 // Merge the split-KV partials of the dense rows: one thread per (row, 4
-// channels).  m* = max_s m_s, O = sum_s 2^(m_s - m*) O_s / sum_s 2^(m_s - m*) l_s.
+// channels), 8 rows per workgroup.
+// m* = max_s m_s, O = sum_s 2^(m_s - m*) O_s / sum_s 2^(m_s - m*) l_s.
 constexpr int kCombineThreads = 256;
+constexpr int kCombineRows = kCombineThreads / (kHeadDim / 4);
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(Params p) {
-  const int wq = blockIdx.x;              // (b*H + h) * nqb + qbi
+  constexpr int kChunks = kBlock / kCombineRows;
+  const int wq = blockIdx.x / kChunks;     // (b*H + h) * nqb + qbi
   const int qbi = wq % p.nqb;
   const int bh = wq / p.nqb;
   const int h = bh % p.H;
   const int b = bh / p.H;
   const int T = p.T;
   const int64_t rs = (int64_t)p.H * kHeadDim;
-  for (int x = threadIdx.x; x < kBlock * (kHeadDim / 4); x += kCombineThreads) {
-    const int row = x / (kHeadDim / 4);
-    const int d0 = (x % (kHeadDim / 4)) * 4;
-    const int tq = (p.qb0 + qbi) * kBlock + row;
-    if (tq >= T) continue;
-    float m = -INFINITY;
-    for (int s = 0; s < p.nsplit; ++s)
-      m = fmaxf(m, p.part_ml[2 * (((int64_t)wq * p.nsplit + s) * kBlock + row)]);
-    const float msub = (m == -INFINITY) ? 0.f : m;
-    float l = 0.f;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int s = 0; s < p.nsplit; ++s) {
-      const int64_t prow = ((int64_t)wq * p.nsplit + s) * kBlock + row;
-      const float2 ml = *reinterpret_cast<const float2 *>(p.part_ml + 2 * prow);
-      const float wgt = __builtin_amdgcn_exp2f(ml.x - msub);
-      l += wgt * ml.y;
-      const float4 po = *reinterpret_cast<const float4 *>(p.part_o + prow * kHeadDim + d0);
-      acc.x += wgt * po.x;
-      acc.y += wgt * po.y;
-      acc.z += wgt * po.z;
-      acc.w += wgt * po.w;
-    }
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    uint16_t *op = p.out + (int64_t)b * T * rs + (int64_t)tq * rs + h * kHeadDim + d0;
-    uint2 val;
-    val.x = pack_bf16x2(acc.x * inv, acc.y * inv);
-    val.y = pack_bf16x2(acc.z * inv, acc.w * inv);
-    *reinterpret_cast<uint2 *>(op) = val;
-    if (p.lse != nullptr && d0 == 0) p.lse[((int64_t)b * p.H + h) * T + tq] = (m + __log2f(l)) * kLn2;
+  const int row = (blockIdx.x % kChunks) * kCombineRows + threadIdx.x / (kHeadDim / 4);
+  const int d0 = (threadIdx.x % (kHeadDim / 4)) * 4;
+  const int tq = (p.qb0 + qbi) * kBlock + row;
+  if (tq >= T) return;
+  const int64_t prow0 = (int64_t)wq * p.nsplit * kBlock + row;   // split s: prow0 + s * kBlock
+  float m = -INFINITY;
+  for (int s = 0; s < p.nsplit; ++s) m = fmaxf(m, p.part_ml[2 * (prow0 + (int64_t)s * kBlock)]);
+  const float msub = (m == -INFINITY) ? 0.f : m;
+  float l = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s = 0; s < p.nsplit; ++s) {
+    const int64_t prow = prow0 + (int64_t)s * kBlock;
+    const float2 ml = *reinterpret_cast<const float2 *>(p.part_ml + 2 * prow);
+    const float4 po = *reinterpret_cast<const float4 *>(p.part_o + prow * kHeadDim + d0);
+    const float wgt = __builtin_amdgcn_exp2f(ml.x - msub);
+    l += wgt * ml.y;
+    acc.x += wgt * po.x;
+    acc.y += wgt * po.y;
+    acc.z += wgt * po.z;
+    acc.w += wgt * po.w;
   }
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  uint16_t *op = p.out + (int64_t)b * T * rs + (int64_t)tq * rs + h * kHeadDim + d0;
+  uint2 val;
+  val.x = pack_bf16x2(acc.x * inv, acc.y * inv);
+  val.y = pack_bf16x2(acc.z * inv, acc.w * inv);
+  *reinterpret_cast<uint2 *>(op) = val;
+  if (p.lse != nullptr && d0 == 0) p.lse[((int64_t)b * p.H + h) * T + tq] = (m + __log2f(l)) * kLn2;
 }
 
 Params make_params(const AttnArgs &a, int qb0, int nqb) {
@@ -700,7 +710,8 @@ hipError_t launch_attn_dense(const AttnArgs &a, void *workspace, size_t workspac
   hipLaunchKernelGGL(attn_fwd_kernel<true>, dim3(total), dim3(kThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.nsplit == 1) return e;
-  hipLaunchKernelGGL(combine_kernel, dim3(a.B * a.H * nq), dim3(kCombineThreads), 0, stream, p);
+  hipLaunchKernelGGL(combine_kernel, dim3(a.B * a.H * nq * (kBlock / kCombineRows)),
+                     dim3(kCombineThreads), 0, stream, p);
   return hipGetLastError();
 }
 
