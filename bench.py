@@ -90,7 +90,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="h3", choices=["h3", "h3_bias", "mid", "long", "tiny"])
-    ap.add_argument("--cpu-heads", type=int, default=24)
+    ap.add_argument("--cpu-heads", type=int, default=56)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (the known-size "
