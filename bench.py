@@ -2,10 +2,15 @@
 workload (B=1, H=56, T=9505 = 9216 video + 289 context tokens, D=128, bf16,
 top-k ratio 0.1, self block forced, context tokens as exact sinks).
 
-A step is one full call on one stream: sparse_attn_route (pool + route
-kernels), sparse_attn_fwd (video query rows) and dense_sink_fwd (context
-rows).  Inputs are resident in HBM before the timed region.  Effective FLOPs
-count 4*128 per (query row, key) pair scored exactly.
+A step is one full call: sparse_attn_route (pool + route kernels) then
+sparse_attn_fwd (video query rows) on the main stream, and dense_sink_fwd
+(context rows, which need no routing) on a second stream forked at the start
+of the step, launched after the routing kernels and joined at the step's
+end, so the dense rows fill the GPU beside routing and the sparse rows.
+The two halves write disjoint rows of ``out``.  ``--one-stream`` runs the
+three calls back to back instead.  Inputs are resident in HBM
+before the timed region.  Effective FLOPs count 4*128 per (query row, key)
+pair scored exactly.
 
 Prints one JSON line.  ``--gpus`` above 1 is refused: this path runs on one
 GPU (a multi-GPU run would shard heads, see the design notes).
@@ -92,6 +97,8 @@ def main():
     ap.add_argument("--workload", default="h3", choices=["h3", "h3_bias", "mid", "long", "tiny"])
     ap.add_argument("--cpu-heads", type=int, default=56)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--one-stream", action="store_true",
+                    help="run the dense rows after the sparse rows on one stream")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (the known-size "
                          "kernel that scales the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -131,20 +138,33 @@ def main():
     dws = torch.empty(dws_n, dtype=torch.uint8, device=dev) if dws_n > 0 else None
     out = torch.empty_like(q)
     stream = torch.cuda.current_stream(dev)
+    side = stream if args.one_stream else torch.cuda.Stream(dev)   # default priority
 
     def step(ev=None):
+        # ev: events [start, after route, after sparse] on the main stream and
+        # [start, after dense] on the side stream
+        if side is not stream:
+            side.wait_stream(stream)
         if ev is not None:
             ev[0].record(stream)
+            ev[3].record(side)
         sa.sparse_attn_route(q, k, ss, wl.topk_ratio, wl.local_radius, block_idx=idx, block_cnt=cnt,
                              workspace=ws)
         if ev is not None:
             ev[1].record(stream)
+        if side is not stream:
+            # queued behind the pool/route launches so those dispatch first
+            with torch.cuda.stream(side):
+                sa.dense_sink_fwd(q, k, v, ss, key_bias=kb, out=out, workspace=dws)
         sa.sparse_attn_fwd(q, k, v, ss, idx, cnt, key_bias=kb, out=out)
         if ev is not None:
             ev[2].record(stream)
-        sa.dense_sink_fwd(q, k, v, ss, key_bias=kb, out=out, workspace=dws)
+        if side is stream:
+            sa.dense_sink_fwd(q, k, v, ss, key_bias=kb, out=out, workspace=dws)
         if ev is not None:
-            ev[3].record(stream)
+            ev[4].record(side)
+        if side is not stream:
+            stream.wait_stream(side)
 
     for _ in range(args.warmup):
         step()
@@ -160,13 +180,18 @@ def main():
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
 
-    # per-stage timing (events between the launches, same stream)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # per-stage timing: events between the launches on the stream each runs on
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for i in range(args.steps):
         step(evs[i])
     torch.cuda.synchronize()
-    st = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(3)] for e in evs])
+    if side is stream:   # dense ran after sparse: time it from the sparse end
+        st = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[4])]
+                       for e in evs])
+    else:
+        st = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[3].elapsed_time(e[4])]
+                       for e in evs])
     med = np.median(st, axis=0)
 
     sparse_flops, dense_flops = effective_flops_from_lists(cnt, idx, T, nvb, H, B)
@@ -199,7 +224,7 @@ def main():
         "stages_ms_p10_p90": {n: [round(float(np.percentile(st[:, j], 10)), 4),
                                   round(float(np.percentile(st[:, j], 90)), 4)]
                               for j, n in enumerate(("route", "sparse_fwd", "dense_fwd"))},
-        "attention_only_tflops": round((sparse_flops + dense_flops) / ((med[1] + med[2]) * 1e-3) / 1e12, 3),
+        "streams": 1 if side is stream else 2,
         "roofline": {"kernel": "attn_fwd_kernel<sparse>", "bound": "mfma", "achieved": round(achieved, 3),
                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
                      "algorithmic_gflop_per_launch": round(sparse_flops / 1e9, 3),

@@ -236,17 +236,32 @@ def dense_sink_fwd(q, k, v, sink_start: int, *, key_bias: Optional[torch.Tensor]
 
 def routed_attention(q, k, v, sink_start: int, topk_ratio: float = 0.1, local_radius: int = 0, *,
                      key_bias: Optional[torch.Tensor] = None, softmax_scale: float = 0.0,
-                     return_lse: bool = False, return_route: bool = False):
+                     return_lse: bool = False, return_route: bool = False,
+                     dense_stream: Optional[torch.cuda.Stream] = None):
     """One full call: sparse_attn_route + sparse_attn_fwd + dense_sink_fwd on
-    the current stream."""
+    the current stream.  With ``dense_stream`` (a stream of the same device)
+    the dense rows, which need no routing, run there instead, forked from and
+    joined back into the current stream; they write rows disjoint from the
+    sparse rows', so the result is the same."""
+    cur = torch.cuda.current_stream(q.device)
+    if dense_stream is not None:
+        dense_stream.wait_stream(cur)
     block_idx, block_cnt = sparse_attn_route(q, k, sink_start, topk_ratio, local_radius)
     B, T, H, _ = q.shape
     out = torch.empty_like(q)
     lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device) if return_lse else None
+    if dense_stream is not None:
+        # launched behind the routing kernels so those dispatch first
+        with torch.cuda.stream(dense_stream):
+            dense_sink_fwd(q, k, v, sink_start, key_bias=key_bias, softmax_scale=softmax_scale,
+                           out=out, lse=lse)
     sparse_attn_fwd(q, k, v, sink_start, block_idx, block_cnt, key_bias=key_bias,
                     softmax_scale=softmax_scale, out=out, lse=lse)
-    dense_sink_fwd(q, k, v, sink_start, key_bias=key_bias, softmax_scale=softmax_scale,
-                   out=out, lse=lse)
+    if dense_stream is None:
+        dense_sink_fwd(q, k, v, sink_start, key_bias=key_bias, softmax_scale=softmax_scale,
+                       out=out, lse=lse)
+    else:
+        cur.wait_stream(dense_stream)
     res = [out]
     if return_lse:
         res.append(lse)

@@ -296,3 +296,19 @@ def test_h3_deterministic_repeat():
     for r in runs[1:]:
         for key in ("out", "lse", "idx", "cnt"):
             assert torch.equal(runs[0][key], r[key]), key
+
+
+def test_h3_dense_stream_overlap_bit_identical():
+    """Dense rows on a second stream, concurrent with routing and the sparse
+    rows (the schedule the benchmark times): the same bits as one stream."""
+    import block_sparse_attention_05_amd as sa
+    wl = workloads.h3(with_bias=True)
+    q, k, v, kb = wl.q.cuda(), wl.k.cuda(), wl.v.cuda(), wl.key_bias.cuda()
+    args = (q, k, v, wl.sink_start, wl.topk_ratio, wl.local_radius)
+    ref_out, ref_lse = sa.routed_attention(*args, key_bias=kb, return_lse=True)
+    side = torch.cuda.Stream()
+    for _ in range(3):
+        out, lse = sa.routed_attention(*args, key_bias=kb, return_lse=True, dense_stream=side)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out)
+        assert torch.equal(lse, ref_lse)
