@@ -323,7 +323,9 @@ void attn_fwd_kernel(Params p) {
     const float *bs = reinterpret_cast<const float *>(smem + kBOff + VS * 256);
 
     // S(j+1) MFMAs, issued in two groups so that they overlap the max phase
-    // and the exponential phase of tile j.
+    // and the exponential phase of tile j.  Their K fragments are read from
+    // LDS a few MFMAs ahead of use, so that the LDS latency is not paid once
+    // per MFMA.
     auto qk_part = [&](auto lo_c, auto hi_c) {
       constexpr int LO = decltype(lo_c)::value;
       constexpr int HI = decltype(hi_c)::value;
@@ -373,9 +375,9 @@ void attn_fwd_kernel(Params p) {
     }
     mt = max_with_partner(mt);
     if (DO_QK) {
+      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 3, 0);
 #pragma unroll
       for (int i = 0; i < 3; ++i) {
-        __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
         __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
         __builtin_amdgcn_sched_group_barrier(kSchedVALU, 4, 0);
       }
@@ -420,9 +422,15 @@ void attn_fwd_kernel(Params p) {
       }
     }
     if (DO_QK) {
+      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 2, 0);
 #pragma unroll
-      for (int i = 0; i < 5; ++i) {
+      for (int i = 0; i < 3; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
         __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedVALU, 8, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
         __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
         __builtin_amdgcn_sched_group_barrier(kSchedVALU, 8, 0);
       }
@@ -562,8 +570,8 @@ void attn_fwd_kernel(Params p) {
     m_used = m;
   }
 
-  if (tq >= T) return;
   if (kDense && p.nsplit > 1) {
+    if (tq >= T) return;
     // partial (unnormalised O, max, sum) of this key range
     const int64_t prow = ((int64_t)wq * p.nsplit + split) * kBlock + (rw * 32 + c32);
     float *po = p.part_o + prow * kHeadDim;
@@ -578,20 +586,33 @@ void attn_fwd_kernel(Params p) {
     if (g == 0) *reinterpret_cast<float2 *>(p.part_ml + 2 * prow) = make_float2(m_used, l_tot);
     return;
   }
+  // The wave's 32 bf16 rows go through LDS (a free part of the V ring, rows
+  // of 256 B with the 16-byte chunks XOR-swizzled by row) and out as whole
+  // rows: each store instruction writes four full 256-byte rows.
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  uint16_t *op = p.out + bbase + (int64_t)tq * rs + h * kHeadDim;
+  unsigned char *stage = smem + kVOff + 8192 + rw * 8192;
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) {
 #pragma unroll
     for (int rq = 0; rq < 4; ++rq) {
-      const int d0 = 32 * dt + 8 * rq + 4 * g;
       uint2 val;
       val.x = pack_bf16x2(o[dt][4 * rq + 0] * inv, o[dt][4 * rq + 1] * inv);
       val.y = pack_bf16x2(o[dt][4 * rq + 2] * inv, o[dt][4 * rq + 3] * inv);
-      *reinterpret_cast<uint2 *>(op + d0) = val;
+      *reinterpret_cast<uint2 *>(stage + c32 * 256 + 16 * ((4 * dt + rq) ^ (c32 & 15)) + 8 * g) = val;
     }
   }
-  if (p.lse != nullptr && g == 0)
+  {
+    const int row0 = qb * kBlock + rw * 32;
+    uint16_t *ob = p.out + bbase + h * kHeadDim;
+    const int ch = lane & 15;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = 4 * i + (lane >> 4);
+      const uint4 val = *reinterpret_cast<const uint4 *>(stage + r * 256 + 16 * (ch ^ (r & 15)));
+      if (row0 + r < T) *reinterpret_cast<uint4 *>(ob + (int64_t)(row0 + r) * rs + 8 * ch) = val;
+    }
+  }
+  if (p.lse != nullptr && g == 0 && tq < T)
     p.lse[((int64_t)b * p.H + h) * T + tq] = (m_used + __log2f(l_tot)) * kLn2;
 }
 
