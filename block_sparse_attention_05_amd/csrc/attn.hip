@@ -94,16 +94,18 @@ __device__ __forceinline__ i32x4s buffer_rsrc(const void *base, uint32_t num_byt
 // other ring slot behind it; the caller waits (vmcnt) before the barrier that
 // publishes the data.
 // The LDS address is lds_base + kOff (kOff folded into the M0 write, so the
-// caller keeps one base register per ring slot).
+// caller keeps one base register per ring slot).  A buffer load into LDS
+// needs one wait state after an SALU write of M0, which the hardware does
+// not check: hence the s_nop.
 template <int kOff>
 __device__ __forceinline__ void lds_dma_b128(const i32x4s &rsrc, uint32_t voffset, uint32_t lds_base) {
-  asm volatile("s_add_u32 m0, %2, %3\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+  asm volatile("s_add_u32 m0, %2, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                :
                : "v"(voffset), "s"(rsrc), "s"(lds_base), "i"(kOff)
                : "memory", "m0", "scc");
 }
 __device__ __forceinline__ void lds_dma_b32(const i32x4s &rsrc, uint32_t voffset, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, 0 offen lds"
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
                :
                : "v"(voffset), "s"(rsrc), "s"(lds_base)
                : "memory", "m0");
