@@ -12,6 +12,11 @@ three calls back to back instead.  Inputs are resident in HBM
 before the timed region.  Effective FLOPs count 4*128 per (query row, key)
 pair scored exactly.
 
+After the headline timing, a second pass runs the three calls back to back
+on one stream with events between them: the per-stage times, the
+attention-only rate and the sparse kernel's roofline come from that pass,
+so each kernel is timed alone.
+
 Prints one JSON line.  ``--gpus`` above 1 is refused: this path runs on one
 GPU (a multi-GPU run would shard heads, see the design notes).
 """
@@ -140,31 +145,28 @@ def main():
     stream = torch.cuda.current_stream(dev)
     side = stream if args.one_stream else torch.cuda.Stream(dev)   # default priority
 
-    def step(ev=None):
-        # ev: events [start, after route, after sparse] on the main stream and
-        # [start, after dense] on the side stream
-        if side is not stream:
-            side.wait_stream(stream)
-        if ev is not None:
-            ev[0].record(stream)
-            ev[3].record(side)
+    def route():
         sa.sparse_attn_route(q, k, ss, wl.topk_ratio, wl.local_radius, block_idx=idx, block_cnt=cnt,
                              workspace=ws)
-        if ev is not None:
-            ev[1].record(stream)
-        if side is not stream:
-            # queued behind the pool/route launches so those dispatch first
-            with torch.cuda.stream(side):
-                sa.dense_sink_fwd(q, k, v, ss, key_bias=kb, out=out, workspace=dws)
+
+    def sparse():
         sa.sparse_attn_fwd(q, k, v, ss, idx, cnt, key_bias=kb, out=out)
-        if ev is not None:
-            ev[2].record(stream)
+
+    def dense():
+        sa.dense_sink_fwd(q, k, v, ss, key_bias=kb, out=out, workspace=dws)
+
+    def step():
         if side is stream:
-            sa.dense_sink_fwd(q, k, v, ss, key_bias=kb, out=out, workspace=dws)
-        if ev is not None:
-            ev[4].record(side)
-        if side is not stream:
-            stream.wait_stream(side)
+            route()
+            sparse()
+            dense()
+            return
+        side.wait_stream(stream)
+        route()
+        with torch.cuda.stream(side):   # queued behind the pool/route launches
+            dense()
+        sparse()
+        stream.wait_stream(side)
 
     for _ in range(args.warmup):
         step()
@@ -180,19 +182,26 @@ def main():
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
 
-    # per-stage timing: events between the launches on the stream each runs on
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    # per-stage timing: the three calls back to back on the main stream, with
+    # events between them, so that each kernel is timed alone
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for i in range(args.steps):
-        step(evs[i])
+        evs[i][0].record(stream)
+        route()
+        evs[i][1].record(stream)
+        sparse()
+        evs[i][2].record(stream)
+        dense()
+        evs[i][3].record(stream)
     torch.cuda.synchronize()
-    if side is stream:   # dense ran after sparse: time it from the sparse end
-        st = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[4])]
-                       for e in evs])
-    else:
-        st = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[3].elapsed_time(e[4])]
-                       for e in evs])
+    st = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(3)] for e in evs])
     med = np.median(st, axis=0)
+
+    # bf16 MFMA peak from this device's CU count and peak clock:
+    # 4 SIMDs x 1024 FLOP per clock per CU (one 32x32x16 MFMA per 32 clocks)
+    cu, clk_khz = sa.sa_device_info(0)
+    peak_dev = {"tflops": round(cu * clk_khz * 1e3 * 4096 / 1e12, 1), "cu": cu, "clock_mhz": clk_khz / 1e3}
 
     sparse_flops, dense_flops = effective_flops_from_lists(cnt, idx, T, nvb, H, B)
     total_flops = sparse_flops + dense_flops
@@ -219,12 +228,16 @@ def main():
         "ms_per_call": round(ms, 4),
         "frac_of_bf16_peak": round(tflops / BF16_PEAK_TFLOPS, 4),
         "effective_gflop": round(total_flops / 1e9, 3),
-        "stages_ms_median": {"route": round(float(med[0]), 4), "sparse_fwd": round(float(med[1]), 4),
+        "stages_ms_median_one_stream": {"route": round(float(med[0]), 4), "sparse_fwd": round(float(med[1]), 4),
                              "dense_fwd": round(float(med[2]), 4)},
-        "stages_ms_p10_p90": {n: [round(float(np.percentile(st[:, j], 10)), 4),
+        "stages_ms_p10_p90_one_stream": {n: [round(float(np.percentile(st[:, j], 10)), 4),
                                   round(float(np.percentile(st[:, j], 90)), 4)]
                               for j, n in enumerate(("route", "sparse_fwd", "dense_fwd"))},
         "streams": 1 if side is stream else 2,
+        "attention_only_tflops": round(total_flops / ((med[1] + med[2]) * 1e-3) / 1e12, 3),
+        "attention_only_frac_of_bf16_peak": round(total_flops / ((med[1] + med[2]) * 1e-3) / 1e12
+                                                  / BF16_PEAK_TFLOPS, 4),
+        "peak_device_tflops": peak_dev,
         "roofline": {"kernel": "attn_fwd_kernel<sparse>", "bound": "mfma", "achieved": round(achieved, 3),
                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
                      "algorithmic_gflop_per_launch": round(sparse_flops / 1e9, 3),

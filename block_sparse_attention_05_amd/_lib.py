@@ -32,6 +32,7 @@ SIGNATURES = {
     "sa_route_workspace_bytes": (_c_size, [_c_int32, _c_int32, _c_int32, _c_int32]),
     "sa_dense_workspace_bytes": (_c_size, [_c_int32, _c_int32, _c_int32, _c_int32]),
     "sa_last_error": (ctypes.c_char_p, []),
+    "sa_device_info": (ctypes.c_int, [_c_int32, _vp, _vp]),
     "sparse_attn_route": (ctypes.c_int, [
         _vp, _vp, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32,
         _c_float, _c_int32, _vp, _c_int32, _vp, _vp, _vp, _c_size, _vp]),
@@ -135,6 +136,13 @@ def sa_route_workspace_bytes(B: int, T: int, H: int, sink_start: int) -> int:
 
 def sa_dense_workspace_bytes(B: int, T: int, H: int, sink_start: int) -> int:
     return lib().sa_dense_workspace_bytes(B, T, H, sink_start)
+
+
+def sa_device_info(device: int = 0):
+    """(compute units, peak shader clock in kHz) of a HIP device."""
+    cu, clk = ctypes.c_int32(0), ctypes.c_int32(0)
+    _check(lib().sa_device_info(int(device), ctypes.byref(cu), ctypes.byref(clk)))
+    return cu.value, clk.value
 
 
 # ---- entry points ----------------------------------------------------------

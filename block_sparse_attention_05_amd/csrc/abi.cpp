@@ -121,6 +121,18 @@ size_t sa_dense_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t sink_st
 
 const char *sa_last_error(void) { return g_err; }
 
+sa_status sa_device_info(int32_t device, int32_t *cu_count, int32_t *clock_khz) {
+  if (cu_count == nullptr || clock_khz == nullptr)
+    return fail(SA_ERR_INVALID_ARG, "cu_count and clock_khz must not be NULL");
+  int cu = 0, clk = 0;
+  hipError_t e = hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, device);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&clk, hipDeviceAttributeClockRate, device);
+  if (e != hipSuccess) return fail(SA_ERR_HIP, "hipDeviceGetAttribute: %s", hipGetErrorString(e));
+  *cu_count = cu;
+  *clock_khz = clk;
+  return ok();
+}
+
 sa_status sparse_attn_route(const void *q, const void *k, int32_t B, int32_t T, int32_t H,
                             int32_t D, int32_t sink_start, int32_t sink_tokens,
                             float topk_ratio, int32_t local_radius, int32_t *block_idx,

@@ -74,8 +74,9 @@ int32_t sa_topk_budget(int32_t nvb, float ratio);
  * invalid arguments. */
 int32_t sa_max_selected(int32_t T, int32_t sink_start, float ratio, int32_t radius);
 
-/* Workspace bytes sparse_attn_route needs: the pooled fp32 means of Q and K,
- * 2 * B * H * NVB * 128 * 4 bytes. */
+/* Workspace bytes sparse_attn_route needs for the pooled means of Q and K:
+ * B * H * NVB16 * 128 * (8 + 4) bytes, NVB16 = NVB rounded up to a multiple
+ * of 16 (Q means kept as fp64 copies, K means as fp32). */
 size_t sa_route_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t sink_start);
 
 /* Workspace bytes with which dense_sink_fwd splits the key range of each
@@ -84,6 +85,13 @@ size_t sa_dense_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t sink_st
 
 /* Message of the last failed call made by this thread ("" if none). */
 const char *sa_last_error(void);
+
+/* Compute-unit count and peak shader clock (kHz) of HIP device `device`, for
+ * quoting a device-derived MFMA peak beside the published one.  Returns
+ * SA_OK, or SA_ERR_HIP (with sa_last_error() set) if the runtime query
+ * fails; both pointers must be non-NULL host pointers (SA_ERR_INVALID_ARG
+ * otherwise). */
+sa_status sa_device_info(int32_t device, int32_t *cu_count, int32_t *clock_khz);
 
 /* ---- routing ------------------------------------------------------------- */
 

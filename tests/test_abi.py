@@ -178,3 +178,9 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="missing"):
         _lib.lib()
+
+
+def test_device_info_rejects_null_pointers(L):
+    # checked on the host before any runtime query, so this runs without a GPU
+    assert L.sa_device_info(0, None, None) == 1
+    assert "must not be NULL" in L.sa_last_error().decode()
