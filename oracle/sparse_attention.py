@@ -35,6 +35,16 @@ Sol-Attn": ``sink_start=video_tokens``).  Blocks are 64 tokens (same page,
    by the video boundary) over all keys ("H3 pipeline integration": context
    query rows and the mixed final block are computed densely with the
    complete K/V).
+7. Video tail modes (same page, "H3 pipeline integration", the paragraph on
+   the video tail mode, and "Spark inference integration", last paragraph).
+   ``"dense"`` is item 6.  ``"pad"`` also routes the video block split by the
+   boundary (block NVB, real video rows ``[64*NVB, sink_start)``): its other
+   query slots are filled with the mean Q of its real rows (``pad_query_block``),
+   so its routing centroid is that mean; it is routed and attended like a
+   complete video block and only its real rows are kept.  Context rows
+   ``[sink_start, T)`` stay dense; K/V are the unmodified full sequence for
+   both paths.  The context suffix must fill the rest of that block
+   (``T >= 64*(NVB+1)``).
 
 Readings taken where the pages are silent (each also listed in the design
 notes): budget ``k = max(1, ceil(ratio*NVB - 1e-6))`` clamped to the number of
@@ -42,11 +52,16 @@ candidates; forced blocks are excluded from the candidates; neighbours are
 block index +-r clipped to the video blocks; ties go to the lower block index;
 every block holding a token >= 64*NVB is a sink block; softmax scale
 ``1/sqrt(128)``; scores are unscaled (a positive scale cannot reorder them).
+In pad mode the key side does not change: candidates are still the NVB
+complete video blocks (budget over NVB), block NVB stays a sink block, and
+the padded block's forced neighbours are the video blocks within the radius
+below it.
 
-Precision: pooled means are the correctly rounded fp32 value of the exact
-block mean (float64 sums of bf16 inputs are exact); route scores are fp32
-values of a float64 dot product of those fp32 means; attention runs in
-float64 throughout.
+Precision: pooled means are the float64 quotient of the exact float64 block
+sum (sums of bf16 inputs are exact there) by the number of rows, rounded to
+fp32; for a complete block the division by 64 is exact, so that is the
+correctly rounded mean.  Route scores are fp32 values of a float64 dot
+product of those fp32 means; attention runs in float64 throughout.
 
 Parity pins (tests/test_oracle_pins.py): every function above is pinned by a
 brute-force, closed-form or library check that does not reuse its code.
@@ -63,9 +78,12 @@ BLOCK = 64
 HEAD_DIM = 128
 NEAR_TIE_REL = 1e-5
 
+TAIL_MODES = ("dense", "pad")
+
 __all__ = [
-    "BLOCK", "HEAD_DIM", "NEAR_TIE_REL", "block_counts", "topk_budget",
-    "forced_blocks", "max_selected", "pool_means", "route_scores",
+    "BLOCK", "HEAD_DIM", "NEAR_TIE_REL", "TAIL_MODES", "block_counts",
+    "query_blocks", "sparse_rows_end", "topk_budget", "forced_blocks",
+    "max_selected", "pool_means", "pad_query_block", "route_scores",
     "select_row", "RowSelection", "Route", "route", "attend", "key_bias_vector",
     "sparse_block_output", "dense_rows_output", "routed_attention",
     "effective_flops",
@@ -84,6 +102,27 @@ def block_counts(T: int, sink_start: int) -> Tuple[int, int]:
     nb = -(-T // BLOCK)
     nvb = sink_start // BLOCK
     return nb, nvb
+
+
+def query_blocks(T: int, sink_start: int, tail_mode: str = "dense") -> int:
+    """NVQ, the routed query blocks: NVB, plus the block split by the video
+    boundary in pad mode.  Pad mode needs the context suffix to complete that
+    block (``T >= 64*(NVB+1)``), else ValueError."""
+    if tail_mode not in TAIL_MODES:
+        raise ValueError("tail_mode must be 'dense' or 'pad'")
+    _, nvb = block_counts(T, sink_start)
+    if tail_mode == "dense" or sink_start % BLOCK == 0:
+        return nvb
+    if T < (nvb + 1) * BLOCK:
+        raise ValueError("pad mode needs the context suffix to complete the split video block")
+    return nvb + 1
+
+
+def sparse_rows_end(T: int, sink_start: int, tail_mode: str = "dense") -> int:
+    """Query rows [0, end) take the sparse path, rows [end, T) the dense one."""
+    nvq = query_blocks(T, sink_start, tail_mode)
+    _, nvb = block_counts(T, sink_start)
+    return sink_start if nvq > nvb else nvb * BLOCK
 
 
 def topk_budget(nvb: int, ratio: float) -> int:
@@ -107,10 +146,11 @@ def forced_blocks(i: int, nvb: int, radius: int) -> List[int]:
     return [j for j in range(i - radius, i + radius + 1) if 0 <= j < nvb]
 
 
-def max_selected(T: int, sink_start: int, ratio: float, radius: int) -> int:
+def max_selected(T: int, sink_start: int, ratio: float, radius: int,
+                 tail_mode: str = "dense") -> int:
     """Upper bound of any exact list's length: budget + forced + sinks."""
     nb, nvb = block_counts(T, sink_start)
-    if nvb == 0:
+    if query_blocks(T, sink_start, tail_mode) == 0:
         return 0
     return min(nvb, topk_budget(nvb, ratio) + 2 * radius + 1) + (nb - nvb)
 
@@ -119,19 +159,37 @@ def max_selected(T: int, sink_start: int, ratio: float, radius: int) -> int:
 # Step 1-2: pooling and route scores
 # ---------------------------------------------------------------------------
 
-def pool_means(x: np.ndarray, nvb: int) -> np.ndarray:
-    """Mean over each complete 64-token video block.
+def pool_means(x: np.ndarray, nblocks: int, end: Optional[int] = None) -> np.ndarray:
+    """Mean over the video rows of each of the first ``nblocks`` blocks.
 
-    x: [B, T, H, D] holding bf16 values (any float dtype).  Returns fp32
-    [B, H, NVB, D]: the float64 block sum (exact for bf16 inputs of ordinary
-    range) divided by 64, rounded once to fp32.
+    Block i holds rows [64i, min(64i+64, end)); ``end`` defaults to
+    64*nblocks (complete blocks only).  x: [B, T, H, D] holding bf16 values
+    (any float dtype).  Returns fp32 [B, H, nblocks, D]: the float64 row sum
+    (exact for bf16 inputs of ordinary range) divided by the row count in
+    float64, rounded to fp32.
     """
     B, T, H, D = x.shape
-    out = np.zeros((B, H, nvb, D), dtype=np.float32)
+    end = nblocks * BLOCK if end is None else end
+    out = np.zeros((B, H, nblocks, D), dtype=np.float32)
     x64 = np.asarray(x, dtype=np.float64)
-    for i in range(nvb):
-        s = x64[:, i * BLOCK:(i + 1) * BLOCK].sum(axis=1)      # [B, H, D]
-        out[:, :, i, :] = (s / BLOCK).astype(np.float32)
+    for i in range(nblocks):
+        r0, r1 = i * BLOCK, min(i * BLOCK + BLOCK, end)
+        s = x64[:, r0:r1].sum(axis=1)                          # [B, H, D]
+        out[:, :, i, :] = (s / (r1 - r0)).astype(np.float32)
+    return out
+
+
+def pad_query_block(q: np.ndarray, b: int, h: int, i: int, sink_start: int) -> np.ndarray:
+    """The 64 query rows that pad mode runs for block i, which the video
+    boundary splits: the real video rows [64i, sink_start) and, in the other
+    slots, the float64 mean Q of those real rows.  float64 [64, D]."""
+    r0 = i * BLOCK
+    real = np.asarray(q[b, r0:sink_start, h], dtype=np.float64)
+    if not (0 < len(real) < BLOCK):
+        raise ValueError("block i is not split by the video boundary")
+    out = np.empty((BLOCK, real.shape[1]), dtype=np.float64)
+    out[:len(real)] = real
+    out[len(real):] = real.mean(axis=0)
     return out
 
 
@@ -190,27 +248,35 @@ class Route:
     nb: int
     nvb: int
     budget: int
-    qbar: np.ndarray                     # fp32 [B, H, NVB, D]
+    qbar: np.ndarray                     # fp32 [B, H, NVQ, D]
     kbar: np.ndarray                     # fp32 [B, H, NVB, D]
-    scores: np.ndarray                   # fp32 [B, H, NVB, NVB]
-    rows: List[List[List[RowSelection]]]  # [B][H][NVB]
+    scores: np.ndarray                   # fp32 [B, H, NVQ, NVB]
+    rows: List[List[List[RowSelection]]]  # [B][H][NVQ]
+    nvq: int = -1                        # routed query blocks (NVB, +1 in pad mode)
+    sparse_end: int = -1                 # query rows [0, sparse_end) are sparse
 
     def lists(self) -> List[List[List[List[int]]]]:
         return [[[r.blocks for r in hrow] for hrow in brow] for brow in self.rows]
 
 
 def route(q: np.ndarray, k: np.ndarray, sink_start: int, ratio: float,
-          radius: int) -> Route:
-    """Pool, score and select for every (batch, head, video query block)."""
+          radius: int, tail_mode: str = "dense") -> Route:
+    """Pool, score and select for every (batch, head, routed query block).
+
+    In pad mode the query block split by the video boundary is pooled over
+    its real video rows (the mean that its padded slots carry) and selects
+    among the same NVB candidates as every other query block."""
     B, T, H, D = q.shape
     nb, nvb = block_counts(T, sink_start)
+    nvq = query_blocks(T, sink_start, tail_mode)
     budget = topk_budget(nvb, ratio)
-    qbar = pool_means(q, nvb)
+    qbar = pool_means(q, nvq, end=sink_start if nvq > nvb else None)
     kbar = pool_means(k, nvb)
     scores = route_scores(qbar, kbar)
     rows = [[[select_row(scores[b, h, i], i, nvb, nb, budget, radius)
-              for i in range(nvb)] for h in range(H)] for b in range(B)]
-    return Route(nb, nvb, budget, qbar, kbar, scores, rows)
+              for i in range(nvq)] for h in range(H)] for b in range(B)]
+    return Route(nb, nvb, budget, qbar, kbar, scores, rows, nvq,
+                 sparse_rows_end(T, sink_start, tail_mode))
 
 
 # ---------------------------------------------------------------------------
@@ -254,17 +320,19 @@ def _scale(scale: Optional[float]) -> float:
 
 
 def sparse_block_output(q, k, v, b: int, h: int, i: int, blocks: Sequence[int],
-                        key_bias=None, nvb: Optional[int] = None, scale=None):
-    """Rows [64i, 64i+64) of head h over the keys of ``blocks`` (keys >= T
-    do not exist)."""
+                        key_bias=None, nvb: Optional[int] = None, scale=None,
+                        qrows: Optional[np.ndarray] = None):
+    """Rows [64i, 64i+64) of head h (or the given ``qrows``) over the keys
+    of ``blocks`` (keys >= T do not exist)."""
     T = q.shape[1]
     if nvb is None:
         raise ValueError("nvb required")
     idx = np.concatenate([np.arange(j * BLOCK, min(j * BLOCK + BLOCK, T)) for j in blocks])
     kb = key_bias_vector(key_bias, b, T, nvb)
     bias = None if kb is None else kb[idx]
-    rows = slice(i * BLOCK, min(i * BLOCK + BLOCK, T))
-    return attend(q[b, rows, h], k[b, idx, h], v[b, idx, h], bias, _scale(scale))
+    if qrows is None:
+        qrows = q[b, i * BLOCK:min(i * BLOCK + BLOCK, T), h]
+    return attend(qrows, k[b, idx, h], v[b, idx, h], bias, _scale(scale))
 
 
 def dense_rows_output(q, k, v, b: int, h: int, rows: np.ndarray,
@@ -276,25 +344,30 @@ def dense_rows_output(q, k, v, b: int, h: int, rows: np.ndarray,
 
 
 def routed_attention(q, k, v, sink_start: int, ratio: float, radius: int,
-                     key_bias=None, scale=None, rt: Optional[Route] = None):
+                     key_bias=None, scale=None, rt: Optional[Route] = None,
+                     tail_mode: str = "dense"):
     """Full forward: returns (out float64 [B,T,H,D], lse [B,H,T], Route)."""
     q = np.asarray(q)
     B, T, H, D = q.shape
     if D != HEAD_DIM:
         raise ValueError("head dim must be 128")
     if rt is None:
-        rt = route(q, k, sink_start, ratio, radius)
+        rt = route(q, k, sink_start, ratio, radius, tail_mode)
     nvb = rt.nvb
+    nvq = nvb if rt.nvq < 0 else rt.nvq
+    end = nvb * BLOCK if rt.sparse_end < 0 else rt.sparse_end
     out = np.zeros((B, T, H, D), dtype=np.float64)
     lse = np.zeros((B, H, T), dtype=np.float64)
-    dense = np.arange(nvb * BLOCK, T)
+    dense = np.arange(end, T)
     for b in range(B):
         for h in range(H):
-            for i in range(nvb):
+            for i in range(nvq):
+                r0, r1 = i * BLOCK, min(i * BLOCK + BLOCK, end)
+                padded = pad_query_block(q, b, h, i, end) if r1 - r0 < BLOCK else None
                 o, l = sparse_block_output(q, k, v, b, h, i, rt.rows[b][h][i].blocks,
-                                           key_bias, nvb, scale)
-                out[b, i * BLOCK:(i + 1) * BLOCK, h] = o
-                lse[b, h, i * BLOCK:(i + 1) * BLOCK] = l
+                                           key_bias, nvb, scale, qrows=padded)
+                out[b, r0:r1, h] = o[:r1 - r0]
+                lse[b, h, r0:r1] = l[:r1 - r0]
             if len(dense):
                 o, l = dense_rows_output(q, k, v, b, h, dense, key_bias, nvb, scale)
                 out[b, dense, h] = o
@@ -303,14 +376,18 @@ def routed_attention(q, k, v, sink_start: int, ratio: float, radius: int,
 
 
 def effective_flops(T: int, H: int, B: int, lists: Sequence, nvb: int,
-                    D: int = HEAD_DIM) -> int:
+                    D: int = HEAD_DIM, sparse_end: Optional[int] = None) -> int:
     """4*D FLOPs per (query row, valid key) pair scored exactly: QK^T and PV
-    each take 2*D.  ``lists`` is [B][H][NVB] of block lists."""
+    each take 2*D.  ``lists`` is [B][H][NVQ] of block lists; query rows
+    [0, sparse_end) (default 64*NVB) are sparse, the rest dense.  Padded
+    query slots are not counted."""
+    end = nvb * BLOCK if sparse_end is None else sparse_end
+    nvq = -(-end // BLOCK)
     pairs = 0
     for b in range(B):
         for h in range(H):
-            for i in range(nvb):
+            for i in range(nvq):
                 nk = sum(min(BLOCK, T - j * BLOCK) for j in lists[b][h][i])
-                pairs += BLOCK * nk
-    pairs += B * H * (T - nvb * BLOCK) * T
+                pairs += min(BLOCK, end - i * BLOCK) * nk
+    pairs += B * H * (T - end) * T
     return 4 * D * pairs

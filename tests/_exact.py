@@ -30,28 +30,32 @@ def round_fraction_to_f32(x: Fraction) -> np.float32:
     return np.float32(sign * m * 2.0 ** (e - 23))
 
 
-def exact_block_means(x: np.ndarray, nvb: int, block: int = 64) -> np.ndarray:
-    """x: [B, T, H, D] of bf16 values -> fp32 [B, H, NVB, D] exact means."""
+def exact_block_means(x: np.ndarray, nvb: int, block: int = 64, end: int = None) -> np.ndarray:
+    """x: [B, T, H, D] of bf16 values -> fp32 [B, H, NVB, D] exact means of
+    rows [block*i, min(block*(i+1), end)) (end defaults to block*nvb)."""
     B, T, H, D = x.shape
+    end = nvb * block if end is None else end
     out = np.zeros((B, H, nvb, D), dtype=np.float32)
     for b in range(B):
         for h in range(H):
             for i in range(nvb):
+                rows = range(i * block, min((i + 1) * block, end))
                 for d in range(D):
-                    s = sum(Fraction(float(x[b, t, h, d])) for t in range(i * block, (i + 1) * block))
-                    out[b, h, i, d] = round_fraction_to_f32(s / block)
+                    s = sum(Fraction(float(x[b, t, h, d])) for t in rows)
+                    out[b, h, i, d] = round_fraction_to_f32(s / len(rows))
     return out
 
 
 def exact_scores(qbar: np.ndarray, kbar: np.ndarray) -> np.ndarray:
-    """fp32 [B, H, N, N]: correctly rounded exact dot products."""
-    B, H, N, D = qbar.shape
-    out = np.zeros((B, H, N, N), dtype=np.float32)
+    """fp32 [B, H, NQ, NK]: correctly rounded exact dot products."""
+    B, H, NQ, D = qbar.shape
+    NK = kbar.shape[2]
+    out = np.zeros((B, H, NQ, NK), dtype=np.float32)
     for b in range(B):
         for h in range(H):
-            qf = [[Fraction(float(v)) for v in qbar[b, h, i]] for i in range(N)]
-            kf = [[Fraction(float(v)) for v in kbar[b, h, j]] for j in range(N)]
-            for i in range(N):
-                for j in range(N):
+            qf = [[Fraction(float(v)) for v in qbar[b, h, i]] for i in range(NQ)]
+            kf = [[Fraction(float(v)) for v in kbar[b, h, j]] for j in range(NK)]
+            for i in range(NQ):
+                for j in range(NK):
                     out[b, h, i, j] = round_fraction_to_f32(sum(a * c for a, c in zip(qf[i], kf[j])))
     return out

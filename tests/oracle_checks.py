@@ -354,6 +354,127 @@ def check_golden_pages_numbers():
     assert ra.topk_budget(nvb, items["default_topk_ratio"]) == 15
 
 
+# ------------------------------------------------------- pad video tail ---
+# Page "Sol-Attn and Spark for MiniMax-H3", H3 pipeline integration (video
+# tail mode) and Spark inference integration (last paragraph).
+
+def check_pad_tail_means_exact():
+    """The split block's centroid is the exact mean of its real video rows,
+    rounded to fp32; complete blocks are unchanged."""
+    x = _np(_varied_bf16((1, 320, 2, 128), seed=51))
+    got = ra.pool_means(x, 5, end=300)              # block 4 holds rows 256..299
+    want = exact_block_means(x, 5, end=300)
+    assert np.array_equal(_bits(got), _bits(want)), "tail mean is not the mean of the real rows"
+    assert np.array_equal(_bits(got[:, :, :4]), _bits(ra.pool_means(x, 4)))
+
+
+def check_pad_centroid_preserved():
+    """The padded 64-row block keeps the real rows and its plain mean is the
+    routing centroid of the split block."""
+    T, ss = 1000, 900
+    q, k, _, _ = _case(T, 2, 52, ss)
+    rt = ra.route(q, k, ss, 0.25, 1, tail_mode="pad")
+    assert (rt.nvb, rt.nvq, rt.sparse_end) == (14, 15, 900)
+    for h in range(2):
+        blk = ra.pad_query_block(q, 0, h, 14, ss)
+        assert blk.shape == (64, 128)
+        assert np.array_equal(blk[:4], q[0, 896:900, h].astype(np.float64))
+        scale = np.abs(q[0, 896:900, h]).max()
+        assert np.abs(blk.mean(axis=0) - rt.qbar[0, h, 14]).max() <= 2.0 ** -23 * scale + 1e-12 * scale
+
+
+def check_pad_route_and_mask():
+    """Pad mode against an independent path: exact centroids and scores,
+    brute-force Top-K for the split block, then a token mask over the dense
+    score matrix in which rows < sink_start use their block's list."""
+    T, ss = 1000, 900                                  # NVB=14, block 14 split at 4 rows
+    q, k, v, _ = _case(T, 2, 53, ss)
+    bias = workloads.sink_key_bias(1, T, ss, seed=54).numpy()
+    out, lse, rt = ra.routed_attention(q, k, v, ss, 0.25, 1, key_bias=bias, tail_mode="pad")
+    nvb, nb = 14, 16
+    s = exact_scores(exact_block_means(q, 15, end=ss), exact_block_means(k, nvb))
+    budget = ra.topk_budget(nvb, 0.25)
+    for h in range(2):
+        cand = list(range(nvb - 1))                    # block 13 is forced (radius 1)
+        want = _brute_topk({j: float(s[0, h, 14, j]) for j in cand}, cand, budget)
+        assert rt.rows[0][h][14].routed == want
+        assert rt.rows[0][h][14].blocks == sorted(set(want) | {13, 14, 15})
+    mask = np.full((2, T, T), -np.inf)
+    for h in range(2):
+        for t in range(T):
+            if t < ss:
+                for j in rt.rows[0][h][t // 64].blocks:
+                    mask[h, t, j * 64:min(T, j * 64 + 64)] = 0.0
+            else:
+                mask[h, t, :] = 0.0
+    mask = mask + _sink_bias_mask(T, nvb, bias)[None]
+    assert np.abs(out - _sdpa(q, k, v, mask=mask[None])).max() < 1e-12
+    qt = torch.from_numpy(q.astype(np.float64))
+    kt = torch.from_numpy(k.astype(np.float64))
+    logits = torch.einsum("bthd,bshd->bhts", qt, kt) / math.sqrt(128) + torch.from_numpy(mask[None])
+    assert np.abs(lse - torch.logsumexp(logits, dim=-1).numpy()).max() < 1e-10
+
+
+def check_pad_modes_agree_where_they_must():
+    """Aligned boundary: the modes are identical.  Split boundary: context
+    rows are the same dense rows in both modes; the real tail rows change
+    from dense to sparse."""
+    q, k, v, ss = _case(400, 2, 55, 320)
+    a, la, ra_ = ra.routed_attention(q, k, v, ss, 0.25, 1)
+    b, lb, rb = ra.routed_attention(q, k, v, ss, 0.25, 1, tail_mode="pad")
+    assert np.array_equal(a, b) and np.array_equal(la, lb) and ra_.lists() == rb.lists()
+    q, k, v, ss = _case(1000, 2, 56, 900)
+    a, la, _ = ra.routed_attention(q, k, v, ss, 0.25, 1)
+    b, lb, _ = ra.routed_attention(q, k, v, ss, 0.25, 1, tail_mode="pad")
+    assert np.abs(a[:, 900:] - b[:, 900:]).max() < 1e-12
+    assert np.abs(la[:, :, 900:] - lb[:, :, 900:]).max() < 1e-12
+    assert np.array_equal(a[:, :896], b[:, :896])
+    assert np.abs(a[:, 896:900] - b[:, 896:900]).max() > 1e-4
+
+
+def check_pad_ratio_one_and_no_complete_block():
+    """Ratio 1 reaches every key, so pad mode is full attention; with no
+    complete video block the split block's list is every (sink) block."""
+    q, k, v, ss = _case(200, 2, 57, 150)               # NVB=2, block 2 split at 22 rows
+    bias = workloads.sink_key_bias(1, 200, ss, seed=58).numpy()
+    out, _, rt = ra.routed_attention(q, k, v, ss, 1.0, 0, key_bias=bias, tail_mode="pad")
+    assert rt.nvq == 3
+    assert np.abs(out - _sdpa(q, k, v, mask=_sink_bias_mask(200, 2, bias)[None, None])).max() < 1e-12
+    q, k, v, ss = _case(150, 2, 59, 40)                # NVB=0, block 0 split at 40 rows
+    out, _, rt = ra.routed_attention(q, k, v, ss, 0.1, 1, tail_mode="pad")
+    assert (rt.nvb, rt.nvq) == (0, 1) and rt.rows[0][1][0].blocks == [0, 1, 2]
+    assert np.abs(out - _sdpa(q, k, v)).max() < 1e-12
+    assert ra.max_selected(150, 40, 0.1, 1, "pad") == 3 and ra.max_selected(150, 40, 0.1, 1) == 0
+
+
+def check_pad_needs_context_slots():
+    for T, ss in ((930, 900), (100, 70)):              # suffix cannot complete the block
+        for fn in (lambda: ra.query_blocks(T, ss, "pad"),
+                   lambda: ra.route(*_case(T, 1, 60, ss)[:2], ss, 0.1, 0, tail_mode="pad")):
+            try:
+                fn()
+            except ValueError:
+                pass
+            else:
+                raise AssertionError("pad mode accepted an incomplete tail block")
+    assert ra.query_blocks(930, 900) == 14 and ra.query_blocks(960, 900, "pad") == 15
+    try:
+        ra.query_blocks(960, 900, "Pad")
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("unknown tail mode accepted")
+
+
+def check_pad_effective_flops():
+    """Closed form: real tail rows count, padded slots do not."""
+    T, ss, nvb = 1000, 900, 14
+    lists = [[[[0, 14, 15]] * nvb + [[13, 14, 15]]]]
+    nk = 64 + 64 + 40
+    want = 4 * 128 * (nvb * 64 * nk + 4 * nk + 100 * T)
+    assert ra.effective_flops(T, 1, 1, lists, nvb, sparse_end=ss) == want
+
+
 ALL_CHECKS = [
     check_pool_exact, check_pool_permutation_invariant, check_scores_exact,
     check_budget, check_topk_bruteforce, check_signed_zero_tie, check_near_tie_flag,
@@ -362,4 +483,7 @@ ALL_CHECKS = [
     check_zero_bias_is_no_bias, check_bias_ln_m_duplicates_key, check_bias_removes_key,
     check_bias_changes_output, check_bias_ignored_on_video_keys, check_constant_v,
     check_convex_hull, check_effective_flops_h3, check_golden_pages_numbers,
+    check_pad_tail_means_exact, check_pad_centroid_preserved, check_pad_route_and_mask,
+    check_pad_modes_agree_where_they_must, check_pad_ratio_one_and_no_complete_block,
+    check_pad_needs_context_slots, check_pad_effective_flops,
 ]

@@ -12,18 +12,18 @@ import oracle_checks as oc
 _orig = {name: getattr(ra, name) for name in (
     "pool_means", "route_scores", "topk_budget", "select_row", "attend",
     "key_bias_vector", "sparse_block_output", "dense_rows_output", "forced_blocks",
-    "route")}
+    "route", "pad_query_block", "sparse_rows_end")}
 
 
-def pool_63(x, nvb):                       # off-by-one block length
-    out = _orig["pool_means"](x, nvb)
+def pool_63(x, nvb, end=None):            # off-by-one block length
+    out = _orig["pool_means"](x, nvb, end)
     x64 = np.asarray(x, np.float64)
     for i in range(nvb):
         out[:, :, i] = (x64[:, i * 64:i * 64 + 63].sum(1) / 64).astype(np.float32)
     return out
 
 
-def pool_f32_sum(x, nvb):                  # accumulates in fp32 in token order
+def pool_f32_sum(x, nvb, end=None):        # accumulates in fp32 in token order
     B, T, H, D = x.shape
     out = np.zeros((B, H, nvb, D), np.float32)
     for i in range(nvb):
@@ -100,10 +100,10 @@ def bias_on_all_keys(key_bias, b, T, nvb):
     return np.asarray(key_bias, np.float64).reshape(-1, T)[b].copy()
 
 
-def gather_shifted(q, k, v, b, h, i, blocks, key_bias=None, nvb=None, scale=None):
+def gather_shifted(q, k, v, b, h, i, blocks, key_bias=None, nvb=None, scale=None, qrows=None):
     nb = -(-q.shape[1] // 64)
     return _orig["sparse_block_output"](q, k, v, b, h, i, [min(j + 1, nb - 1) for j in blocks],
-                                        key_bias, nvb, scale)
+                                        key_bias, nvb, scale, qrows)
 
 
 def dense_without_sinks(q, k, v, b, h, rows, key_bias=None, nvb=0, scale=None):
@@ -118,8 +118,37 @@ def forced_one_sided(i, nvb, radius):
     return [j for j in range(i, i + radius + 1) if 0 <= j < nvb]
 
 
-def route_qk_swapped(q, k, sink_start, ratio, radius):
-    return _orig["route"](k, q, sink_start, ratio, radius)
+def route_qk_swapped(q, k, sink_start, ratio, radius, tail_mode="dense"):
+    return _orig["route"](k, q, sink_start, ratio, radius, tail_mode)
+
+
+# A positive rescale of one centroid cannot change its row's selection, so
+# only the pooling pin can see this one.
+def pool_tail_by_64(x, nblocks, end=None):   # split block's sum divided by 64
+    out = _orig["pool_means"](x, nblocks, end)
+    if end is not None and end < 64 * nblocks:
+        i = nblocks - 1
+        s = np.asarray(x, np.float64)[:, 64 * i:end].sum(1)
+        out[:, :, i] = (s / 64).astype(np.float32)
+    return out
+
+
+def pool_tail_physical(x, nblocks, end=None):  # pools the context rows too
+    return _orig["pool_means"](x, nblocks)
+
+
+def pad_zero_fill(q, b, h, i, sink_start):
+    blk = _orig["pad_query_block"](q, b, h, i, sink_start)
+    blk[sink_start - 64 * i:] = 0.0
+    return blk
+
+
+def route_without_tail(q, k, sink_start, ratio, radius, tail_mode="dense"):
+    return _orig["route"](q, k, sink_start, ratio, radius)
+
+
+def sparse_end_whole_block(T, sink_start, tail_mode="dense"):
+    return -(-_orig["sparse_rows_end"](T, sink_start, tail_mode) // 64) * 64
 
 
 # (oracle function, mutant, the pin expected to catch it)
@@ -144,6 +173,13 @@ MUTANTS = [
     ("forced_blocks", forced_one_sided, oc.check_topk_bruteforce),
     ("forced_blocks", forced_one_sided, oc.check_golden_pages_numbers),
     ("route", route_qk_swapped, oc.check_route_glue),
+    ("pool_means", pool_tail_by_64, oc.check_pad_tail_means_exact),
+    ("pool_means", pool_tail_physical, oc.check_pad_tail_means_exact),
+    ("pad_query_block", pad_zero_fill, oc.check_pad_centroid_preserved),
+    ("route", route_without_tail, oc.check_pad_route_and_mask),
+    ("sparse_rows_end", sparse_end_whole_block, oc.check_pad_route_and_mask),
+    ("sparse_rows_end", sparse_end_whole_block, oc.check_pad_modes_agree_where_they_must),
+    ("forced_blocks", forced_one_sided, oc.check_pad_route_and_mask),
 ]
 
 
