@@ -18,6 +18,9 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsparse_a
 SA_OK, SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_WORKSPACE, SA_ERR_HIP = range(5)
 HEAD_DIM = 128
 BLOCK = 64
+# video tail modes: where the real rows of a video block split by the video
+# boundary are computed (dense path, or routed and sparse)
+VIDEO_TAIL_MODES = {"dense": 0, "pad": 1}
 
 _lib = None
 
@@ -27,20 +30,21 @@ _c_int32, _c_int64, _c_size, _c_float, _vp = (ctypes.c_int32, ctypes.c_int64, ct
 SIGNATURES = {
     "sa_num_blocks": (_c_int32, [_c_int32]),
     "sa_num_sparse_blocks": (_c_int32, [_c_int32, _c_int32]),
+    "sa_num_query_blocks": (_c_int32, [_c_int32, _c_int32, _c_int32]),
     "sa_topk_budget": (_c_int32, [_c_int32, _c_float]),
-    "sa_max_selected": (_c_int32, [_c_int32, _c_int32, _c_float, _c_int32]),
-    "sa_route_workspace_bytes": (_c_size, [_c_int32, _c_int32, _c_int32, _c_int32]),
+    "sa_max_selected": (_c_int32, [_c_int32, _c_int32, _c_int32, _c_float, _c_int32]),
+    "sa_route_workspace_bytes": (_c_size, [_c_int32, _c_int32, _c_int32, _c_int32, _c_int32]),
     "sa_dense_workspace_bytes": (_c_size, [_c_int32, _c_int32, _c_int32, _c_int32]),
     "sa_last_error": (ctypes.c_char_p, []),
     "sa_device_info": (ctypes.c_int, [_c_int32, _vp, _vp]),
     "sparse_attn_route": (ctypes.c_int, [
-        _vp, _vp, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32,
+        _vp, _vp, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32,
         _c_float, _c_int32, _vp, _c_int32, _vp, _vp, _vp, _c_size, _vp]),
     "sparse_attn_fwd": (ctypes.c_int, [
-        _vp, _vp, _vp, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32,
+        _vp, _vp, _vp, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32,
         _vp, _c_int64, _vp, _vp, _c_int32, _c_float, _vp, _vp, _vp]),
     "dense_sink_fwd": (ctypes.c_int, [
-        _vp, _vp, _vp, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32,
+        _vp, _vp, _vp, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32,
         _vp, _c_int64, _c_float, _vp, _vp, _vp, _c_size, _vp]),
 }
 
@@ -97,6 +101,12 @@ def _check_qkv(*ts: torch.Tensor):
             raise ValueError("q, k, v must share shape and device")
 
 
+def _mode(video_tail_mode) -> int:
+    if video_tail_mode not in VIDEO_TAIL_MODES:
+        raise ValueError(f"video_tail_mode must be one of {sorted(VIDEO_TAIL_MODES)}")
+    return VIDEO_TAIL_MODES[video_tail_mode]
+
+
 def _bias(key_bias: Optional[torch.Tensor], B: int, T: int, device):
     """Normalize the natural-log key bias to the float32 [B, T] contract;
     reject a wrong element count before anything runs."""
@@ -122,16 +132,22 @@ def sa_num_sparse_blocks(T: int, sink_start: int) -> int:
     return lib().sa_num_sparse_blocks(T, sink_start)
 
 
+def sa_num_query_blocks(T: int, sink_start: int, video_tail_mode: str = "dense") -> int:
+    return lib().sa_num_query_blocks(T, sink_start, _mode(video_tail_mode))
+
+
 def sa_topk_budget(nvb: int, ratio: float) -> int:
     return lib().sa_topk_budget(nvb, ratio)
 
 
-def sa_max_selected(T: int, sink_start: int, ratio: float, radius: int) -> int:
-    return lib().sa_max_selected(T, sink_start, ratio, radius)
+def sa_max_selected(T: int, sink_start: int, ratio: float, radius: int,
+                    video_tail_mode: str = "dense") -> int:
+    return lib().sa_max_selected(T, sink_start, _mode(video_tail_mode), ratio, radius)
 
 
-def sa_route_workspace_bytes(B: int, T: int, H: int, sink_start: int) -> int:
-    return lib().sa_route_workspace_bytes(B, T, H, sink_start)
+def sa_route_workspace_bytes(B: int, T: int, H: int, sink_start: int,
+                             video_tail_mode: str = "dense") -> int:
+    return lib().sa_route_workspace_bytes(B, T, H, sink_start, _mode(video_tail_mode))
 
 
 def sa_dense_workspace_bytes(B: int, T: int, H: int, sink_start: int) -> int:
@@ -149,51 +165,61 @@ def sa_device_info(device: int = 0):
 
 def sparse_attn_route(q: torch.Tensor, k: torch.Tensor, sink_start: int,
                       topk_ratio: float = 0.1, local_radius: int = 0, *,
+                      video_tail_mode: str = "dense",
                       max_sel: Optional[int] = None, block_idx: Optional[torch.Tensor] = None,
                       block_cnt: Optional[torch.Tensor] = None,
                       route_scores: Optional[torch.Tensor] = None,
                       workspace: Optional[torch.Tensor] = None,
                       ) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Exact block lists of every video query block.  Returns
-    (block_idx int32 [B,H,NVB,max_sel], block_cnt int32 [B,H,NVB]);
-    ``route_scores`` (fp32 [B,H,NVB,NVB]) is filled when given."""
+    """Exact block lists of every routed query block.  Returns
+    (block_idx int32 [B,H,NVQ,max_sel], block_cnt int32 [B,H,NVQ]);
+    ``route_scores`` (fp32 [B,H,NVQ,NVB]) is filled when given.  NVQ is NVB,
+    plus the block split by the video boundary in pad mode."""
     _check_qkv(q, k)
     B, T, H, D = q.shape
     L = lib()
+    mode = _mode(video_tail_mode)
     nvb = L.sa_num_sparse_blocks(T, sink_start)
     if nvb < 0:
         raise ValueError("sink_start must lie in [0, T]")
-    need = L.sa_max_selected(T, sink_start, topk_ratio, local_radius)
+    nvq = L.sa_num_query_blocks(T, sink_start, mode)
+    if nvq < 0:
+        raise ValueError("pad mode needs the context suffix to complete the split video block "
+                         "(T >= 64*(NVB+1))")
+    need = L.sa_max_selected(T, sink_start, mode, topk_ratio, local_radius)
     if max_sel is None:
         max_sel = max(need, 1)
     dev = q.device
     if block_idx is None:
-        block_idx = torch.empty((B, H, nvb, max_sel), dtype=torch.int32, device=dev)
+        block_idx = torch.empty((B, H, nvq, max_sel), dtype=torch.int32, device=dev)
     if block_cnt is None:
-        block_cnt = torch.empty((B, H, nvb), dtype=torch.int32, device=dev)
-    ws_bytes = L.sa_route_workspace_bytes(B, T, H, sink_start)
+        block_cnt = torch.empty((B, H, nvq), dtype=torch.int32, device=dev)
+    ws_bytes = L.sa_route_workspace_bytes(B, T, H, sink_start, mode)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     for name, t, dt in (("block_idx", block_idx, torch.int32), ("block_cnt", block_cnt, torch.int32)):
         if t.dtype != dt or not t.is_contiguous() or t.device != dev:
             raise ValueError(f"{name} must be a contiguous int32 tensor on {dev}")
-    if block_idx.numel() < B * H * nvb * max_sel or block_cnt.numel() < B * H * nvb:
+    if block_idx.numel() < B * H * nvq * max_sel or block_cnt.numel() < B * H * nvq:
         raise ValueError("block_idx / block_cnt too small")
     if route_scores is not None and (route_scores.dtype != torch.float32 or not route_scores.is_contiguous()
-                                     or route_scores.numel() < B * H * nvb * nvb):
-        raise ValueError("route_scores must be contiguous float32 [B,H,NVB,NVB]")
+                                     or route_scores.numel() < B * H * nvq * nvb
+                                     or route_scores.device != dev):
+        raise ValueError("route_scores must be contiguous float32 [B,H,NVQ,NVB] on the device of q")
     _check(L.sparse_attn_route(
-        _ptr(q), _ptr(k), B, T, H, D, sink_start, T - sink_start, float(topk_ratio),
+        _ptr(q), _ptr(k), B, T, H, D, sink_start, T - sink_start, mode, float(topk_ratio),
         int(local_radius), _ptr(block_idx), int(max_sel), _ptr(block_cnt), _ptr(route_scores),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(dev)))
     return block_idx, block_cnt
 
 
 def sparse_attn_fwd(q, k, v, sink_start: int, block_idx: torch.Tensor, block_cnt: torch.Tensor, *,
+                    video_tail_mode: str = "dense",
                     key_bias: Optional[torch.Tensor] = None, softmax_scale: float = 0.0,
                     out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
-    """Exact attention of rows [0, 64*NVB) over their block lists; writes
-    those rows of ``out`` (allocated if None) and returns it."""
+    """Exact attention of the sparse rows ([0, 64*NVB), or [0, sink_start)
+    in pad mode) over their block lists; writes those rows of ``out``
+    (allocated if None) and returns it."""
     _check_qkv(q, k, v)
     B, T, H, D = q.shape
     if out is None:
@@ -202,28 +228,33 @@ def sparse_attn_fwd(q, k, v, sink_start: int, block_idx: torch.Tensor, block_cnt
     if block_idx.dtype != torch.int32 or block_cnt.dtype != torch.int32 or \
             not block_idx.is_contiguous() or not block_cnt.is_contiguous():
         raise ValueError("block_idx / block_cnt must be contiguous int32")
-    nvb = lib().sa_num_sparse_blocks(T, sink_start)
+    mode = _mode(video_tail_mode)
+    nvq = lib().sa_num_query_blocks(T, sink_start, mode)
     max_sel = block_idx.shape[-1] if block_idx.dim() == 4 else 0
-    if nvb > 0 and (block_idx.dim() != 4 or tuple(block_idx.shape[:3]) != (B, H, nvb)
-                    or block_cnt.numel() != B * H * nvb):
-        raise ValueError("block_idx must be [B,H,NVB,max_sel] and block_cnt [B,H,NVB]")
+    if nvq > 0 and (block_idx.dim() != 4 or tuple(block_idx.shape[:3]) != (B, H, nvq)
+                    or block_cnt.numel() != B * H * nvq):
+        raise ValueError("block_idx must be [B,H,NVQ,max_sel] and block_cnt [B,H,NVQ]")
+    if block_idx.device != q.device or block_cnt.device != q.device:
+        raise ValueError("block_idx / block_cnt must be on the device of q")
     if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != B * H * T):
         raise ValueError("lse must be contiguous float32 [B,H,T]")
     kb, kb_n = _bias(key_bias, B, T, q.device)
     _check(lib().sparse_attn_fwd(
-        _ptr(q), _ptr(k), _ptr(v), B, T, H, D, sink_start, T - sink_start, _ptr(kb), kb_n,
+        _ptr(q), _ptr(k), _ptr(v), B, T, H, D, sink_start, T - sink_start, mode, _ptr(kb), kb_n,
         _ptr(block_idx), _ptr(block_cnt), int(max_sel), float(softmax_scale), _ptr(out), _ptr(lse),
         _stream(q.device)))
     return out
 
 
-def dense_sink_fwd(q, k, v, sink_start: int, *, key_bias: Optional[torch.Tensor] = None,
+def dense_sink_fwd(q, k, v, sink_start: int, *, video_tail_mode: str = "dense",
+                   key_bias: Optional[torch.Tensor] = None,
                    softmax_scale: float = 0.0, out: Optional[torch.Tensor] = None,
                    lse: Optional[torch.Tensor] = None, workspace="auto"):
-    """Dense attention of rows [64*NVB, T) over all keys; writes those rows
-    of ``out`` (allocated if None) and returns it.  ``workspace``: a uint8
-    device tensor, None (no key split), or "auto" (allocate what the split
-    needs)."""
+    """Dense attention of the dense rows ([64*NVB, T), or [sink_start, T) in
+    pad mode) over all keys; writes those rows of ``out`` (allocated if
+    None) and returns it.  ``workspace``: a uint8 device tensor, None (no
+    key split), or "auto" (allocate what the split needs)."""
+    mode = _mode(video_tail_mode)
     _check_qkv(q, k, v)
     B, T, H, D = q.shape
     if out is None:
@@ -237,12 +268,13 @@ def dense_sink_fwd(q, k, v, sink_start: int, *, key_bias: Optional[torch.Tensor]
         workspace = torch.empty(n, dtype=torch.uint8, device=q.device) if n > 0 else None
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().dense_sink_fwd(
-        _ptr(q), _ptr(k), _ptr(v), B, T, H, D, sink_start, T - sink_start, _ptr(kb), kb_n,
+        _ptr(q), _ptr(k), _ptr(v), B, T, H, D, sink_start, T - sink_start, mode, _ptr(kb), kb_n,
         float(softmax_scale), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, _stream(q.device)))
     return out
 
 
 def routed_attention(q, k, v, sink_start: int, topk_ratio: float = 0.1, local_radius: int = 0, *,
+                     video_tail_mode: str = "dense",
                      key_bias: Optional[torch.Tensor] = None, softmax_scale: float = 0.0,
                      return_lse: bool = False, return_route: bool = False,
                      dense_stream: Optional[torch.cuda.Stream] = None):
@@ -254,20 +286,21 @@ def routed_attention(q, k, v, sink_start: int, topk_ratio: float = 0.1, local_ra
     cur = torch.cuda.current_stream(q.device)
     if dense_stream is not None:
         dense_stream.wait_stream(cur)
-    block_idx, block_cnt = sparse_attn_route(q, k, sink_start, topk_ratio, local_radius)
+    block_idx, block_cnt = sparse_attn_route(q, k, sink_start, topk_ratio, local_radius,
+                                             video_tail_mode=video_tail_mode)
     B, T, H, _ = q.shape
     out = torch.empty_like(q)
     lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device) if return_lse else None
     if dense_stream is not None:
         # launched behind the routing kernels so those dispatch first
         with torch.cuda.stream(dense_stream):
-            dense_sink_fwd(q, k, v, sink_start, key_bias=key_bias, softmax_scale=softmax_scale,
-                           out=out, lse=lse)
-    sparse_attn_fwd(q, k, v, sink_start, block_idx, block_cnt, key_bias=key_bias,
-                    softmax_scale=softmax_scale, out=out, lse=lse)
+            dense_sink_fwd(q, k, v, sink_start, video_tail_mode=video_tail_mode,
+                           key_bias=key_bias, softmax_scale=softmax_scale, out=out, lse=lse)
+    sparse_attn_fwd(q, k, v, sink_start, block_idx, block_cnt, video_tail_mode=video_tail_mode,
+                    key_bias=key_bias, softmax_scale=softmax_scale, out=out, lse=lse)
     if dense_stream is None:
-        dense_sink_fwd(q, k, v, sink_start, key_bias=key_bias, softmax_scale=softmax_scale,
-                       out=out, lse=lse)
+        dense_sink_fwd(q, k, v, sink_start, video_tail_mode=video_tail_mode, key_bias=key_bias,
+                       softmax_scale=softmax_scale, out=out, lse=lse)
     else:
         cur.wait_stream(dense_stream)
     res = [out]

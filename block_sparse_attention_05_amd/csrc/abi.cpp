@@ -30,9 +30,24 @@ sa_status ok() {
 
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// Routed query blocks (NVQ) and the end of the sparse rows for a valid
+// (T, sink_start, mode); NVQ = -1 when pad mode lacks the context slots that
+// complete the split block.
+struct Split {
+  int32_t nvb, nvq, rows_end;
+};
+
+Split split_rows(int32_t T, int32_t sink_start, int32_t mode) {
+  const int32_t nvb = sink_start / sa::kBlock;
+  if (mode == SA_VIDEO_TAIL_DENSE || sink_start % sa::kBlock == 0)
+    return {nvb, nvb, nvb * sa::kBlock};
+  if ((int64_t)T < (int64_t)(nvb + 1) * sa::kBlock) return {nvb, -1, -1};
+  return {nvb, nvb + 1, sink_start};
+}
+
 // Shape checks shared by the three entry points.
 sa_status check_shape(int32_t B, int32_t T, int32_t H, int32_t D, int32_t sink_start,
-                      int32_t sink_tokens) {
+                      int32_t sink_tokens, int32_t mode) {
   if (D != sa::kHeadDim) return fail(SA_ERR_INVALID_ARG, "D must be 128 (got %d)", D);
   if (B <= 0 || T <= 0 || H <= 0)
     return fail(SA_ERR_INVALID_ARG, "B, T, H must be positive (got %d, %d, %d)", B, T, H);
@@ -42,6 +57,13 @@ sa_status check_shape(int32_t B, int32_t T, int32_t H, int32_t D, int32_t sink_s
   if ((int64_t)sink_start + sink_tokens != T)
     return fail(SA_ERR_INVALID_ARG, "sink_start + sink_tokens must equal T (%d + %d != %d)",
                 sink_start, sink_tokens, T);
+  if (mode != SA_VIDEO_TAIL_DENSE && mode != SA_VIDEO_TAIL_PAD)
+    return fail(SA_ERR_INVALID_ARG, "video_tail_mode must be 0 (dense) or 1 (pad), got %d", mode);
+  if (split_rows(T, sink_start, mode).nvq < 0)
+    return fail(SA_ERR_INVALID_ARG,
+                "pad mode needs T >= 64*(NVB+1) = %d so the context suffix completes the split "
+                "video block (T=%d)",
+                (sink_start / sa::kBlock + 1) * sa::kBlock, T);
   // every launch indexes workgroups with int and elements with int64
   const int64_t nb = (T + sa::kBlock - 1) / sa::kBlock;
   if ((int64_t)B * H * nb > INT32_MAX / 2)
@@ -93,24 +115,35 @@ int32_t sa_topk_budget(int32_t nvb, float ratio) {
   return k < 1.0 ? 1 : (int32_t)k;
 }
 
-int32_t sa_max_selected(int32_t T, int32_t sink_start, float ratio, int32_t radius) {
+int32_t sa_num_query_blocks(int32_t T, int32_t sink_start, int32_t video_tail_mode) {
+  if (sink_start < 0 || sink_start > T) return -1;
+  if (video_tail_mode != SA_VIDEO_TAIL_DENSE && video_tail_mode != SA_VIDEO_TAIL_PAD) return -1;
+  return split_rows(T, sink_start, video_tail_mode).nvq;
+}
+
+int32_t sa_max_selected(int32_t T, int32_t sink_start, int32_t video_tail_mode, float ratio,
+                        int32_t radius) {
+  const int32_t nvq = sa_num_query_blocks(T, sink_start, video_tail_mode);
   const int32_t nvb = sa_num_sparse_blocks(T, sink_start);
-  if (nvb < 0 || radius < 0) return -1;
+  if (nvq < 0 || radius < 0) return -1;
   const int32_t budget = sa_topk_budget(nvb, ratio);
   if (budget < 0) return -1;
-  if (nvb == 0) return 0;
+  if (nvq == 0) return 0;
   const int64_t local = (int64_t)budget + 2 * (int64_t)radius + 1;
   const int32_t routed = local < nvb ? (int32_t)local : nvb;
   return routed + (sa_num_blocks(T) - nvb);
 }
 
-size_t sa_route_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t sink_start) {
+size_t sa_route_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t sink_start,
+                                int32_t video_tail_mode) {
+  const int32_t nvq = sa_num_query_blocks(T, sink_start, video_tail_mode);
   const int32_t nvb = sa_num_sparse_blocks(T, sink_start);
-  if (B <= 0 || H <= 0 || nvb <= 0) return 0;
-  // query means in fp64, then key means in fp32, each over NVB rounded up to
-  // a multiple of 16 blocks
+  if (B <= 0 || H <= 0 || nvq <= 0) return 0;
+  // query means in fp64 over NVQ, then key means in fp32 over NVB, each
+  // rounded up to a multiple of 16 blocks
+  const size_t nvq16 = ((size_t)nvq + 15) / 16 * 16;
   const size_t nvb16 = ((size_t)nvb + 15) / 16 * 16;
-  return (size_t)B * (size_t)H * nvb16 * sa::kHeadDim * (sizeof(double) + sizeof(float));
+  return (size_t)B * (size_t)H * sa::kHeadDim * (nvq16 * sizeof(double) + nvb16 * sizeof(float));
 }
 
 size_t sa_dense_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t sink_start) {
@@ -135,17 +168,19 @@ sa_status sa_device_info(int32_t device, int32_t *cu_count, int32_t *clock_khz) 
 
 sa_status sparse_attn_route(const void *q, const void *k, int32_t B, int32_t T, int32_t H,
                             int32_t D, int32_t sink_start, int32_t sink_tokens,
-                            float topk_ratio, int32_t local_radius, int32_t *block_idx,
-                            int32_t max_sel, int32_t *block_cnt, float *route_scores,
-                            void *workspace, size_t workspace_bytes, void *stream) {
-  sa_status st = check_shape(B, T, H, D, sink_start, sink_tokens);
+                            int32_t video_tail_mode, float topk_ratio, int32_t local_radius,
+                            int32_t *block_idx, int32_t max_sel, int32_t *block_cnt,
+                            float *route_scores, void *workspace, size_t workspace_bytes,
+                            void *stream) {
+  sa_status st = check_shape(B, T, H, D, sink_start, sink_tokens, video_tail_mode);
   if (st != SA_OK) return st;
   if ((st = check_bf16(q, "q")) != SA_OK) return st;
   if ((st = check_bf16(k, "k")) != SA_OK) return st;
   if (!(topk_ratio > 0.f && topk_ratio <= 1.f))
     return fail(SA_ERR_INVALID_ARG, "topk_ratio must lie in (0, 1]");
   if (local_radius < 0) return fail(SA_ERR_INVALID_ARG, "local_radius must be >= 0");
-  const int32_t nvb = sa_num_sparse_blocks(T, sink_start);
+  const Split sp = split_rows(T, sink_start, video_tail_mode);
+  const int32_t nvb = sp.nvb;
   const int32_t nb = sa_num_blocks(T);
   if ((int64_t)B * H > 65535)
     return fail(SA_ERR_UNSUPPORTED, "routing supports B*H up to 65535 (got %lld)",
@@ -153,16 +188,17 @@ sa_status sparse_attn_route(const void *q, const void *k, int32_t B, int32_t T, 
   if (nvb > sa::kMaxRouteBlocks)
     return fail(SA_ERR_UNSUPPORTED, "at most %d video blocks can be routed (got %d)",
                 sa::kMaxRouteBlocks, nvb);
-  const int32_t need_sel = sa_max_selected(T, sink_start, topk_ratio, local_radius);
+  const int32_t need_sel =
+      sa_max_selected(T, sink_start, video_tail_mode, topk_ratio, local_radius);
   if (max_sel < need_sel)
     return fail(SA_ERR_INVALID_ARG, "max_sel must be >= %d (got %d)", need_sel, max_sel);
-  if (nvb == 0) return ok();
+  if (sp.nvq == 0) return ok();
   if (block_idx == nullptr || block_cnt == nullptr)
     return fail(SA_ERR_INVALID_ARG, "block_idx and block_cnt must not be NULL");
   if (!aligned(block_idx, 4) || !aligned(block_cnt, 4) ||
       (route_scores != nullptr && !aligned(route_scores, 4)))
     return fail(SA_ERR_INVALID_ARG, "block_idx, block_cnt, route_scores must be 4-byte aligned");
-  const size_t need_ws = sa_route_workspace_bytes(B, T, H, sink_start);
+  const size_t need_ws = sa_route_workspace_bytes(B, T, H, sink_start, video_tail_mode);
   if (workspace_bytes < need_ws)
     return fail(SA_ERR_WORKSPACE, "workspace must hold %zu bytes (got %zu)", need_ws,
                 workspace_bytes);
@@ -170,12 +206,15 @@ sa_status sparse_attn_route(const void *q, const void *k, int32_t B, int32_t T, 
     return fail(SA_ERR_WORKSPACE, "workspace must be a 16-byte aligned device pointer");
 
   const int32_t budget = sa_topk_budget(nvb, topk_ratio);
+  // a radius beyond NVB forces the same blocks as NVB (and keeps i + radius
+  // inside int in the kernel)
+  const int32_t radius = local_radius < nvb ? local_radius : nvb;
   double *qbar = static_cast<double *>(workspace);
-  float *kbar = reinterpret_cast<float *>(qbar + (size_t)B * H * (((size_t)nvb + 15) / 16 * 16) * sa::kHeadDim);
+  float *kbar = reinterpret_cast<float *>(qbar + (size_t)B * H * (((size_t)sp.nvq + 15) / 16 * 16) * sa::kHeadDim);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = sa::launch_pool(q, k, qbar, kbar, B, T, H, nvb, s);
+  hipError_t e = sa::launch_pool(q, k, qbar, kbar, B, T, H, sp.nvq, nvb, sp.rows_end, s);
   if (e != hipSuccess) return fail(SA_ERR_HIP, "pool launch: %s", hipGetErrorString(e));
-  e = sa::launch_route(qbar, kbar, B, H, nvb, nb, budget, local_radius, max_sel, block_idx,
+  e = sa::launch_route(qbar, kbar, B, H, sp.nvq, nvb, nb, budget, radius, max_sel, block_idx,
                        block_cnt, route_scores, s);
   if (e != hipSuccess) return fail(SA_ERR_HIP, "route launch: %s", hipGetErrorString(e));
   return ok();
@@ -183,10 +222,10 @@ sa_status sparse_attn_route(const void *q, const void *k, int32_t B, int32_t T, 
 
 sa_status sparse_attn_fwd(const void *q, const void *k, const void *v, int32_t B, int32_t T,
                           int32_t H, int32_t D, int32_t sink_start, int32_t sink_tokens,
-                          const float *key_bias, int64_t key_bias_numel,
+                          int32_t video_tail_mode, const float *key_bias, int64_t key_bias_numel,
                           const int32_t *block_idx, const int32_t *block_cnt, int32_t max_sel,
                           float softmax_scale, void *out, float *lse, void *stream) {
-  sa_status st = check_shape(B, T, H, D, sink_start, sink_tokens);
+  sa_status st = check_shape(B, T, H, D, sink_start, sink_tokens, video_tail_mode);
   if (st != SA_OK) return st;
   if ((st = check_bf16(q, "q")) != SA_OK) return st;
   if ((st = check_bf16(k, "k")) != SA_OK) return st;
@@ -196,8 +235,8 @@ sa_status sparse_attn_fwd(const void *q, const void *k, const void *v, int32_t B
   float scale_log2 = 0.f;
   if ((st = check_scale(softmax_scale, &scale_log2)) != SA_OK) return st;
   if (lse != nullptr && !aligned(lse, 4)) return fail(SA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
-  const int32_t nvb = sa_num_sparse_blocks(T, sink_start);
-  if (nvb == 0) return ok();
+  const Split sp = split_rows(T, sink_start, video_tail_mode);
+  if (sp.nvq == 0) return ok();
   if (block_idx == nullptr || block_cnt == nullptr)
     return fail(SA_ERR_INVALID_ARG, "block_idx and block_cnt must not be NULL");
   if (!aligned(block_idx, 4) || !aligned(block_cnt, 4))
@@ -217,7 +256,9 @@ sa_status sparse_attn_fwd(const void *q, const void *k, const void *v, int32_t B
   a.T = T;
   a.H = H;
   a.nb = sa_num_blocks(T);
-  a.nvb = nvb;
+  a.nvb = sp.nvb;
+  a.nvq = sp.nvq;
+  a.rows_end = sp.rows_end;
   a.max_sel = max_sel;
   a.scale_log2 = scale_log2;
   hipError_t e = sa::launch_attn_sparse(a, static_cast<hipStream_t>(stream));
@@ -227,10 +268,10 @@ sa_status sparse_attn_fwd(const void *q, const void *k, const void *v, int32_t B
 
 sa_status dense_sink_fwd(const void *q, const void *k, const void *v, int32_t B, int32_t T,
                          int32_t H, int32_t D, int32_t sink_start, int32_t sink_tokens,
-                         const float *key_bias, int64_t key_bias_numel, float softmax_scale,
-                         void *out, float *lse, void *workspace, size_t workspace_bytes,
-                         void *stream) {
-  sa_status st = check_shape(B, T, H, D, sink_start, sink_tokens);
+                         int32_t video_tail_mode, const float *key_bias, int64_t key_bias_numel,
+                         float softmax_scale, void *out, float *lse, void *workspace,
+                         size_t workspace_bytes, void *stream) {
+  sa_status st = check_shape(B, T, H, D, sink_start, sink_tokens, video_tail_mode);
   if (st != SA_OK) return st;
   if ((st = check_bf16(q, "q")) != SA_OK) return st;
   if ((st = check_bf16(k, "k")) != SA_OK) return st;
@@ -240,8 +281,8 @@ sa_status dense_sink_fwd(const void *q, const void *k, const void *v, int32_t B,
   float scale_log2 = 0.f;
   if ((st = check_scale(softmax_scale, &scale_log2)) != SA_OK) return st;
   if (lse != nullptr && !aligned(lse, 4)) return fail(SA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
-  const int32_t nvb = sa_num_sparse_blocks(T, sink_start);
-  if ((int64_t)nvb * sa::kBlock == T) return ok();
+  const Split sp = split_rows(T, sink_start, video_tail_mode);
+  if (sp.rows_end == T) return ok();
   if (workspace_bytes > 0 && (workspace == nullptr || !aligned(workspace, 16)))
     return fail(SA_ERR_WORKSPACE, "workspace must be a 16-byte aligned device pointer");
 
@@ -256,7 +297,9 @@ sa_status dense_sink_fwd(const void *q, const void *k, const void *v, int32_t B,
   a.T = T;
   a.H = H;
   a.nb = sa_num_blocks(T);
-  a.nvb = nvb;
+  a.nvb = sp.nvb;
+  a.nvq = sp.nvq;
+  a.rows_end = sp.rows_end;
   a.max_sel = 0;
   a.scale_log2 = scale_log2;
   hipError_t e = sa::launch_attn_dense(a, workspace, workspace_bytes, static_cast<hipStream_t>(stream));

@@ -13,6 +13,16 @@
 // own online-softmax state; the two key halves of each row are merged at the
 // end.
 //
+// Only rows in [row_lo, row_hi) are written.  That is how a query block split
+// by the video boundary is served: in the pad video tail mode (same page, H3
+// pipeline integration) the sparse path writes its real video rows and the
+// dense path its context rows.  The pages fill the block's non-video query
+// slots with the mean Q of its real rows; here those slots keep the context
+// rows' Q and their results are dropped.  The outputs are the same: a query
+// row's softmax and output do not depend on the other rows of its block, and
+// the block's routing centroid (the real rows' mean) is formed by the pooling
+// kernel.
+//
 // Data movement.  K and V tiles (64 keys x 256 B) go from HBM/L2 straight to
 // LDS with buffer_load ... lds (no register staging): the tile's base is in
 // the per-lane offset, so keys past T fall outside the buffer range and read
@@ -131,6 +141,7 @@ struct Params {
   float *part_ml;     // split-KV partial (max, sum) per row
   int B, T, H, nb, nvb, max_sel;
   int qb0, nqb;
+  int row_lo, row_hi;  // rows written: [row_lo, row_hi)
   int nsplit, tiles_per_split;
   float scale_log2;
 };
@@ -187,7 +198,7 @@ void attn_fwd_kernel(Params p) {
     const int pe = p.nvb < t_end ? p.nvb : t_end;
     n_plain = pe > t_begin ? pe - t_begin : 0;
   } else {
-    const int64_t li = (int64_t)bh * p.nvb + qb;
+    const int64_t li = (int64_t)bh * p.nqb + qbi;
     list = p.block_idx + li * p.max_sel;
     // The first 64 entries are read together with the count (the two loads
     // do not depend on each other).
@@ -611,10 +622,11 @@ void attn_fwd_kernel(Params p) {
     for (int i = 0; i < 8; ++i) {
       const int r = 4 * i + (lane >> 4);
       const uint4 val = *reinterpret_cast<const uint4 *>(stage + r * 256 + 16 * (ch ^ (r & 15)));
-      if (row0 + r < T) *reinterpret_cast<uint4 *>(ob + (int64_t)(row0 + r) * rs + 8 * ch) = val;
+      if (row0 + r >= p.row_lo && row0 + r < p.row_hi)
+        *reinterpret_cast<uint4 *>(ob + (int64_t)(row0 + r) * rs + 8 * ch) = val;
     }
   }
-  if (p.lse != nullptr && g == 0 && tq < T)
+  if (p.lse != nullptr && g == 0 && tq >= p.row_lo && tq < p.row_hi)
     p.lse[((int64_t)b * p.H + h) * T + tq] = (m_used + __log2f(l_tot)) * kLn2;
 }
 
@@ -635,7 +647,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(Params p) {
   const int row = (blockIdx.x % kChunks) * kCombineRows + threadIdx.x / (kHeadDim / 4);
   const int d0 = (threadIdx.x % (kHeadDim / 4)) * 4;
   const int tq = (p.qb0 + qbi) * kBlock + row;
-  if (tq >= T) return;
+  if (tq < p.row_lo || tq >= p.row_hi) return;
   const int64_t prow0 = (int64_t)wq * p.nsplit * kBlock + row;   // split s: prow0 + s * kBlock
   float m = -INFINITY;
   for (int s = 0; s < p.nsplit; ++s) m = fmaxf(m, p.part_ml[2 * (prow0 + (int64_t)s * kBlock)]);
@@ -680,6 +692,8 @@ Params make_params(const AttnArgs &a, int qb0, int nqb) {
   p.max_sel = a.max_sel;
   p.qb0 = qb0;
   p.nqb = nqb;
+  p.row_lo = 0;
+  p.row_hi = a.T;
   p.nsplit = 1;
   p.tiles_per_split = a.nb;
   p.scale_log2 = a.scale_log2;
@@ -709,9 +723,10 @@ size_t dense_workspace_bytes(int B, int H, int nb, int nvb) {
 }
 
 hipError_t launch_attn_sparse(const AttnArgs &a, hipStream_t stream) {
-  if (a.nvb <= 0) return hipSuccess;
-  const Params p = make_params(a, 0, a.nvb);
-  const int total = a.B * a.H * a.nvb;
+  if (a.nvq <= 0) return hipSuccess;
+  Params p = make_params(a, 0, a.nvq);
+  p.row_hi = a.rows_end;
+  const int total = a.B * a.H * a.nvq;
   hipLaunchKernelGGL(attn_fwd_kernel<false>, dim3(total), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
@@ -719,8 +734,9 @@ hipError_t launch_attn_sparse(const AttnArgs &a, hipStream_t stream) {
 hipError_t launch_attn_dense(const AttnArgs &a, void *workspace, size_t workspace_bytes,
                              hipStream_t stream) {
   const int nq = a.nb - a.nvb;
-  if (nq <= 0) return hipSuccess;
+  if (nq <= 0 || a.rows_end >= a.T) return hipSuccess;
   Params p = make_params(a, a.nvb, nq);
+  p.row_lo = a.rows_end;
   const int s = dense_splits(a.B, a.H, a.nb, a.nvb);
   if (s > 1 && workspace != nullptr && workspace_bytes >= dense_workspace_bytes(a.B, a.H, a.nb, a.nvb)) {
     p.nsplit = s;

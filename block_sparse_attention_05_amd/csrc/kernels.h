@@ -12,13 +12,15 @@ constexpr int kBlock = 64;     // tokens per routing block
 constexpr int kHeadDim = 128;  // head dimension
 constexpr int kMaxRouteBlocks = 1024;  // widest per-row sort in the route kernel
 
-// Mean of every complete 64-token video block of Q and K:
-// qbar/kbar fp32 [B, H, nvb, 128].
+// Means of the routed blocks: Q blocks [0, nvq) over rows below q_end (a
+// split last block only over its real rows), K blocks [0, nvb), in the route
+// kernel's operand order (query tiles ceil(nvq/16), key tiles ceil(nvb/16)).
 hipError_t launch_pool(const void *q, const void *k, double *qbar, float *kbar,
-                       int B, int T, int H, int nvb, hipStream_t stream);
+                       int B, int T, int H, int nvq, int nvb, int q_end, hipStream_t stream);
 
-// Route scores, Top-K and list emission for every (b, h, query block < nvb).
-hipError_t launch_route(const double *qbar, const float *kbar, int B, int H, int nvb,
+// Route scores, Top-K and list emission for every (b, h, query block < nvq)
+// against the key blocks [0, nvb).
+hipError_t launch_route(const double *qbar, const float *kbar, int B, int H, int nvq, int nvb,
                         int nb, int budget, int radius, int max_sel, int32_t *block_idx,
                         int32_t *block_cnt, float *scores, hipStream_t stream);
 
@@ -27,15 +29,17 @@ struct AttnArgs {
   void *out;                  // bf16 [B, T, H, 128]
   float *lse;                 // nullable fp32 [B, H, T]
   const float *key_bias;      // nullable fp32 [B, T], natural log
-  const int32_t *block_idx;   // sparse only
-  const int32_t *block_cnt;   // sparse only
+  const int32_t *block_idx;   // sparse only: [B, H, nvq, max_sel]
+  const int32_t *block_cnt;   // sparse only: [B, H, nvq]
   int B, T, H, nb, nvb, max_sel;
+  int nvq;                    // routed query blocks
+  int rows_end;               // rows [0, rows_end) are sparse, [rows_end, T) dense
   float scale_log2;           // softmax_scale * log2(e)
 };
 
-// Sparse rows [0, 64*nvb) over their block lists.
+// Sparse rows [0, rows_end) of query blocks [0, nvq) over their block lists.
 hipError_t launch_attn_sparse(const AttnArgs &a, hipStream_t stream);
-// Dense rows [64*nvb, T) over all keys.  With a workspace of at least
+// Dense rows [rows_end, T) over all keys.  With a workspace of at least
 // dense_workspace_bytes() the key range of each query block is split over
 // dense_splits() workgroups whose partial results are merged by a second
 // kernel; otherwise one workgroup walks all keys.

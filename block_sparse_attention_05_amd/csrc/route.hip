@@ -7,7 +7,11 @@
 // chunked Sol-Attn producers", Tests and source audit: sink blocks go straight
 // into the exact list and are never routed candidates.
 //
-// One workgroup (8 wavefronts) serves 16 query blocks of one (b, h):
+// One workgroup (8 wavefronts) serves 16 query blocks of one (b, h).  Query
+// blocks are the nvq routed ones: the nvb complete video blocks and, in the
+// pad video tail mode, block nvb, split by the video boundary (first page,
+// H3 pipeline integration); it is routed like the others, its forced
+// neighbours being the video blocks within the radius below it.
 //  1. scores s_ij for its 16 rows against every key block j < nvb on fp64
 //     MFMA (v_mfma_f64_16x16x4f64), one 16-key tile per accumulator.
 //     fp32 x fp32 products are exact in fp64, so the fp64 dot product
@@ -140,8 +144,8 @@ __device__ __forceinline__ uint32_t tournament_select(const uint32_t (&u)[E], in
 
 template <int E>
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(
-    const double *__restrict__ qbar, const float *__restrict__ kbar, int H, int nvb, int nb,
-    int budget, int radius, int max_sel, int32_t *__restrict__ block_idx,
+    const double *__restrict__ qbar, const float *__restrict__ kbar, int H, int nvq, int nvb,
+    int nb, int budget, int radius, int max_sel, int32_t *__restrict__ block_idx,
     int32_t *__restrict__ block_cnt, float *__restrict__ scores_out) {
   constexpr int ld = 64 * E;  // LDS score row stride (floats)
   extern __shared__ __align__(16) float sc[];  // [kRouteRows][ld]
@@ -151,15 +155,16 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
-  const int nt = (nvb + 15) >> 4;
-  route_scores_tile(reinterpret_cast<const double2 *>(qbar) + ((int64_t)bh * nt + blockIdx.x) * 16 * 64,
-                    reinterpret_cast<const float4 *>(kbar) + (int64_t)bh * nt * 8 * 64, nt, sc, ld,
+  const int ntq = (nvq + 15) >> 4;  // query and key tiles
+  const int ntk = (nvb + 15) >> 4;
+  route_scores_tile(reinterpret_cast<const double2 *>(qbar) + ((int64_t)bh * ntq + blockIdx.x) * 16 * 64,
+                    reinterpret_cast<const float4 *>(kbar) + (int64_t)bh * ntk * 8 * 64, ntk, sc, ld,
                     lane, wave);
   __syncthreads();
 
   for (int rr = wave; rr < kRouteRows; rr += kRouteWaves) {
     const int i = i0 + rr;
-    if (i >= nvb) break;  // wave-uniform
+    if (i >= nvq) break;  // wave-uniform
     const int f_lo = i - radius < 0 ? 0 : i - radius;
     const int f_hi = i + radius > nvb - 1 ? nvb - 1 : i + radius;
     const int n_cand = nvb - (f_hi - f_lo + 1);
@@ -172,7 +177,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     for (int e = 0; e < E; ++e) {
       const int j = 64 * e + lane;
       const float s = sc[rr * ld + j];
-      if (scores_out != nullptr && j < nvb) scores_out[((int64_t)bh * nvb + i) * nvb + j] = s;
+      if (scores_out != nullptr && j < nvb) scores_out[((int64_t)bh * nvq + i) * nvb + j] = s;
       const bool v = j < nvb && (j < f_lo || j > f_hi);
       u[e] = v ? order_key(s) : 0u;
       mn = v && u[e] < mn ? u[e] : mn;
@@ -218,7 +223,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     // stopped on it, or (stop = -1) its first rem keys by block index
     const uint32_t hm = high_bits(stop);
     const uint32_t ph = pre & hm;
-    int32_t *out = block_idx + ((int64_t)bh * nvb + i) * max_sel;
+    int32_t *out = block_idx + ((int64_t)bh * nvq + i) * max_sel;
     int base = 0, ties = rem;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
@@ -240,45 +245,37 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     for (int j = nvb + lane; j < nb; j += 64) out[base + (j - nvb)] = j;
     const int cnt = base + (nb - nvb);
     for (int x = cnt + lane; x < max_sel; x += 64) out[x] = -1;
-    if (lane == 0) block_cnt[(int64_t)bh * nvb + i] = cnt;
+    if (lane == 0) block_cnt[(int64_t)bh * nvq + i] = cnt;
   }
 }
 
 template <int E>
-hipError_t launch_route_e(const double *qbar, const float *kbar, int B, int H, int nvb, int nb,
-                          int budget, int radius, int max_sel, int32_t *block_idx,
+hipError_t launch_route_e(const double *qbar, const float *kbar, int B, int H, int nvq, int nvb,
+                          int nb, int budget, int radius, int max_sel, int32_t *block_idx,
                           int32_t *block_cnt, float *scores, hipStream_t stream) {
-  dim3 grid((nvb + kRouteRows - 1) / kRouteRows, B * H);
+  dim3 grid((nvq + kRouteRows - 1) / kRouteRows, B * H);
   const size_t lds = (size_t)kRouteRows * 64 * E * sizeof(float);
   hipLaunchKernelGGL((route_kernel<E>), grid, dim3(kRouteThreads), lds, stream, qbar, kbar, H,
-                     nvb, nb, budget, radius, max_sel, block_idx, block_cnt, scores);
+                     nvq, nvb, nb, budget, radius, max_sel, block_idx, block_cnt, scores);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_route(const double *qbar, const float *kbar, int B, int H, int nvb, int nb,
-                        int budget, int radius, int max_sel, int32_t *block_idx,
+hipError_t launch_route(const double *qbar, const float *kbar, int B, int H, int nvq, int nvb,
+                        int nb, int budget, int radius, int max_sel, int32_t *block_idx,
                         int32_t *block_cnt, float *scores, hipStream_t stream) {
-  if (nvb <= 0) return hipSuccess;
-  if (nvb <= 64)
-    return launch_route_e<1>(qbar, kbar, B, H, nvb, nb, budget, radius, max_sel, block_idx,
-                             block_cnt, scores, stream);
-  if (nvb <= 128)
-    return launch_route_e<2>(qbar, kbar, B, H, nvb, nb, budget, radius, max_sel, block_idx,
-                             block_cnt, scores, stream);
-  if (nvb <= 192)
-    return launch_route_e<3>(qbar, kbar, B, H, nvb, nb, budget, radius, max_sel, block_idx,
-                             block_cnt, scores, stream);
-  if (nvb <= 256)
-    return launch_route_e<4>(qbar, kbar, B, H, nvb, nb, budget, radius, max_sel, block_idx,
-                                block_cnt, scores, stream);
-  if (nvb <= 512)
-    return launch_route_e<8>(qbar, kbar, B, H, nvb, nb, budget, radius, max_sel, block_idx,
-                             block_cnt, scores, stream);
-  if (nvb <= kMaxRouteBlocks)
-    return launch_route_e<16>(qbar, kbar, B, H, nvb, nb, budget, radius, max_sel, block_idx,
-                              block_cnt, scores, stream);
+  if (nvq <= 0) return hipSuccess;
+#define SA_ROUTE_E(E)                                                                       \
+  launch_route_e<E>(qbar, kbar, B, H, nvq, nvb, nb, budget, radius, max_sel, block_idx, \
+                    block_cnt, scores, stream)
+  if (nvb <= 64) return SA_ROUTE_E(1);
+  if (nvb <= 128) return SA_ROUTE_E(2);
+  if (nvb <= 192) return SA_ROUTE_E(3);
+  if (nvb <= 256) return SA_ROUTE_E(4);
+  if (nvb <= 512) return SA_ROUTE_E(8);
+  if (nvb <= kMaxRouteBlocks) return SA_ROUTE_E(16);
+#undef SA_ROUTE_E
   return hipErrorInvalidValue;
 }
 

@@ -12,11 +12,23 @@
  * (same page, "Spark primitives").  With
  *     NB  = ceil(T / 64)        all blocks (the last may be partial),
  *     NVB = sink_start / 64     complete video blocks,
- * blocks [0, NVB) are routed, and every block holding a token >= 64*NVB is a
- * sink block.  Query rows [0, 64*NVB) take the sparse path; rows
- * [64*NVB, T) (context rows and a video block split by the boundary) take the
- * dense path over all keys ("H3 pipeline integration": context query rows
- * and the mixed final block are computed densely with the complete K/V).
+ * key blocks [0, NVB) are routed, and every block holding a token >= 64*NVB
+ * is a sink block.  Where the video boundary splits block NVB
+ * (sink_start % 64 != 0), `video_tail_mode` says which path its real video
+ * rows take (same page, "H3 pipeline integration", the video tail mode
+ * paragraph, and "Spark inference integration", last paragraph):
+ *   SA_VIDEO_TAIL_DENSE (0, the pages' default): query blocks [0, NVB) are
+ *     routed and rows [0, 64*NVB) take the sparse path; rows [64*NVB, T)
+ *     (the split block and the context rows) take the dense path over all
+ *     keys.
+ *   SA_VIDEO_TAIL_PAD (1): the split block is routed too, so NVQ = NVB + 1
+ *     query blocks; its non-video query slots count as holding the mean Q of
+ *     its real rows, so its routing centroid is that mean.  Rows
+ *     [0, sink_start) take the sparse path and only the context rows
+ *     [sink_start, T) the dense one.  The context suffix must complete the
+ *     split block: T >= 64*(NVB+1), else SA_ERR_INVALID_ARG.
+ * With sink_start % 64 == 0 the two modes are the same (NVQ = NVB).  K/V are
+ * the complete, unmodified sequence for both paths in both modes.
  *
  * A full call is sparse_attn_route + sparse_attn_fwd + dense_sink_fwd on one
  * stream.
@@ -47,6 +59,11 @@ extern "C" {
 #endif
 
 typedef enum {
+  SA_VIDEO_TAIL_DENSE = 0,
+  SA_VIDEO_TAIL_PAD = 1
+} sa_video_tail_mode;
+
+typedef enum {
   SA_OK = 0,
   SA_ERR_INVALID_ARG = 1,
   SA_ERR_UNSUPPORTED = 2,
@@ -63,6 +80,12 @@ int32_t sa_num_blocks(int32_t T);
  * [0, T]. */
 int32_t sa_num_sparse_blocks(int32_t T, int32_t sink_start);
 
+/* NVQ, the routed query blocks: NVB, or NVB + 1 in pad mode when the video
+ * boundary splits block NVB.  -1 if sink_start is not in [0, T], the mode is
+ * unknown, or pad mode lacks the context slots that complete the split block
+ * (T < 64*(NVB+1)). */
+int32_t sa_num_query_blocks(int32_t T, int32_t sink_start, int32_t video_tail_mode);
+
 /* Fixed-ratio Top-K budget before clamping: max(1, ceil(ratio * nvb - 1e-6))
  * with the product in double (page "Sol-Attn and Spark for MiniMax-H3",
  * "Spark inference integration": native mean Top-K routing with ratio 0.1).
@@ -70,17 +93,22 @@ int32_t sa_num_sparse_blocks(int32_t T, int32_t sink_start);
 int32_t sa_topk_budget(int32_t nvb, float ratio);
 
 /* Longest exact list any query block can get:
- * min(NVB, budget + 2*radius + 1) + (NB - NVB); 0 when NVB == 0; -1 on
+ * min(NVB, budget + 2*radius + 1) + (NB - NVB); 0 when NVQ == 0; -1 on
  * invalid arguments. */
-int32_t sa_max_selected(int32_t T, int32_t sink_start, float ratio, int32_t radius);
+int32_t sa_max_selected(int32_t T, int32_t sink_start, int32_t video_tail_mode, float ratio,
+                        int32_t radius);
 
 /* Workspace bytes sparse_attn_route needs for the pooled means of Q and K:
- * B * H * NVB16 * 128 * (8 + 4) bytes, NVB16 = NVB rounded up to a multiple
- * of 16 (Q means kept as fp64 copies, K means as fp32). */
-size_t sa_route_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t sink_start);
+ * B * H * 128 * (NVQ16 * 8 + NVB16 * 4) bytes, NVQ16 / NVB16 = NVQ / NVB
+ * rounded up to a multiple of 16 (Q means kept as fp64 copies, K means as
+ * fp32); 0 when NVQ <= 0. */
+size_t sa_route_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t sink_start,
+                                int32_t video_tail_mode);
 
 /* Workspace bytes with which dense_sink_fwd splits the key range of each
- * dense query block over several workgroups (0 when it would not split). */
+ * dense query block over several workgroups (0 when it would not split).
+ * The same in both video tail modes (the dense path walks blocks
+ * [NVB, NB) in both). */
 size_t sa_dense_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t sink_start);
 
 /* Message of the last failed call made by this thread ("" if none). */
@@ -108,12 +136,18 @@ sa_status sa_device_info(int32_t device, int32_t *cu_count, int32_t *clock_khz);
  * chunked Sol-Attn producers", Tests and source audit (sink blocks are put
  * straight into the exact list and excluded from the routed candidates).
  *
- * Computes, for every batch b, head h and query block i < NVB:
- *   qbar_i, kbar_j = fp32 mean of the 64 Q (K) rows of block i (j); the sum
- *                    is exact, so the mean is correctly rounded;
+ * Computes, for every batch b, head h and query block i < NVQ:
+ *   qbar_i         = mean of the Q rows of block i below 64*NVB (dense mode)
+ *                    or sink_start (pad mode): 64 rows, or the real video
+ *                    rows of the split block; kbar_j = mean of the 64 K rows
+ *                    of block j < NVB.  The fp64 sum is exact; the mean is
+ *                    the fp64 quotient by the row count rounded to fp32
+ *                    (correctly rounded for 64 rows);
  *   s_ij           = qbar_i . kbar_j for j < NVB, fp32 of a float64 dot
  *                    product (unscaled);
- *   F(i)           = { j : |j - i| <= local_radius } within [0, NVB);
+ *   F(i)           = { j : |j - i| <= local_radius } within [0, NVB) (for
+ *                    the split block i = NVB: the video blocks within the
+ *                    radius below it);
  *   R(i)           = the first min(budget, NVB - |F(i)|) blocks of
  *                    [0, NVB) \ F(i) ordered by (s_ij descending, j
  *                    ascending), -0.0 equal to +0.0;
@@ -123,28 +157,36 @@ sa_status sa_device_info(int32_t device, int32_t *cu_count, int32_t *clock_khz);
  * D             must be 128.
  * sink_start    video tokens, 0 <= sink_start <= T; sink_tokens must equal
  *               T - sink_start.
+ * video_tail_mode  SA_VIDEO_TAIL_DENSE or SA_VIDEO_TAIL_PAD (see the top of
+ *               this file); the same value must be passed to
+ *               sparse_attn_fwd and dense_sink_fwd.
  * topk_ratio    in (0, 1].  local_radius >= 0.
- * block_idx     int32 [B, H, NVB, max_sel] out: ascending lists, padded -1.
- * max_sel       >= sa_max_selected(T, sink_start, topk_ratio, local_radius).
- * block_cnt     int32 [B, H, NVB] out: list lengths.
- * route_scores  nullable; fp32 [B, H, NVB, NVB] out: s_ij.
+ * block_idx     int32 [B, H, NVQ, max_sel] out: ascending lists, padded -1.
+ * max_sel       >= sa_max_selected(T, sink_start, video_tail_mode,
+ *               topk_ratio, local_radius).
+ * block_cnt     int32 [B, H, NVQ] out: list lengths.
+ * route_scores  nullable; fp32 [B, H, NVQ, NVB] out: s_ij.
  * workspace     device scratch of workspace_bytes >=
- *               sa_route_workspace_bytes(B, T, H, sink_start), 16-byte
- *               aligned.  The pooled means are left there, over NVB16 = NVB
- *               rounded up to a multiple of 16 blocks: first the Q means
- *               (fp64 copies of the fp32 means), then the K means (fp32),
- *               each in the operand order of the route kernel's fp64 MFMA:
+ *               sa_route_workspace_bytes(B, T, H, sink_start,
+ *               video_tail_mode), 16-byte aligned.  The pooled means are
+ *               left there: first the Q means over NVQ16 blocks (fp64 copies
+ *               of the fp32 means), then the K means over NVB16 blocks
+ *               (fp32), NVQ16 / NVB16 = NVQ / NVB rounded up to a multiple of
+ *               16, each in the operand order of the route kernel's fp64 MFMA:
  *               mean (b, h, block i, channel d) sits at piece
  *               [b][h][i / 16][s][16 * (d / 32) + i % 16], element d % 32 - w*s,
  *               where a piece holds w = 2 (Q) or 4 (K) consecutive steps and
  *               s = (d % 32) / w.  May be NULL when that size is 0.
  * Errors: SA_ERR_UNSUPPORTED when NVB > 1024 (per-row selection width) or
  * B*H > 65535 (launch grid).
- * With NVB == 0 nothing is enqueued and SA_OK is returned.
+ * With NVQ == 0 nothing is enqueued and SA_OK is returned.  With NVB == 0
+ * and NVQ == 1 (pad mode, no complete video block) the one list is every
+ * block [0, NB).
  */
 sa_status sparse_attn_route(const void *q, const void *k,
                             int32_t B, int32_t T, int32_t H, int32_t D,
                             int32_t sink_start, int32_t sink_tokens,
+                            int32_t video_tail_mode,
                             float topk_ratio, int32_t local_radius,
                             int32_t *block_idx, int32_t max_sel, int32_t *block_cnt,
                             float *route_scores,
@@ -154,8 +196,9 @@ sa_status sparse_attn_route(const void *q, const void *k,
 /* ---- attention ----------------------------------------------------------- */
 
 /*
- * sparse_attn_fwd - exact attention of the video query rows [0, 64*NVB)
- * over the keys of their block lists.
+ * sparse_attn_fwd - exact attention of the sparse query rows (rows
+ * [0, 64*NVB) in dense mode, [0, sink_start) in pad mode) over the keys of
+ * their block lists.
  *
  * Defined by: page "Sol-Attn and Spark for MiniMax-H3", "Spark inference
  * integration" (K/V tiles streamed through one FP32 online-softmax/output
@@ -164,7 +207,7 @@ sa_status sparse_attn_route(const void *q, const void *k,
  * to log2 units and consumed only by the exact branch; biased key blocks must
  * be sink-routed).
  *
- * For row t of query block i and key j in a block of list(i), j < T:
+ * For row t of query block i < NVQ and key j in a block of list(i), j < T:
  *   l_tj = softmax_scale * (q_t . k_j) + beta_j,
  *   beta_j = key_bias[b, j] if j >= 64*NVB (a sink key) else 0,
  *   out_t = sum_j softmax_j(l_t) v_j  (bf16, round to nearest even),
@@ -176,15 +219,18 @@ sa_status sparse_attn_route(const void *q, const void *k,
  *               on non-sink keys are ignored (callers must keep biased keys
  *               in sink blocks).
  * block_idx, block_cnt, max_sel  as produced by sparse_attn_route with the
- *               same B, T, H, sink_start.  Entries outside [0, NB) are
- *               skipped and counts are clamped to max_sel.
+ *               same B, T, H, sink_start, video_tail_mode ([B, H, NVQ, ...]).
+ *               Entries outside [0, NB) are skipped and counts are clamped
+ *               to max_sel.
  * softmax_scale 0 selects 1/sqrt(128).
- * out           bf16 [B, T, H, 128]; only rows [0, 64*NVB) are written.
- * lse           nullable fp32 [B, H, T]; only rows [0, 64*NVB) are written.
+ * out           bf16 [B, T, H, 128]; only the sparse rows are written.
+ * lse           nullable fp32 [B, H, T]; only the sparse rows are written.
+ * With NVQ == 0 nothing is enqueued.
  */
 sa_status sparse_attn_fwd(const void *q, const void *k, const void *v,
                           int32_t B, int32_t T, int32_t H, int32_t D,
                           int32_t sink_start, int32_t sink_tokens,
+                          int32_t video_tail_mode,
                           const float *key_bias, int64_t key_bias_numel,
                           const int32_t *block_idx, const int32_t *block_cnt, int32_t max_sel,
                           float softmax_scale,
@@ -192,13 +238,14 @@ sa_status sparse_attn_fwd(const void *q, const void *k, const void *v,
                           void *stream);
 
 /*
- * dense_sink_fwd - dense attention of query rows [64*NVB, T) (context query
- * rows and a video block split by the boundary) over all T keys, same
- * formula, same bias rule and the same kernel as sparse_attn_fwd (page
+ * dense_sink_fwd - dense attention of the dense query rows (rows [64*NVB, T)
+ * in dense mode: context rows and a video block split by the boundary;
+ * rows [sink_start, T) in pad mode: context rows only) over all T keys,
+ * same formula, same bias rule and the same kernel as sparse_attn_fwd (page
  * "Sol-Attn and Spark for MiniMax-H3", "H3 pipeline integration": context
  * query rows are computed with dense attention over the complete K/V).
  *
- * out / lse     only rows [64*NVB, T) are written.  With 64*NVB == T
+ * out / lse     only the dense rows are written.  With none (64*NVB == T)
  *               nothing is enqueued.
  * workspace     optional device scratch.  With workspace_bytes >=
  *               sa_dense_workspace_bytes(B, T, H, sink_start) > 0 the keys of
@@ -210,6 +257,7 @@ sa_status sparse_attn_fwd(const void *q, const void *k, const void *v,
 sa_status dense_sink_fwd(const void *q, const void *k, const void *v,
                          int32_t B, int32_t T, int32_t H, int32_t D,
                          int32_t sink_start, int32_t sink_tokens,
+                         int32_t video_tail_mode,
                          const float *key_bias, int64_t key_bias_numel,
                          float softmax_scale,
                          void *out, float *lse,

@@ -30,13 +30,17 @@ def run_gpu(wl, *, key_bias=None, ratio=None, radius=None, scores=True, lse=True
     radius = wl.local_radius if radius is None else radius
     kb = key_bias if key_bias is not None else wl.key_bias
     kb = None if kb is None else kb.to(dev)
+    mode = wl.tail_mode
     nb, nvb = ora.block_counts(T, wl.sink_start)
-    sc = torch.full((B, H, nvb, nvb), float("nan"), device=dev) if (scores and nvb) else None
-    idx, cnt = sa.sparse_attn_route(q, k, wl.sink_start, ratio, radius, route_scores=sc)
+    nvq = ora.query_blocks(T, wl.sink_start, mode)
+    sc = torch.full((B, H, nvq, nvb), float("nan"), device=dev) if (scores and nvb) else None
+    idx, cnt = sa.sparse_attn_route(q, k, wl.sink_start, ratio, radius, video_tail_mode=mode,
+                                    route_scores=sc)
     out = torch.full_like(q, float("nan"))
     ls = torch.full((B, H, T), float("nan"), device=dev) if lse else None
-    sa.sparse_attn_fwd(q, k, v, wl.sink_start, idx, cnt, key_bias=kb, out=out, lse=ls)
-    sa.dense_sink_fwd(q, k, v, wl.sink_start, key_bias=kb, out=out, lse=ls)
+    sa.sparse_attn_fwd(q, k, v, wl.sink_start, idx, cnt, video_tail_mode=mode, key_bias=kb,
+                       out=out, lse=ls)
+    sa.dense_sink_fwd(q, k, v, wl.sink_start, video_tail_mode=mode, key_bias=kb, out=out, lse=ls)
     torch.cuda.synchronize()
     return dict(out=out.cpu(), lse=None if ls is None else ls.cpu(), idx=idx.cpu(), cnt=cnt.cpu(),
                 scores=None if sc is None else sc.cpu())

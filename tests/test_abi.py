@@ -51,49 +51,67 @@ def test_shape_helpers_match_oracle(L):
                 continue
             nb, nvb = ora.block_counts(T, ss)
             assert L.sa_num_sparse_blocks(T, ss) == nvb
-            for ratio in (0.1, 0.25, 1.0 / 3.0, 1.0):
-                for r in (0, 1, 2):
-                    assert L.sa_max_selected(T, ss, ratio, r) == ora.max_selected(T, ss, ratio, r)
+            for mode, name in ((0, "dense"), (1, "pad")):
+                assert L.sa_num_query_blocks(T, ss, mode) == _or_minus_one(ora.query_blocks, T, ss, name)
+                for ratio in (0.1, 0.25, 1.0 / 3.0, 1.0):
+                    for r in (0, 1, 2):
+                        assert L.sa_max_selected(T, ss, mode, ratio, r) == \
+                            _or_minus_one(ora.max_selected, T, ss, ratio, r, name)
     assert L.sa_num_sparse_blocks(10, 11) == -1
+    assert L.sa_num_query_blocks(10, 11, 0) == -1 and L.sa_num_query_blocks(100, 64, 2) == -1
+    assert L.sa_num_query_blocks(1000, 900, 1) == 15 and L.sa_num_query_blocks(930, 900, 1) == -1
     for nvb in list(range(0, 40)) + [128, 144, 512, 1024]:
         for ratio in (1e-4, 0.05, 0.1, 0.2, 0.25, 0.3, 1.0 / 3.0, 0.5, 0.9, 1.0):
             assert L.sa_topk_budget(nvb, ratio) == ora.topk_budget(nvb, ratio), (nvb, ratio)
     assert L.sa_topk_budget(10, 0.0) == -1 and L.sa_topk_budget(10, 1.5) == -1
     assert L.sa_topk_budget(10, float("nan")) == -1
-    assert L.sa_route_workspace_bytes(1, 9505, 56, 9216) == 56 * 144 * 128 * (8 + 4)
-    assert L.sa_route_workspace_bytes(1, 9505, 56, 10) == 0
+    assert L.sa_route_workspace_bytes(1, 9505, 56, 9216, 0) == 56 * 144 * 128 * (8 + 4)
+    assert L.sa_route_workspace_bytes(1, 9505, 56, 9216, 1) == 56 * 144 * 128 * (8 + 4)
+    assert L.sa_route_workspace_bytes(1, 9505, 56, 10, 0) == 0
+    # pad mode: query means over NVQ = 1 (rounded to 16 blocks), no key means
+    assert L.sa_route_workspace_bytes(1, 9505, 56, 10, 1) == 56 * 16 * 128 * 8
+    # NVB = 144, NVQ = 145: query tiles 10, key tiles 9
+    assert L.sa_route_workspace_bytes(2, 9505, 56, 9216 + 5, 1) == 2 * 56 * 128 * (160 * 8 + 144 * 4)
+    assert L.sa_route_workspace_bytes(1, 930, 2, 900, 1) == 0
     assert L.sa_dense_workspace_bytes(1, 9216, 56, 9216) == 0          # no dense rows
     assert L.sa_dense_workspace_bytes(1, 9505, 56, 9216) % (64 * 130 * 4) == 0
+
+
+def _or_minus_one(fn, *args):
+    try:
+        return fn(*args)
+    except ValueError:
+        return -1
 
 
 FAKE = ctypes.c_void_p(1 << 20)     # aligned, never dereferenced: validation fails first
 
 
 def _route(L, **kw):
-    a = dict(q=FAKE, k=FAKE, B=1, T=1024, H=2, D=128, ss=1024, st=0, ratio=0.25, radius=0,
+    a = dict(q=FAKE, k=FAKE, B=1, T=1024, H=2, D=128, ss=1024, st=0, mode=0, ratio=0.25, radius=0,
              idx=FAKE, max_sel=5, cnt=FAKE, scores=None, ws=FAKE, ws_bytes=1 << 20, stream=None)
     a.update(kw)
     return L.sparse_attn_route(a["q"], a["k"], a["B"], a["T"], a["H"], a["D"], a["ss"], a["st"],
-                               a["ratio"], a["radius"], a["idx"], a["max_sel"], a["cnt"],
+                               a["mode"], a["ratio"], a["radius"], a["idx"], a["max_sel"], a["cnt"],
                                a["scores"], a["ws"], a["ws_bytes"], a["stream"])
 
 
 def _fwd(L, **kw):
-    a = dict(q=FAKE, k=FAKE, v=FAKE, B=1, T=1024, H=2, D=128, ss=1024, st=0, bias=None,
+    a = dict(q=FAKE, k=FAKE, v=FAKE, B=1, T=1024, H=2, D=128, ss=1024, st=0, mode=0, bias=None,
              bias_n=0, idx=FAKE, cnt=FAKE, max_sel=5, scale=0.0, out=FAKE, lse=None, stream=None)
     a.update(kw)
     return L.sparse_attn_fwd(a["q"], a["k"], a["v"], a["B"], a["T"], a["H"], a["D"], a["ss"],
-                             a["st"], a["bias"], a["bias_n"], a["idx"], a["cnt"], a["max_sel"],
-                             a["scale"], a["out"], a["lse"], a["stream"])
+                             a["st"], a["mode"], a["bias"], a["bias_n"], a["idx"], a["cnt"],
+                             a["max_sel"], a["scale"], a["out"], a["lse"], a["stream"])
 
 
 def _dense(L, **kw):
-    a = dict(q=FAKE, k=FAKE, v=FAKE, B=1, T=1000, H=2, D=128, ss=900, st=100, bias=None,
+    a = dict(q=FAKE, k=FAKE, v=FAKE, B=1, T=1000, H=2, D=128, ss=900, st=100, mode=0, bias=None,
              bias_n=0, scale=0.0, out=FAKE, lse=None, ws=None, ws_bytes=0, stream=None)
     a.update(kw)
     return L.dense_sink_fwd(a["q"], a["k"], a["v"], a["B"], a["T"], a["H"], a["D"], a["ss"],
-                            a["st"], a["bias"], a["bias_n"], a["scale"], a["out"], a["lse"],
-                            a["ws"], a["ws_bytes"], a["stream"])
+                            a["st"], a["mode"], a["bias"], a["bias_n"], a["scale"], a["out"],
+                            a["lse"], a["ws"], a["ws_bytes"], a["stream"])
 
 
 INVALID, UNSUPPORTED, WORKSPACE = 1, 2, 3
@@ -117,6 +135,14 @@ ROUTE_CASES = [
     (dict(ws=None), WORKSPACE, "workspace"),
     (dict(T=65600, ss=65600, max_sel=200, ratio=0.1), UNSUPPORTED, "video blocks"),
     (dict(B=2, H=40000, T=64, ss=64, max_sel=1), UNSUPPORTED, "B*H"),
+    (dict(mode=2), INVALID, "video_tail_mode"),
+    (dict(mode=-1), INVALID, "video_tail_mode"),
+    (dict(mode=1, T=930, ss=900, st=30, max_sel=20), INVALID, "pad mode needs"),
+    # pad mode, NVB = 15, NVQ = 16, NB = 19: a list holds up to 3 routed + 3
+    # forced + 4 sink blocks; the means take 2 heads x 128 x (16 x 8 + 16 x 4) B
+    (dict(mode=1, T=1174, ss=1007, st=167, max_sel=9, ratio=0.2, radius=1), INVALID, "max_sel"),
+    (dict(mode=1, T=1174, ss=1007, st=167, max_sel=10, ratio=0.2, radius=1,
+          ws_bytes=2 * 128 * 16 * 12 - 1), WORKSPACE, "workspace"),
 ]
 
 
@@ -137,6 +163,8 @@ FWD_CASES = [
     (dict(idx=None), INVALID, "block_idx"),
     (dict(max_sel=0), INVALID, "max_sel"),
     (dict(ss=2000), INVALID, "sink_start"),
+    (dict(mode=3), INVALID, "video_tail_mode"),
+    (dict(mode=1, T=930, ss=900, st=30), INVALID, "pad mode needs"),
 ]
 
 
@@ -155,6 +183,8 @@ DENSE_CASES = [
     (dict(ws=None, ws_bytes=1024), WORKSPACE, "workspace"),
     (dict(ws=ctypes.c_void_p((1 << 20) + 4), ws_bytes=1024), WORKSPACE, "workspace"),
     (dict(T=1 << 24, ss=(1 << 24) - 64, st=64, H=128), UNSUPPORTED, "2 GiB"),
+    (dict(mode=7), INVALID, "video_tail_mode"),
+    (dict(mode=1, T=100, ss=70, st=30), INVALID, "pad mode needs"),
 ]
 
 
@@ -169,6 +199,7 @@ def test_nothing_to_do_is_ok(L):
     assert _route(L, T=1000, ss=10, st=990, max_sel=16, idx=None, cnt=None, ws=None, ws_bytes=0) == 0
     assert _fwd(L, T=1000, ss=10, st=990, idx=None, cnt=None) == 0
     assert _dense(L, T=1024, ss=1024, st=0) == 0
+    assert _dense(L, T=1024, ss=1024, st=0, mode=1) == 0
     assert L.sa_last_error().decode() == ""
 
 

@@ -17,13 +17,13 @@ pytestmark = pytest.mark.gpu
 
 def _check_route(res, rt, wl):
     B, T, H, _ = wl.q.shape
-    nvb = rt.nvb
-    if nvb == 0:
+    nvb, nvq = rt.nvb, rt.nvq
+    if nvq == 0:
         return
     rows, mism, ties, unexp = compare_lists(res["idx"], res["cnt"], rt)
     log(f"[{wl.name}] lists: rows={rows} mismatched={mism} near_ties={ties} unexplained={unexp}")
     assert unexp == 0
-    if res["scores"] is not None:
+    if res["scores"] is not None and nvb > 0:
         g = res["scores"].numpy()
         # fp32 of an fp64 dot product on both sides: equal except where the two
         # fp64 sums straddle an fp32 rounding boundary (1 ulp)
@@ -37,7 +37,7 @@ def _check_route(res, rt, wl):
     nb = rt.nb
     for b in range(B):
         for h in range(H):
-            for i in range(nvb):
+            for i in range(nvq):
                 s = set(idx[b, h, i, :cnt[b, h, i]].tolist())
                 assert set(ora.forced_blocks(i, nvb, wl.local_radius)) <= s
                 assert set(range(nvb, nb)) <= s
@@ -60,7 +60,7 @@ def _full_parity(wl, key_bias=None):
     log(f"[{wl.name}] GPU run")
     res = run_gpu(wl, key_bias=kb)
     log(f"[{wl.name}] oracle run")
-    rt = ora.route(q, k, wl.sink_start, wl.topk_ratio, wl.local_radius)
+    rt = ora.route(q, k, wl.sink_start, wl.topk_ratio, wl.local_radius, tail_mode=wl.tail_mode)
     _check_route(res, rt, wl)
     _adopt_gpu_lists(res, rt)
     want, want_lse, _ = ora.routed_attention(q, k, v, wl.sink_start, wl.topk_ratio,
@@ -98,6 +98,85 @@ def test_split_video_block_and_bias():
     wl = workloads.Workload("split_block", q, k, v, sink_start=tv2, topk_ratio=0.2, local_radius=1,
                             key_bias=bias)
     _full_parity(wl)
+
+
+# ---- pad video tail mode ---------------------------------------------------
+
+def _split_workload(mode, name="split_block"):
+    q, k, v, tv = workloads.video_qkv(B=1, H=3, frames=2, ctx_tokens=150, seed=7, height=16, width=32)
+    tv2 = tv - 17                          # 1024 - 17: boundary splits block 15
+    bias = workloads.sink_key_bias(1, q.shape[1], tv2, seed=8)
+    return workloads.Workload(f"{name}_{mode}", q, k, v, sink_start=tv2, topk_ratio=0.2,
+                              local_radius=1, key_bias=bias, tail_mode=mode)
+
+
+def test_pad_split_video_block_and_bias():
+    # block 15 (47 real video rows) is routed and sparse, context rows dense
+    res, rt = _full_parity(_split_workload("pad"))
+    assert rt.nvq == rt.nvb + 1 and res["cnt"].shape[2] == rt.nvq
+
+
+def test_pad_h3_shape_split_tail():
+    # H3 sequence with the video boundary 17 rows before a block edge
+    q, k, v, tv = workloads.video_qkv(B=1, H=4, frames=9, ctx_tokens=289, seed=13)
+    bias = workloads.sink_key_bias(1, q.shape[1], tv - 17, seed=14)
+    wl = workloads.Workload("h3_H4_pad", q, k, v, sink_start=tv - 17, topk_ratio=0.1,
+                            local_radius=1, key_bias=bias, tail_mode="pad")
+    _full_parity(wl)
+
+
+def test_pad_without_complete_video_block():
+    # NVB = 0: the split block 0 is the only query block; its list is every block
+    q, k, v = workloads.random_qkv(1, 700, 2, seed=15)
+    wl = workloads.Workload("pad_nvb0", q, k, v, sink_start=40, topk_ratio=0.1, local_radius=1,
+                            tail_mode="pad")
+    res, rt = _full_parity(wl)
+    assert res["cnt"].flatten().tolist() == [11, 11]
+
+
+def test_pad_and_dense_modes_share_bits_where_they_must():
+    """Complete video blocks and context rows are the same computation in
+    both modes (same lists, same kernels, same key splits): equal bits.  With
+    a block-aligned boundary the whole call is equal."""
+    a = run_gpu(_split_workload("dense"))
+    b = run_gpu(_split_workload("pad"))
+    ss = 1024 - 17
+    assert torch.equal(a["idx"], b["idx"][:, :, :-1]) and torch.equal(a["cnt"], b["cnt"][:, :, :-1])
+    assert torch.equal(a["out"][:, :960], b["out"][:, :960])
+    assert torch.equal(a["out"][:, ss:], b["out"][:, ss:])
+    assert torch.equal(a["lse"][:, :, ss:], b["lse"][:, :, ss:])
+    assert not torch.equal(a["out"][:, 960:ss], b["out"][:, 960:ss])
+    wl = workloads.mid()
+    c = run_gpu(wl)
+    wl.tail_mode = "pad"
+    d = run_gpu(wl)
+    for key in ("out", "lse", "idx", "cnt", "scores"):
+        assert torch.equal(c[key], d[key]), key
+
+
+def test_pad_pooled_tail_mean_bit_exact():
+    import block_sparse_attention_05_amd as sa
+    wl = _split_workload("pad")
+    q, k = wl.q.cuda(), wl.k.cuda()
+    B, T, H, _ = q.shape
+    ss = wl.sink_start
+    nvb, nvq = ss // 64, ss // 64 + 1
+    ws = torch.zeros(sa.sa_route_workspace_bytes(B, T, H, ss, "pad"), dtype=torch.uint8, device="cuda")
+    sa.sparse_attn_route(q, k, ss, 0.2, 1, video_tail_mode="pad", workspace=ws)
+    torch.cuda.synchronize()
+    ntq, ntk = -(-nvq // 16), -(-nvb // 16)
+    nq, nk = B * H * ntq * 16 * 128, B * H * ntk * 16 * 128
+    raw = ws.cpu()
+    qt = raw[: 8 * nq].view(torch.float64).numpy().reshape(B, H, ntq, 16, 64, 2)
+    kt = raw[8 * nq: 8 * nq + 4 * nk].view(torch.float32).numpy().reshape(B, H, ntk, 8, 64, 4)
+    d = np.arange(128)[None, :]
+    iq = np.arange(nvq)[:, None]
+    ik = np.arange(nvb)[:, None]
+    qm = qt[:, :, iq // 16, (d % 32) // 2, 16 * (d // 32) + iq % 16, d % 2]
+    km = kt[:, :, ik // 16, (d % 32) // 4, 16 * (d // 32) + ik % 16, d % 4]
+    qo = ora.pool_means(to_np(wl.q), nvq, end=ss)
+    assert np.array_equal(qm.astype(np.float32).view(np.uint32), qo.view(np.uint32))
+    assert np.array_equal(km.view(np.uint32), ora.pool_means(to_np(wl.k), nvb).view(np.uint32))
 
 
 def _tied_keys(nvb, copies, seed):

@@ -46,6 +46,7 @@ class Workload:
     topk_ratio: float
     local_radius: int
     key_bias: Optional[torch.Tensor] = None   # float32 [B, T] natural log, CPU
+    tail_mode: str = "dense"   # video tail mode: "dense" or "pad"
 
     @property
     def shape(self):
