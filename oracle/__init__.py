@@ -7,7 +7,10 @@ binding, and it imports neither.
 
 Every function follows the pages it cites step by step, in plain NumPy
 (float64 unless the pages fix fp32), with no blocking, fusion or reordering
-beyond what the definitions state.  Parity status of each function is listed
-in the module docstring of :mod:`oracle.sparse_attention`.
+beyond what the definitions state.  :mod:`oracle.sparse_attention` holds the
+routed attention path (pooling, route scores, Top-K, exact and dense
+attention, the video tail modes); :mod:`oracle.spark_summaries` holds the
+Spark virtual summaries and the approximate branch for skipped blocks.  Each
+module docstring lists what pins its functions.
 """
 

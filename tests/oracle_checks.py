@@ -17,6 +17,7 @@ import torch
 import torch.nn.functional as F
 
 import oracle.sparse_attention as ra
+import oracle.spark_summaries as sp
 import workloads
 from _exact import exact_block_means, exact_scores
 
@@ -475,6 +476,149 @@ def check_pad_effective_flops():
     assert ra.effective_flops(T, 1, 1, lists, nvb, sparse_end=ss) == want
 
 
+# ------------------------------------------------ Spark virtual summaries ---
+# Page "Sol-Attn and Spark for MiniMax-H3", Spark primitives (spark_reweight)
+# and Spark inference integration (global anchor, summaries merged with exact
+# attention).
+
+def _bf16(x):
+    return torch.from_numpy(np.asarray(x, np.float32)).to(torch.bfloat16).float().numpy()
+
+
+def check_anchor_exact():
+    """The anchor is the exact mean of the video query rows, rounded to fp32
+    then bf16; context rows do not count."""
+    from fractions import Fraction
+    from _exact import round_fraction_to_f32
+    q = _np(_varied_bf16((1, 200, 2, 128), seed=61))
+    got = sp.global_anchor(q, 150)
+    assert got.shape == (1, 1, 2, 128)
+    want = np.zeros((1, 1, 2, 128), np.float32)
+    for h in range(2):
+        for d in range(128):
+            m = sum(Fraction(float(q[0, t, h, d])) for t in range(150)) / 150
+            want[0, 0, h, d] = round_fraction_to_f32(m)
+    assert np.array_equal(_bits(got), _bits(_bf16(want)))
+
+
+def check_summaries_explicit_softmax():
+    """ak, av, lm against torch.softmax / logsumexp over each block's keys,
+    a partial final block included (its missing keys do not count)."""
+    T, H, P = 200, 2, 2                                  # blocks of 64, 64, 64, 8
+    _, k, v = (_np(x) for x in workloads.random_qkv(1, T, H, seed=62))
+    a = _np(_varied_bf16((1, P, H, 128), seed=63))
+    ak, av, lm = sp.virtual_summaries(a, k, v, logmass_key="pre_round", store="f64")
+    akr, avr, lmr = sp.virtual_summaries(a, k, v)        # stored bf16, stored-key log-mass
+    assert ak.shape == (1, P, H, 4, 128) and lm.shape == (1, P, H, 4)
+    s = 1.0 / math.sqrt(128)
+    for p in range(P):
+        for h in range(H):
+            for j in range(4):
+                kt = torch.from_numpy(k[0, 64 * j:min(T, 64 * j + 64), h].astype(np.float64))
+                vt = torch.from_numpy(v[0, 64 * j:min(T, 64 * j + 64), h].astype(np.float64))
+                at = torch.from_numpy(a[0, p, h].astype(np.float64))
+                z = (kt @ at) * s
+                w = torch.softmax(z, dim=0)
+                wk, wv = (w @ kt).numpy(), (w @ vt).numpy()
+                assert np.abs(ak[0, p, h, j] - wk).max() < 1e-12
+                assert np.abs(av[0, p, h, j] - wv).max() < 1e-12
+                lse = float(torch.logsumexp(z, dim=0))
+                assert abs(lm[0, p, h, j] - (lse - s * float(at @ torch.from_numpy(wk)))) < 1e-10
+                # stored: bf16 of the weighted key/value, log-mass shifted by the stored key
+                assert np.array_equal(_bits(akr[0, p, h, j]), _bits(_bf16(wk)))
+                assert np.array_equal(_bits(avr[0, p, h, j]), _bits(_bf16(wv)))
+                shift = s * float(at @ torch.from_numpy(_bf16(wk).astype(np.float64)))
+                assert abs(lmr[0, p, h, j] - (lse - shift)) < 1e-10
+
+
+def check_log_mass_closed_forms():
+    """A block of n identical keys: ak is that key and lm = ln n (64 for a
+    full block, 8 for the partial final block of T = 200)."""
+    T, H = 200, 1
+    _, k, v = (_np(x) for x in workloads.random_qkv(1, T, H, seed=64))
+    for j in range(4):
+        k[0, 64 * j:min(T, 64 * j + 64)] = k[0, 64 * j]
+    a = _np(_varied_bf16((1, 1, H, 128), seed=65))
+    ak, _, lm = sp.virtual_summaries(a, k, v)
+    for j, n in enumerate((64, 64, 64, 8)):
+        assert np.array_equal(ak[0, 0, 0, j], k[0, 64 * j, 0].astype(np.float64))
+        assert abs(lm[0, 0, 0, j] - math.log(n)) < 1e-9
+
+
+def _anchor_rows_case(seed):
+    """Q whose query block 2 rows all equal the anchor, plus unrounded
+    summaries shifted by the unrounded key."""
+    T, H, ss = 600, 2, 512                               # NVB = 8, sinks 8, 9 (last partial)
+    q, k, v = (_np(x) for x in workloads.random_qkv(1, T, H, seed=seed))
+    a = sp.global_anchor(q, ss)
+    q[0, 128:192] = a[0, 0][None]
+    summ = sp.virtual_summaries(a, k, v, logmass_key="pre_round", store="f64")
+    return q, k, v, ss, summ
+
+
+def check_spark_anchor_rows_are_exact():
+    """For a query row equal to the anchor, every skipped block's virtual key
+    carries that block's exact softmax mass and weighted value, so the row
+    equals full attention over all keys (with the sink bias)."""
+    q, k, v, ss, summ = _anchor_rows_case(66)
+    bias = workloads.sink_key_bias(1, 600, ss, seed=67).numpy()
+    out, lse, rt = sp.routed_attention_spark(q, k, v, ss, 0.25, 1, summ, key_bias=bias)
+    assert len(rt.rows[0][0][2].blocks) < rt.nb             # some blocks are skipped
+    want = _sdpa(q, k, v, mask=_sink_bias_mask(600, 8, bias)[None, None])
+    assert np.abs(out[0, 128:192] - want[0, 128:192]).max() < 1e-10
+    qt = torch.from_numpy(q.astype(np.float64))
+    kt = torch.from_numpy(k.astype(np.float64))
+    logits = torch.einsum("bthd,bshd->bhts", qt, kt) / math.sqrt(128) + torch.from_numpy(_sink_bias_mask(600, 8, bias))
+    assert np.abs(lse[0, :, 128:192] - torch.logsumexp(logits, dim=-1).numpy()[0, :, 128:192]).max() < 1e-10
+    # and the other rows do differ from full attention
+    assert np.abs(out[0, :128] - want[0, :128]).max() > 1e-4
+
+
+def check_spark_ratio_one_is_exact():
+    """Ratio 1 leaves no block skipped: the approximate branch adds nothing."""
+    q, k, v, ss = _case(600, 2, 68, 512)
+    a = sp.global_anchor(q, ss)
+    summ = sp.virtual_summaries(a, k, v)
+    o1, l1, _ = sp.routed_attention_spark(q, k, v, ss, 1.0, 0, summ)
+    o2, l2, _ = ra.routed_attention(q, k, v, ss, 1.0, 0)
+    assert np.abs(o1 - o2).max() < 1e-12 and np.abs(l1 - l2).max() < 1e-12
+
+
+def check_spark_token_mask_path():
+    """Against one dense formulation: every row sees all T keys plus NVB
+    virtual keys; a mask keeps, for sparse rows, the keys of its exact
+    blocks and the virtual keys of its skipped blocks (with bias lm), and
+    for dense rows the real keys only."""
+    T, ss, H = 1000, 900, 2                              # NVB = 14, split tail (pad mode)
+    q, k, v, _ = _case(T, H, 69, ss)
+    bias = workloads.sink_key_bias(1, T, ss, seed=70).numpy()
+    a = sp.global_anchor(q, ss)
+    ak, av, lm = sp.virtual_summaries(a, k, v)
+    out, _, rt = sp.routed_attention_spark(q, k, v, ss, 0.25, 1, (ak, av, lm), key_bias=bias,
+                                           tail_mode="pad")
+    nvb = 14
+    k2 = np.concatenate([k, np.transpose(ak[:, 0, :, :nvb], (0, 2, 1, 3))], axis=1)
+    v2 = np.concatenate([v, np.transpose(av[:, 0, :, :nvb], (0, 2, 1, 3))], axis=1)
+    mask = np.full((H, T, T + nvb), -np.inf)
+    for h in range(H):
+        for t in range(T):
+            if t < ss:
+                blocks = rt.rows[0][h][t // 64].blocks
+                for j in blocks:
+                    mask[h, t, j * 64:min(T, j * 64 + 64)] = 0.0
+                for j in range(nvb):
+                    if j not in blocks:
+                        mask[h, t, T + j] = lm[0, 0, h, j]
+            else:
+                mask[h, t, :T] = 0.0
+    sb = np.zeros(T + nvb)
+    sb[:T] = bias[0]
+    sb[: nvb * 64] = 0.0
+    mask = mask + sb[None, None, :]
+    want = _sdpa(q, k2, v2, mask=mask[None])
+    assert np.abs(out - want).max() < 1e-12
+
+
 ALL_CHECKS = [
     check_pool_exact, check_pool_permutation_invariant, check_scores_exact,
     check_budget, check_topk_bruteforce, check_signed_zero_tie, check_near_tie_flag,
@@ -486,4 +630,6 @@ ALL_CHECKS = [
     check_pad_tail_means_exact, check_pad_centroid_preserved, check_pad_route_and_mask,
     check_pad_modes_agree_where_they_must, check_pad_ratio_one_and_no_complete_block,
     check_pad_needs_context_slots, check_pad_effective_flops,
+    check_anchor_exact, check_summaries_explicit_softmax, check_log_mass_closed_forms,
+    check_spark_anchor_rows_are_exact, check_spark_ratio_one_is_exact, check_spark_token_mask_path,
 ]

@@ -7,6 +7,7 @@ import numpy as np
 import pytest
 
 import oracle.sparse_attention as ra
+import oracle.spark_summaries as sp
 import oracle_checks as oc
 
 _orig = {name: getattr(ra, name) for name in (
@@ -151,6 +152,85 @@ def sparse_end_whole_block(T, sink_start, tail_mode="dense"):
     return -(-_orig["sparse_rows_end"](T, sink_start, tail_mode) // 64) * 64
 
 
+_sp_orig = {name: getattr(sp, name) for name in (
+    "virtual_summaries", "approx_block_output", "global_anchor", "log_mass")}
+
+
+def log_mass_sign(a, keys, key_for_shift, scale):           # + instead of -
+    z = _sp_orig["log_mass"](a, keys, key_for_shift, scale)
+    return z + 2 * scale * float(np.dot(np.asarray(a, np.float64), np.asarray(key_for_shift, np.float64)))
+
+
+def log_mass_unscaled_shift(a, keys, key_for_shift, scale):
+    z = _sp_orig["log_mass"](a, keys, key_for_shift, scale)
+    return z + (scale - 1.0) * float(np.dot(np.asarray(a, np.float64), np.asarray(key_for_shift, np.float64)))
+
+
+def summaries_uniform(a, k, v, scale=None, logmass_key="stored", store="bf16"):
+    """Plain block means with ln(n) mass: the summary without reweighting."""
+    ak, av, lm = _sp_orig["virtual_summaries"](a, k, v, scale, logmass_key, store)
+    T = k.shape[1]
+    for j in range(ak.shape[3]):
+        kk = np.asarray(k, np.float64)[:, 64 * j:min(T, 64 * j + 64)].mean(1)   # [B, H, D]
+        vv = np.asarray(v, np.float64)[:, 64 * j:min(T, 64 * j + 64)].mean(1)
+        ak[:, :, :, j] = kk[:, None]
+        av[:, :, :, j] = vv[:, None]
+        lm[:, :, :, j] = math.log(min(T, 64 * j + 64) - 64 * j)
+    return ak, av, lm
+
+
+def summaries_zero_padded(a, k, v, scale=None, logmass_key="stored", store="bf16"):
+    """The partial final block padded with zero keys and values."""
+    T = k.shape[1]
+    pad = (-T) % 64
+    z = np.zeros((k.shape[0], pad) + k.shape[2:], np.float32)
+    return _sp_orig["virtual_summaries"](a, np.concatenate([k, z], 1), np.concatenate([v, z], 1),
+                                         scale, logmass_key, store)
+
+
+def approx_every_block_virtual(q, k, v, b, h, i, blocks, ak, av, lm, key_bias=None, nvb=0,
+                               scale=None, qrows=None):
+    """Exact blocks summarised too (their mass counted twice)."""
+    T = q.shape[1]
+    idx = np.concatenate([np.arange(j * 64, min(j * 64 + 64, T)) for j in blocks])
+    kb = ra.key_bias_vector(key_bias, b, T, nvb)
+    keys = np.concatenate([k[b, idx, h], ak[b, 0, h, :nvb]])
+    vals = np.concatenate([v[b, idx, h], av[b, 0, h, :nvb]])
+    bias = np.concatenate([np.zeros(len(idx)) if kb is None else kb[idx], lm[b, 0, h, :nvb]])
+    if qrows is None:
+        qrows = q[b, i * 64:min(i * 64 + 64, T), h]
+    return ra.attend(qrows, keys, vals, bias, 1.0 / math.sqrt(128) if not scale else scale)
+
+
+def approx_sinks_virtual(q, k, v, b, h, i, blocks, ak, av, lm, key_bias=None, nvb=0, scale=None,
+                         qrows=None):
+    """Sink blocks summarised instead of exact."""
+    nb = -(-q.shape[1] // 64)
+    kept = [j for j in blocks if j < nvb]
+    return _sp_orig["approx_block_output"](q, k, v, b, h, i, kept, ak, av, lm, key_bias, nb, scale,
+                                           qrows)
+
+
+def approx_no_logmass(q, k, v, b, h, i, blocks, ak, av, lm, key_bias=None, nvb=0, scale=None,
+                      qrows=None):
+    return _sp_orig["approx_block_output"](q, k, v, b, h, i, blocks, ak, av, np.zeros_like(lm),
+                                           key_bias, nvb, scale, qrows)
+
+
+def approx_keys_as_values(q, k, v, b, h, i, blocks, ak, av, lm, key_bias=None, nvb=0, scale=None,
+                          qrows=None):
+    return _sp_orig["approx_block_output"](q, k, v, b, h, i, blocks, ak, ak, lm, key_bias, nvb,
+                                           scale, qrows)
+
+
+def anchor_all_rows(q, sink_start):                 # context query rows averaged in
+    return _sp_orig["global_anchor"](q, q.shape[1])
+
+
+def anchor_block_rows(q, sink_start):               # complete video blocks only
+    return _sp_orig["global_anchor"](q, sink_start // 64 * 64)
+
+
 # (oracle function, mutant, the pin expected to catch it)
 MUTANTS = [
     ("pool_means", pool_63, oc.check_pool_exact),
@@ -182,11 +262,37 @@ MUTANTS = [
     ("forced_blocks", forced_one_sided, oc.check_pad_route_and_mask),
 ]
 
+SP_MUTANTS = [
+    ("log_mass", log_mass_sign, oc.check_summaries_explicit_softmax),
+    ("log_mass", log_mass_unscaled_shift, oc.check_summaries_explicit_softmax),
+    ("log_mass", log_mass_unscaled_shift, oc.check_spark_anchor_rows_are_exact),
+    ("virtual_summaries", summaries_uniform, oc.check_summaries_explicit_softmax),
+    ("virtual_summaries", summaries_uniform, oc.check_spark_anchor_rows_are_exact),
+    ("virtual_summaries", summaries_zero_padded, oc.check_log_mass_closed_forms),
+    ("virtual_summaries", summaries_zero_padded, oc.check_summaries_explicit_softmax),
+    ("approx_block_output", approx_every_block_virtual, oc.check_spark_anchor_rows_are_exact),
+    ("approx_block_output", approx_every_block_virtual, oc.check_spark_ratio_one_is_exact),
+    ("approx_block_output", approx_sinks_virtual, oc.check_spark_anchor_rows_are_exact),
+    ("approx_block_output", approx_no_logmass, oc.check_spark_anchor_rows_are_exact),
+    ("approx_block_output", approx_keys_as_values, oc.check_spark_anchor_rows_are_exact),
+    ("global_anchor", anchor_all_rows, oc.check_anchor_exact),
+    ("global_anchor", anchor_block_rows, oc.check_anchor_exact),
+]
+
 
 @pytest.mark.parametrize("name,mutant,check", MUTANTS,
                          ids=[f"{m.__name__}-{c.__name__}" for _, m, c in MUTANTS])
 def test_mutant_is_caught(monkeypatch, name, mutant, check):
     check()                                   # passes on the oracle as written
     monkeypatch.setattr(ra, name, mutant)
+    with pytest.raises((AssertionError, ValueError, IndexError)):
+        check()
+
+
+@pytest.mark.parametrize("name,mutant,check", SP_MUTANTS,
+                         ids=[f"{m.__name__}-{c.__name__}" for _, m, c in SP_MUTANTS])
+def test_summary_mutant_is_caught(monkeypatch, name, mutant, check):
+    check()
+    monkeypatch.setattr(sp, name, mutant)
     with pytest.raises((AssertionError, ValueError, IndexError)):
         check()
