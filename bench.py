@@ -17,6 +17,12 @@ on one stream with events between them: the per-stage times, the
 attention-only rate and the sparse kernel's roofline come from that pass,
 so each kernel is timed alone.
 
+A third measurement (``spark`` in the JSON line, skipped by ``--no-spark``)
+times the Spark variant of the same call on the same inputs: global anchor,
+virtual summaries, route, sparse rows with one virtual key per skipped video
+block, dense rows, back to back on one stream with events between the
+stages.  It does not change the headline numbers.
+
 Prints one JSON line.  ``--gpus`` above 1 is refused: this path runs on one
 GPU (a multi-GPU run would shard heads, see the design notes).
 """
@@ -55,6 +61,71 @@ def effective_flops_from_lists(cnt, idx, T, nvb, H, B):
                 sparse_pairs += 64 * int(keys_in_block[idx[b, h, i, :cnt[b, h, i]]].sum())
     dense_pairs = B * H * (T - 64 * nvb) * T
     return 4 * 128 * sparse_pairs, 4 * 128 * dense_pairs
+
+
+def spark_measure(sa, wl, q, k, v, kb, idx, cnt, ws, out, dws, steps, sparse_flops, dense_flops):
+    """Per-stage and whole-call times of the Spark path (one stream)."""
+    B, T, H, D = q.shape
+    ss = wl.sink_start
+    nb = -(-T // 64)
+    nvb = ss // 64
+    anchor = sa.spark_global_anchor(q, ss)
+    aws = torch.empty(max(16, sa.sa_anchor_workspace_bytes(B, T, H, ss)), dtype=torch.uint8, device=q.device)
+    ak, av, lm = sa.spark_reweight(anchor, k, v)
+    stream = torch.cuda.current_stream(q.device)
+    stages = [
+        ("anchor", lambda: sa.spark_global_anchor(q, ss, out=anchor, workspace=aws)),
+        ("reweight", lambda: sa.spark_reweight(anchor, k, v, ak=ak, av=av, lm=lm)),
+        ("route", lambda: sa.sparse_attn_route(q, k, ss, wl.topk_ratio, wl.local_radius, block_idx=idx,
+                                               block_cnt=cnt, workspace=ws)),
+        ("sparse_fwd_spark", lambda: sa.sparse_attn_fwd_spark(q, k, v, ss, idx, cnt, (ak, av, lm),
+                                                              key_bias=kb, out=out)),
+        ("dense_fwd", lambda: sa.dense_sink_fwd(q, k, v, ss, key_bias=kb, out=out, workspace=dws)),
+    ]
+    for _ in range(3):
+        for _, fn in stages:
+            fn()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(steps)]
+    for i in range(steps):
+        evs[i][0].record(stream)
+        for j, (_, fn) in enumerate(stages):
+            fn()
+            evs[i][j + 1].record(stream)
+    torch.cuda.synchronize()
+    st = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(len(stages))] for e in evs])
+    call = np.array([e[0].elapsed_time(e[-1]) for e in evs])
+    med = np.median(st, axis=0)
+    mean = st.mean(axis=0)
+    names = [n for n, _ in stages]
+    # algorithmic HBM bytes of the summaries kernel: K and V read once, the
+    # anchor read, ak / av / lm written
+    rw_bytes = 2 * B * T * H * D * 2 + B * H * D * 2 + 2 * B * H * nb * D * 2 + B * H * nb * 4
+    rw_ms = float(mean[names.index("reweight")])
+    rw_gbps = rw_bytes / (rw_ms * 1e-3) / 1e9
+    an_bytes = B * ss * H * D * 2
+    an_gbps = an_bytes / (float(mean[names.index("anchor")]) * 1e-3) / 1e9
+    # virtual (row, summary key) pairs: every sparse row times its skipped video blocks
+    c = cnt.cpu().numpy()
+    i_ = idx.cpu().numpy()
+    exact_video = np.array([[[int((i_[b, h, r, :c[b, h, r]] < nvb).sum()) for r in range(i_.shape[2])]
+                             for h in range(H)] for b in range(B)])
+    virtual_pairs = int(64 * (nvb - exact_video).sum())
+    sp_ms = float(mean[names.index("sparse_fwd_spark")])
+    sp_flops = sparse_flops + 4 * D * virtual_pairs
+    return {
+        "path": "global anchor + virtual summaries + route + sparse rows with one virtual key per "
+                "skipped video block + dense rows, one stream",
+        "ms_per_call_median": round(float(np.median(call)), 4),
+        "stages_ms_median": {n: round(float(x), 4) for n, x in zip(names, med)},
+        "effective_gflop_exact": round((sparse_flops + dense_flops) / 1e9, 3),
+        "virtual_pairs": virtual_pairs,
+        "sparse_fwd_spark_tflops": round(sp_flops / (sp_ms * 1e-3) / 1e12, 3),
+        "reweight_roofline": {"kernel": "reweight_kernel", "bound": "hbm", "achieved": round(rw_gbps, 1),
+                              "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(rw_gbps / HBM_PEAK_GBPS, 4),
+                              "algorithmic_bytes_per_launch": rw_bytes, "launch_ms_mean": round(rw_ms, 4)},
+        "anchor_gbps": round(an_gbps, 1),
+    }
 
 
 def traffic_for_current_kernel():
@@ -102,6 +173,8 @@ def main():
     ap.add_argument("--workload", default="h3", choices=["h3", "h3_bias", "mid", "long", "tiny"])
     ap.add_argument("--cpu-heads", type=int, default=56)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-spark", action="store_true",
+                    help="skip the Spark approximate-branch measurement")
     ap.add_argument("--one-stream", action="store_true",
                     help="run the dense rows after the sparse rows on one stream")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -244,6 +317,9 @@ def main():
                      "launch_ms_mean": round(sparse_ms, 4),
                      "traffic": traffic_for_current_kernel()},
     }
+    if not args.no_spark:
+        res["spark"] = spark_measure(sa, wl, q, k, v, kb, idx, cnt, ws, out, dws, args.steps,
+                                     sparse_flops, dense_flops)
     if not args.no_cpu_baseline:
         cb = cpu_baseline(wl, args.cpu_heads)
         cb.pop("seconds")

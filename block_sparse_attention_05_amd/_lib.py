@@ -46,6 +46,15 @@ SIGNATURES = {
     "dense_sink_fwd": (ctypes.c_int, [
         _vp, _vp, _vp, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32,
         _vp, _c_int64, _c_float, _vp, _vp, _vp, _c_size, _vp]),
+    "sa_anchor_workspace_bytes": (_c_size, [_c_int32, _c_int32, _c_int32, _c_int32]),
+    "spark_global_anchor": (ctypes.c_int, [
+        _vp, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32, _vp, _vp, _c_size, _vp]),
+    "spark_reweight": (ctypes.c_int, [
+        _vp, _vp, _vp, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32, _c_float, _c_int32,
+        _vp, _vp, _vp, _vp]),
+    "sparse_attn_fwd_spark": (ctypes.c_int, [
+        _vp, _vp, _vp, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32,
+        _vp, _c_int64, _vp, _vp, _c_int32, _vp, _vp, _vp, _c_float, _vp, _vp, _vp]),
 }
 
 
@@ -308,4 +317,132 @@ def routed_attention(q, k, v, sink_start: int, topk_ratio: float = 0.1, local_ra
         res.append(lse)
     if return_route:
         res.append((block_idx, block_cnt))
+    return res[0] if len(res) == 1 else tuple(res)
+
+
+# ---- Spark virtual summaries and the approximate branch --------------------
+
+LOGMASS_KEYS = {"stored": 0, "pre_round": 1}
+
+
+def sa_anchor_workspace_bytes(B: int, T: int, H: int, sink_start: int) -> int:
+    return lib().sa_anchor_workspace_bytes(B, T, H, sink_start)
+
+
+def spark_global_anchor(q: torch.Tensor, sink_start: int, *, out: Optional[torch.Tensor] = None,
+                        workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """bf16 [B, 1, H, 128]: the mean of the video query rows [0, sink_start)
+    of every (batch, head)."""
+    _check_qkv(q)
+    B, T, H, D = q.shape
+    if out is None:
+        out = torch.empty((B, 1, H, D), dtype=torch.bfloat16, device=q.device)
+    if out.dtype != torch.bfloat16 or not out.is_contiguous() or out.numel() != B * H * D \
+            or out.device != q.device:
+        raise ValueError("out must be contiguous bfloat16 [B, 1, H, 128] on the device of q")
+    n = lib().sa_anchor_workspace_bytes(B, T, H, sink_start)
+    if workspace is None:
+        workspace = torch.empty(max(n, 16), dtype=torch.uint8, device=q.device)
+    _check(lib().spark_global_anchor(
+        _ptr(q), B, T, H, D, sink_start, T - sink_start, _ptr(out), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(q.device)))
+    return out
+
+
+def spark_reweight(a: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, softmax_scale: float = 0.0,
+                   logmass_key: str = "stored", ak: Optional[torch.Tensor] = None,
+                   av: Optional[torch.Tensor] = None, lm: Optional[torch.Tensor] = None):
+    """Virtual summaries for anchors a [B, P, H, 128]: returns (ak, av bf16
+    [B, P, H, NB, 128], lm fp32 [B, P, H, NB])."""
+    _check_qkv(k, v)
+    B, T, H, D = k.shape
+    if a.dtype != torch.bfloat16 or a.dim() != 4 or a.shape[0] != B or a.shape[2] != H \
+            or a.shape[3] != D or not a.is_contiguous() or a.device != k.device:
+        raise ValueError("a must be contiguous bfloat16 [B, P, H, 128] on the device of k")
+    if logmass_key not in LOGMASS_KEYS:
+        raise ValueError(f"logmass_key must be one of {sorted(LOGMASS_KEYS)}")
+    P = a.shape[1]
+    nb = -(-T // BLOCK)
+    dev = k.device
+    if ak is None:
+        ak = torch.empty((B, P, H, nb, D), dtype=torch.bfloat16, device=dev)
+    if av is None:
+        av = torch.empty((B, P, H, nb, D), dtype=torch.bfloat16, device=dev)
+    if lm is None:
+        lm = torch.empty((B, P, H, nb), dtype=torch.float32, device=dev)
+    for name, t, dt, numel in (("ak", ak, torch.bfloat16, B * P * H * nb * D),
+                               ("av", av, torch.bfloat16, B * P * H * nb * D),
+                               ("lm", lm, torch.float32, B * P * H * nb)):
+        if t.dtype != dt or not t.is_contiguous() or t.numel() != numel or t.device != dev:
+            raise ValueError(f"{name} must be a contiguous {dt} tensor of {numel} elements on {dev}")
+    _check(lib().spark_reweight(
+        _ptr(a), _ptr(k), _ptr(v), B, P, T, H, D, float(softmax_scale), LOGMASS_KEYS[logmass_key],
+        _ptr(ak), _ptr(av), _ptr(lm), _stream(dev)))
+    return ak, av, lm
+
+
+def sparse_attn_fwd_spark(q, k, v, sink_start: int, block_idx: torch.Tensor, block_cnt: torch.Tensor,
+                          summaries, *, video_tail_mode: str = "dense",
+                          key_bias: Optional[torch.Tensor] = None, softmax_scale: float = 0.0,
+                          out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
+    """sparse_attn_fwd plus one virtual key per skipped video block, from
+    ``summaries`` = (ak, av, lm) of one anchor per (batch, head)."""
+    _check_qkv(q, k, v)
+    B, T, H, D = q.shape
+    ak, av, lm = summaries
+    nb = -(-T // BLOCK)
+    for name, t, dt, numel in (("ak", ak, torch.bfloat16, B * H * nb * D),
+                               ("av", av, torch.bfloat16, B * H * nb * D),
+                               ("lm", lm, torch.float32, B * H * nb)):
+        if t.dtype != dt or not t.is_contiguous() or t.numel() != numel or t.device != q.device:
+            raise ValueError(f"{name} must be a contiguous {dt} tensor of one anchor "
+                             f"({numel} elements) on the device of q")
+    if out is None:
+        out = torch.empty_like(q)
+    _check_qkv(q, out)
+    if block_idx.dtype != torch.int32 or block_cnt.dtype != torch.int32 or \
+            not block_idx.is_contiguous() or not block_cnt.is_contiguous():
+        raise ValueError("block_idx / block_cnt must be contiguous int32")
+    mode = _mode(video_tail_mode)
+    nvq = lib().sa_num_query_blocks(T, sink_start, mode)
+    max_sel = block_idx.shape[-1] if block_idx.dim() == 4 else 0
+    if nvq > 0 and (block_idx.dim() != 4 or tuple(block_idx.shape[:3]) != (B, H, nvq)
+                    or block_cnt.numel() != B * H * nvq):
+        raise ValueError("block_idx must be [B,H,NVQ,max_sel] and block_cnt [B,H,NVQ]")
+    if block_idx.device != q.device or block_cnt.device != q.device:
+        raise ValueError("block_idx / block_cnt must be on the device of q")
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != B * H * T):
+        raise ValueError("lse must be contiguous float32 [B,H,T]")
+    kb, kb_n = _bias(key_bias, B, T, q.device)
+    _check(lib().sparse_attn_fwd_spark(
+        _ptr(q), _ptr(k), _ptr(v), B, T, H, D, sink_start, T - sink_start, mode, _ptr(kb), kb_n,
+        _ptr(block_idx), _ptr(block_cnt), int(max_sel), _ptr(ak), _ptr(av), _ptr(lm),
+        float(softmax_scale), _ptr(out), _ptr(lse), _stream(q.device)))
+    return out
+
+
+def routed_attention_spark(q, k, v, sink_start: int, topk_ratio: float = 0.1, local_radius: int = 0, *,
+                           video_tail_mode: str = "dense", key_bias: Optional[torch.Tensor] = None,
+                           softmax_scale: float = 0.0, return_lse: bool = False,
+                           return_parts: bool = False):
+    """One call of the Spark path: global anchor, virtual summaries, route,
+    sparse rows with the approximate branch, dense rows, on the current
+    stream."""
+    anchor = spark_global_anchor(q, sink_start)
+    summaries = spark_reweight(anchor, k, v, softmax_scale=softmax_scale)
+    block_idx, block_cnt = sparse_attn_route(q, k, sink_start, topk_ratio, local_radius,
+                                             video_tail_mode=video_tail_mode)
+    B, T, H, _ = q.shape
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device) if return_lse else None
+    sparse_attn_fwd_spark(q, k, v, sink_start, block_idx, block_cnt, summaries,
+                          video_tail_mode=video_tail_mode, key_bias=key_bias,
+                          softmax_scale=softmax_scale, out=out, lse=lse)
+    dense_sink_fwd(q, k, v, sink_start, video_tail_mode=video_tail_mode, key_bias=key_bias,
+                   softmax_scale=softmax_scale, out=out, lse=lse)
+    res = [out]
+    if return_lse:
+        res.append(lse)
+    if return_parts:
+        res.append(dict(anchor=anchor, summaries=summaries, block_idx=block_idx, block_cnt=block_cnt))
     return res[0] if len(res) == 1 else tuple(res)

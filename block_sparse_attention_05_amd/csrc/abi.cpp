@@ -307,4 +307,117 @@ sa_status dense_sink_fwd(const void *q, const void *k, const void *v, int32_t B,
   return ok();
 }
 
+// ---- Spark summaries and the approximate branch ---------------------------
+
+size_t sa_anchor_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t sink_start) {
+  if (B <= 0 || H <= 0 || sink_start <= 0 || sink_start > T) return 0;
+  return sa::anchor_workspace_bytes(B, H, sink_start);
+}
+
+sa_status spark_global_anchor(const void *q, int32_t B, int32_t T, int32_t H, int32_t D,
+                              int32_t sink_start, int32_t sink_tokens, void *anchor,
+                              void *workspace, size_t workspace_bytes, void *stream) {
+  sa_status st = check_shape(B, T, H, D, sink_start, sink_tokens, SA_VIDEO_TAIL_DENSE);
+  if (st != SA_OK) return st;
+  if (sink_start == 0) return fail(SA_ERR_INVALID_ARG, "the anchor needs sink_start >= 1 video rows");
+  if ((st = check_bf16(q, "q")) != SA_OK) return st;
+  if ((st = check_bf16(anchor, "anchor")) != SA_OK) return st;
+  const size_t need = sa_anchor_workspace_bytes(B, T, H, sink_start);
+  if (workspace_bytes < need)
+    return fail(SA_ERR_WORKSPACE, "workspace must hold %zu bytes (got %zu)", need, workspace_bytes);
+  if (workspace == nullptr || !aligned(workspace, 16))
+    return fail(SA_ERR_WORKSPACE, "workspace must be a 16-byte aligned device pointer");
+  hipError_t e = sa::launch_anchor(q, workspace, anchor, B, T, H, sink_start,
+                                   static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SA_ERR_HIP, "anchor launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+sa_status spark_reweight(const void *anchors, const void *k, const void *v, int32_t B, int32_t P,
+                         int32_t T, int32_t H, int32_t D, float softmax_scale, int32_t logmass_key,
+                         void *ak, void *av, float *lm, void *stream) {
+  sa_status st = check_shape(B, T, H, D, T, 0, SA_VIDEO_TAIL_DENSE);
+  if (st != SA_OK) return st;
+  if (P <= 0) return fail(SA_ERR_INVALID_ARG, "P (anchors) must be positive (got %d)", P);
+  if ((int64_t)B * P * H * ((T + sa::kBlock - 1) / sa::kBlock) > INT32_MAX / 2)
+    return fail(SA_ERR_UNSUPPORTED, "B*P*H*ceil(T/64) too large");
+  if ((int64_t)B * P > 65535) return fail(SA_ERR_UNSUPPORTED, "B*P must stay below 65536 (launch grid)");
+  if (logmass_key != 0 && logmass_key != 1)
+    return fail(SA_ERR_INVALID_ARG, "logmass_key must be 0 (stored bf16 key) or 1 (pre-round key)");
+  if ((st = check_bf16(anchors, "anchors")) != SA_OK) return st;
+  if ((st = check_bf16(k, "k")) != SA_OK) return st;
+  if ((st = check_bf16(v, "v")) != SA_OK) return st;
+  if ((st = check_bf16(ak, "ak")) != SA_OK) return st;
+  if ((st = check_bf16(av, "av")) != SA_OK) return st;
+  if (lm == nullptr || !aligned(lm, 4))
+    return fail(SA_ERR_INVALID_ARG, "lm must be a non-NULL 4-byte aligned pointer");
+  float scale_log2 = 0.f;
+  if ((st = check_scale(softmax_scale, &scale_log2)) != SA_OK) return st;
+  const float scale =
+      softmax_scale == 0.f ? (float)(1.0 / std::sqrt((double)sa::kHeadDim)) : softmax_scale;
+  hipError_t e = sa::launch_reweight(anchors, k, v, ak, av, lm, B, P, T, H, scale, logmass_key,
+                                     static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SA_ERR_HIP, "reweight launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+sa_status sparse_attn_fwd_spark(const void *q, const void *k, const void *v, int32_t B, int32_t T,
+                                int32_t H, int32_t D, int32_t sink_start, int32_t sink_tokens,
+                                int32_t video_tail_mode, const float *key_bias,
+                                int64_t key_bias_numel, const int32_t *block_idx,
+                                const int32_t *block_cnt, int32_t max_sel, const void *ak,
+                                const void *av, const float *lm, float softmax_scale, void *out,
+                                float *lse, void *stream) {
+  sa_status st = check_shape(B, T, H, D, sink_start, sink_tokens, video_tail_mode);
+  if (st != SA_OK) return st;
+  if ((st = check_bf16(q, "q")) != SA_OK) return st;
+  if ((st = check_bf16(k, "k")) != SA_OK) return st;
+  if ((st = check_bf16(v, "v")) != SA_OK) return st;
+  if ((st = check_bf16(out, "out")) != SA_OK) return st;
+  if ((st = check_bias(key_bias, key_bias_numel, B, T)) != SA_OK) return st;
+  float scale_log2 = 0.f;
+  if ((st = check_scale(softmax_scale, &scale_log2)) != SA_OK) return st;
+  if (lse != nullptr && !aligned(lse, 4)) return fail(SA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  const Split sp = split_rows(T, sink_start, video_tail_mode);
+  if (sp.nvq == 0) return ok();
+  if (sp.nvb > sa::kMaxRouteBlocks)
+    return fail(SA_ERR_UNSUPPORTED, "the approximate branch supports at most %d video blocks (got %d)",
+                sa::kMaxRouteBlocks, sp.nvb);
+  if (block_idx == nullptr || block_cnt == nullptr)
+    return fail(SA_ERR_INVALID_ARG, "block_idx and block_cnt must not be NULL");
+  if (!aligned(block_idx, 4) || !aligned(block_cnt, 4))
+    return fail(SA_ERR_INVALID_ARG, "block_idx and block_cnt must be 4-byte aligned");
+  if (max_sel <= 0) return fail(SA_ERR_INVALID_ARG, "max_sel must be positive");
+  if ((st = check_bf16(ak, "ak")) != SA_OK) return st;
+  if ((st = check_bf16(av, "av")) != SA_OK) return st;
+  if (lm == nullptr || !aligned(lm, 4))
+    return fail(SA_ERR_INVALID_ARG, "lm must be a non-NULL 4-byte aligned pointer");
+
+  sa::AttnArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.lse = lse;
+  a.key_bias = key_bias;
+  a.block_idx = block_idx;
+  a.block_cnt = block_cnt;
+  a.B = B;
+  a.T = T;
+  a.H = H;
+  a.nb = sa_num_blocks(T);
+  a.nvb = sp.nvb;
+  a.nvq = sp.nvq;
+  a.rows_end = sp.rows_end;
+  a.max_sel = max_sel;
+  a.scale_log2 = scale_log2;
+  a.sum_k = ak;
+  a.sum_v = av;
+  a.sum_lm = lm;
+  hipError_t e = sa::launch_attn_sparse_spark(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess)
+    return fail(SA_ERR_HIP, "sparse attention (approximate branch) launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 }  // extern "C"

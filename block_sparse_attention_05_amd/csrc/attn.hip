@@ -81,6 +81,8 @@ constexpr int kKOff = 0;                    // K ring: 2 x 16 KiB
 constexpr int kVOff = 32768;                // V ring: 2 x 16 KiB
 constexpr int kBOff = 65536;                // bias ring: 2 x 256 B
 constexpr int kLdsBytes = 65536 + 512;
+constexpr int kVbOff = kLdsBytes;           // approximate branch: virtual-key logit bias
+constexpr int kVbBytes = kMaxRouteBlocks * 4;
 
 // sched_group_barrier instruction classes
 constexpr int kSchedVALU = 0x002;
@@ -144,6 +146,11 @@ struct Params {
   int row_lo, row_hi;  // rows written: [row_lo, row_hi)
   int nsplit, tiles_per_split;
   float scale_log2;
+  // approximate branch: summaries of (b, h) at sum_k/sum_v + bh*nb*128 and
+  // sum_lm + bh*nb; nvt = ceil(nvb/64) virtual tiles
+  const uint16_t *sum_k, *sum_v;
+  const float *sum_lm;
+  int nvt;
 };
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
@@ -151,11 +158,12 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-template <bool kDense>
+template <bool kDense, bool kSpark = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_kernel(Params p) {
   // K ring (2 tiles) | V ring (2 tiles) | natural-log key bias ring (2 tiles)
-  __shared__ __align__(16) unsigned char smem[kLdsBytes];
+  // [| virtual-key bias, approximate branch]
+  __shared__ __align__(16) unsigned char smem[kLdsBytes + (kSpark ? kVbBytes : 0)];
 
   const int total = p.B * p.H * p.nqb * p.nsplit;
   const int w = xcd_remap(blockIdx.x, total);
@@ -213,8 +221,13 @@ void attn_fwd_kernel(Params p) {
       n_plain += __popcll(__ballot(e < p.nvb));
     }
   }
-  const int n = t_end - t_begin;
+  const int n = t_end - t_begin;  // exact tiles
   if (kbias == nullptr) n_plain = n;
+  // With the approximate branch, nv virtual tiles (64 block summaries each)
+  // come first; then the exact tiles, unbiased ones before biased ones.
+  const int nv = kSpark ? p.nvt : 0;
+  const int nt = nv + n;
+  const int np_end = nv + n_plain;
 
   // Q^T fragments for this lane's query row: d = 16*dc + 8*g + [0, 8).
   // Loaded after the list so that the first tile copies do not wait for them.
@@ -235,7 +248,12 @@ void attn_fwd_kernel(Params p) {
   // The next 64-entry chunk is loaded one call before it is needed, so that
   // the end-of-step wait already covers it: a wait placed by the compiler at
   // the use would also drain the K/V tile loads in flight.
+  // A virtual tile j < nv returns its first summary index 64*j instead.
   auto tile_key0 = [&](int j) -> int {
+    if (kSpark) {
+      if (j < nv) return kBlock * j;
+      j -= nv;
+    }
     const int it = t_begin + j;
     if (kDense) return it * kBlock;
     if (it - list_cb >= 64) {
@@ -282,17 +300,40 @@ void attn_fwd_kernel(Params p) {
   const uint32_t rows8 = (uint32_t)(8 * row_bytes);
   const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>(LDS_PTR(unsigned char, smem));
   const uint32_t wave_lds = (uint32_t)__builtin_amdgcn_readfirstlane(4096 * wave);
-  auto issue_k = [&](int key0, int slot) {
-    const uint32_t base = (uint32_t)key0 * (uint32_t)row_bytes + k_lane;
+  // Summary rows (approximate branch) are 256 B apart, one (b, h) slab of
+  // nb rows; rows past nb read as zero.  Same LDS placement as K/V rows.
+  const int64_t sbase = (int64_t)bh * p.nb * kHeadDim;
+  const i32x4s rsk = buffer_rsrc(kSpark ? p.sum_k + sbase : p.k, kSpark ? (uint32_t)p.nb * 256u : 0u);
+  const i32x4s rsv = buffer_rsrc(kSpark ? p.sum_v + sbase : p.v, kSpark ? (uint32_t)p.nb * 256u : 0u);
+  const uint32_t sk_lane = (uint32_t)((16 * wave + (lane >> 3)) * 256 + 16 * ((lane & 7) ^ (lane >> 3)));
+  const uint32_t sv_lane = (uint32_t)((16 * wave + (lane >> 3)) * 256 + 16 * ((lane & 7) ^ (2 * ((lane >> 3) & 3))));
+  auto issue_k = [&](int key0, int slot, bool virt) {
     const uint32_t lb = lds0 + kKOff + (uint32_t)(slot * 16384) + wave_lds;
+    if (kSpark && virt) {
+      const uint32_t base = (uint32_t)key0 * 256u + sk_lane;
+      lds_dma_b128<0>(rsk, base, lb);
+      lds_dma_b128<1024>(rsk, base + 128, lb);
+      lds_dma_b128<2048>(rsk, base + 2048, lb);
+      lds_dma_b128<3072>(rsk, base + 2048 + 128, lb);
+      return;
+    }
+    const uint32_t base = (uint32_t)key0 * (uint32_t)row_bytes + k_lane;
     lds_dma_b128<0>(rk, base, lb);
     lds_dma_b128<1024>(rk, base + 128, lb);
     lds_dma_b128<2048>(rk, base + rows8, lb);
     lds_dma_b128<3072>(rk, base + rows8 + 128, lb);
   };
-  auto issue_v = [&](int key0, int slot) {
-    const uint32_t base = (uint32_t)key0 * (uint32_t)row_bytes + v_lane;
+  auto issue_v = [&](int key0, int slot, bool virt) {
     const uint32_t lb = lds0 + kVOff + (uint32_t)(slot * 16384) + wave_lds;
+    if (kSpark && virt) {
+      const uint32_t base = (uint32_t)key0 * 256u + sv_lane;
+      lds_dma_b128<0>(rsv, base, lb);
+      lds_dma_b128<1024>(rsv, base + 128, lb);
+      lds_dma_b128<2048>(rsv, base + 2048, lb);
+      lds_dma_b128<3072>(rsv, base + 2048 + 128, lb);
+      return;
+    }
+    const uint32_t base = (uint32_t)key0 * (uint32_t)row_bytes + v_lane;
     lds_dma_b128<0>(rv, base, lb);
     lds_dma_b128<1024>(rv, base + 128, lb);
     lds_dma_b128<2048>(rv, base + rows8, lb);
@@ -324,16 +365,20 @@ void attn_fwd_kernel(Params p) {
   const float c = p.scale_log2;
 
   // One pipeline step on tile j (scores in s_cur, V in slot VS) that also
-  // computes S(j+1) into s_nxt from K slot VS^1 when DO_QK.
-  auto step = [&](auto vs_c, auto biased_c, auto masked_c, auto do_qk_c, f32x16 &s_cur,
-                  f32x16 &s_nxt, int key0) {
+  // computes S(j+1) into s_nxt from K slot VS^1 when DO_QK.  A VIRT tile
+  // (approximate branch) takes its logit bias from the virtual-key bias
+  // array at its first summary index key0.
+  auto step = [&](auto vs_c, auto biased_c, auto masked_c, auto do_qk_c, auto virt_c,
+                  f32x16 &s_cur, f32x16 &s_nxt, int key0) {
     constexpr int VS = decltype(vs_c)::value;
     constexpr bool BIASED = decltype(biased_c)::value;
     constexpr bool MASKED = decltype(masked_c)::value;
     constexpr bool DO_QK = decltype(do_qk_c)::value;
+    constexpr bool VIRT = decltype(virt_c)::value;
     const unsigned char *vbuf = smem + kVOff + VS * 16384;
     const unsigned char *kbuf = smem + kKOff + (VS ^ 1) * 16384;
-    const float *bs = reinterpret_cast<const float *>(smem + kBOff + VS * 256);
+    const float *bs = VIRT ? reinterpret_cast<const float *>(smem + kVbOff) + key0
+                           : reinterpret_cast<const float *>(smem + kBOff + VS * 256);
 
     // S(j+1) MFMAs, issued in two groups so that they overlap the max phase
     // and the exponential phase of tile j.  Their K fragments are read from
@@ -469,18 +514,37 @@ void attn_fwd_kernel(Params p) {
   // step j-1 finished reading, and ends with the barrier that publishes them.
   f32x16 s0, s1;
   int k_cur = 0, k_nxt = 0;
-  if (n > 0) {
+  if (nt > 0) {
     k_cur = tile_key0(0);
-    issue_k(k_cur, 0);
-    issue_v(k_cur, 0);
-    if (n > 1) {
+    issue_k(k_cur, 0, 0 < nv);
+    issue_v(k_cur, 0, 0 < nv);
+    if (nt > 1) {
       k_nxt = tile_key0(1);
-      issue_k(k_nxt, 1);
+      issue_k(k_nxt, 1, 1 < nv);
+    }
+  }
+  if (kSpark && nv > 0) {
+    // Virtual-key bias: lm of every video block the list skips, -inf for
+    // the blocks it holds exactly and for indices past nvb.  Wave w fills
+    // virtual tiles w, w+4, ...: lane x tests its block against every list
+    // entry (the first 64 are already in list_v) and the barrier that ends
+    // the prologue publishes the array.
+    float *vb = reinterpret_cast<float *>(smem + kVbOff);
+    const float *lmp = p.sum_lm + (int64_t)bh * p.nb;
+    for (int vt = __builtin_amdgcn_readfirstlane(wave); vt < nv; vt += kThreads / 64) {
+      const int x = kBlock * vt + lane;
+      bool exact = false;
+      for (int cb = 0; cb < t_end; cb += 64) {
+        const int chunk = cb == 0 ? list_v : (cb + lane < t_end ? list[cb + lane] : -1);
+        const int ne = t_end - cb < 64 ? t_end - cb : 64;
+        for (int ei = 0; ei < ne; ++ei) exact |= __builtin_amdgcn_readlane(chunk, ei) == x;
+      }
+      vb[x] = (x < p.nvb && !exact) ? lmp[x] : -INFINITY;
     }
   }
   __builtin_amdgcn_s_waitcnt(kVmcntZero);
   __syncthreads();
-  if (n > 0) {
+  if (nt > 0) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) s0[r] = 0.f;
 #pragma unroll
@@ -494,15 +558,15 @@ void attn_fwd_kernel(Params p) {
 
   // Steady-state step j < n-1 (S(j+1) computed); the last step is peeled and
   // is the only one that masks keys past T.
-  auto run_step = [&](auto vs_c, auto biased, f32x16 &s_cur, f32x16 &s_nxt, int j) {
+  auto run_step = [&](auto vs_c, auto biased, auto virt, f32x16 &s_cur, f32x16 &s_nxt, int j) {
     const int key_j = k_cur;
-    issue_v(k_nxt, decltype(vs_c)::value ^ 1);
+    issue_v(k_nxt, decltype(vs_c)::value ^ 1, j + 1 < nv);
     int k_nn = 0;
-    if (j + 2 < n) {
+    if (j + 2 < nt) {
       k_nn = tile_key0(j + 2);
-      issue_k(k_nn, decltype(vs_c)::value);
+      issue_k(k_nn, decltype(vs_c)::value, j + 2 < nv);
     }
-    step(vs_c, biased, Bool<false>{}, Bool<true>{}, s_cur, s_nxt, key_j);
+    step(vs_c, biased, Bool<false>{}, Bool<true>{}, virt, s_cur, s_nxt, key_j);
     k_cur = k_nxt;
     k_nxt = k_nn;
     __builtin_amdgcn_s_waitcnt(kVmcntZero);
@@ -510,40 +574,59 @@ void attn_fwd_kernel(Params p) {
   };
   auto last_step = [&](auto vs_c, f32x16 &s_cur, f32x16 &s_nxt) {
     const int key_j = k_cur;
+    if (kSpark && nt - 1 < nv) {  // no exact tile at all: the last one is virtual
+      step(vs_c, Bool<true>{}, Bool<false>{}, Bool<false>{}, Bool<true>{}, s_cur, s_nxt, key_j);
+      __syncthreads();
+      return;
+    }
     const bool masked = key_j + kBlock > T;
-    if (n - 1 >= n_plain) {
-      if (masked) step(vs_c, Bool<true>{}, Bool<true>{}, Bool<false>{}, s_cur, s_nxt, key_j);
-      else step(vs_c, Bool<true>{}, Bool<false>{}, Bool<false>{}, s_cur, s_nxt, key_j);
+    if (nt - 1 >= np_end) {
+      if (masked) step(vs_c, Bool<true>{}, Bool<true>{}, Bool<false>{}, Bool<false>{}, s_cur, s_nxt, key_j);
+      else step(vs_c, Bool<true>{}, Bool<false>{}, Bool<false>{}, Bool<false>{}, s_cur, s_nxt, key_j);
     } else {
-      if (masked) step(vs_c, Bool<false>{}, Bool<true>{}, Bool<false>{}, s_cur, s_nxt, key_j);
-      else step(vs_c, Bool<false>{}, Bool<false>{}, Bool<false>{}, s_cur, s_nxt, key_j);
+      if (masked) step(vs_c, Bool<false>{}, Bool<true>{}, Bool<false>{}, Bool<false>{}, s_cur, s_nxt, key_j);
+      else step(vs_c, Bool<false>{}, Bool<false>{}, Bool<false>{}, Bool<false>{}, s_cur, s_nxt, key_j);
     }
     __syncthreads();
   };
   // Steps j < n_plain are unbiased and the rest biased.  Each loop body holds
   // one step variant only: a runtime choice between the two inside a loop
   // makes the compiler route the O accumulators through copies every step.
+  // Any tile kind, chosen at run time (phase transitions only).
+  auto run_any = [&](auto vs_c, f32x16 &s_cur, f32x16 &s_nxt, int j) {
+    if (kSpark && j < nv) run_step(vs_c, Bool<true>{}, Bool<true>{}, s_cur, s_nxt, j);
+    else if (j < np_end) run_step(vs_c, Bool<false>{}, Bool<false>{}, s_cur, s_nxt, j);
+    else run_step(vs_c, Bool<true>{}, Bool<false>{}, s_cur, s_nxt, j);
+  };
   int j = 0;
-  for (; j + 2 < n && j + 2 <= n_plain; j += 2) {
-    run_step(Int<0>{}, Bool<false>{}, s0, s1, j);
-    run_step(Int<1>{}, Bool<false>{}, s1, s0, j + 1);
+  if (kSpark) {
+    for (; j + 2 < nt && j + 2 <= nv; j += 2) {
+      run_step(Int<0>{}, Bool<true>{}, Bool<true>{}, s0, s1, j);
+      run_step(Int<1>{}, Bool<true>{}, Bool<true>{}, s1, s0, j + 1);
+    }
+    if (j + 2 < nt && j < nv) {  // j + 1 == nv
+      run_any(Int<0>{}, s0, s1, j);
+      run_any(Int<1>{}, s1, s0, j + 1);
+      j += 2;
+    }
   }
-  if (j + 2 < n && j < n_plain) {  // j + 1 == n_plain
-    run_step(Int<0>{}, Bool<false>{}, s0, s1, j);
-    run_step(Int<1>{}, Bool<true>{}, s1, s0, j + 1);
+  for (; j + 2 < nt && j + 2 <= np_end; j += 2) {
+    run_step(Int<0>{}, Bool<false>{}, Bool<false>{}, s0, s1, j);
+    run_step(Int<1>{}, Bool<false>{}, Bool<false>{}, s1, s0, j + 1);
+  }
+  if (j + 2 < nt && j < np_end) {  // j + 1 == np_end (and j >= nv)
+    run_step(Int<0>{}, Bool<false>{}, Bool<false>{}, s0, s1, j);
+    run_step(Int<1>{}, Bool<true>{}, Bool<false>{}, s1, s0, j + 1);
     j += 2;
   }
-  for (; j + 2 < n; j += 2) {
-    run_step(Int<0>{}, Bool<true>{}, s0, s1, j);
-    run_step(Int<1>{}, Bool<true>{}, s1, s0, j + 1);
+  for (; j + 2 < nt; j += 2) {
+    run_step(Int<0>{}, Bool<true>{}, Bool<false>{}, s0, s1, j);
+    run_step(Int<1>{}, Bool<true>{}, Bool<false>{}, s1, s0, j + 1);
   }
-  if (j + 1 < n) {
-    if (j >= n_plain)
-      run_step(Int<0>{}, Bool<true>{}, s0, s1, j);
-    else
-      run_step(Int<0>{}, Bool<false>{}, s0, s1, j);
+  if (j + 1 < nt) {
+    run_any(Int<0>{}, s0, s1, j);
     last_step(Int<1>{}, s1, s0);
-  } else if (j < n) {
+  } else if (j < nt) {
     last_step(Int<0>{}, s0, s1);
   }
 
@@ -697,6 +780,10 @@ Params make_params(const AttnArgs &a, int qb0, int nqb) {
   p.nsplit = 1;
   p.tiles_per_split = a.nb;
   p.scale_log2 = a.scale_log2;
+  p.sum_k = static_cast<const uint16_t *>(a.sum_k);
+  p.sum_v = static_cast<const uint16_t *>(a.sum_v);
+  p.sum_lm = a.sum_lm;
+  p.nvt = 0;
   return p;
 }
 
@@ -728,6 +815,18 @@ hipError_t launch_attn_sparse(const AttnArgs &a, hipStream_t stream) {
   p.row_hi = a.rows_end;
   const int total = a.B * a.H * a.nvq;
   hipLaunchKernelGGL(attn_fwd_kernel<false>, dim3(total), dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_sparse_spark(const AttnArgs &a, hipStream_t stream) {
+  if (a.nvq <= 0) return hipSuccess;
+  if (a.nvb > kMaxRouteBlocks || a.sum_k == nullptr || a.sum_v == nullptr || a.sum_lm == nullptr)
+    return hipErrorInvalidValue;
+  Params p = make_params(a, 0, a.nvq);
+  p.row_hi = a.rows_end;
+  p.nvt = (a.nvb + kBlock - 1) / kBlock;
+  const int total = a.B * a.H * a.nvq;
+  hipLaunchKernelGGL((attn_fwd_kernel<false, true>), dim3(total), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

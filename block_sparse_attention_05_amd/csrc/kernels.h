@@ -35,10 +35,16 @@ struct AttnArgs {
   int nvq;                    // routed query blocks
   int rows_end;               // rows [0, rows_end) are sparse, [rows_end, T) dense
   float scale_log2;           // softmax_scale * log2(e)
+  // approximate branch (nullable): one summary per (b, h, K/V block)
+  const void *sum_k, *sum_v;  // bf16 [B, 1, H, nb, 128]
+  const float *sum_lm;        // fp32 [B, 1, H, nb], natural log
 };
 
 // Sparse rows [0, rows_end) of query blocks [0, nvq) over their block lists.
 hipError_t launch_attn_sparse(const AttnArgs &a, hipStream_t stream);
+// The same plus one virtual key (sum_k, sum_v, additive logit sum_lm) per
+// video block that a row's list skips.  Needs nvb <= kMaxRouteBlocks.
+hipError_t launch_attn_sparse_spark(const AttnArgs &a, hipStream_t stream);
 // Dense rows [rows_end, T) over all keys.  With a workspace of at least
 // dense_workspace_bytes() the key range of each query block is split over
 // dense_splits() workgroups whose partial results are merged by a second
@@ -47,5 +53,16 @@ hipError_t launch_attn_dense(const AttnArgs &a, void *workspace, size_t workspac
                              hipStream_t stream);
 int dense_splits(int B, int H, int nb, int nvb);
 size_t dense_workspace_bytes(int B, int H, int nb, int nvb);
+
+// Spark summaries (spark.hip).
+// Global anchor: mean of the video rows [0, sink_start) of Q per (b, h),
+// bf16 [B, 1, H, 128]; the workspace holds fp64 partial sums.
+size_t anchor_workspace_bytes(int B, int H, int sink_start);
+hipError_t launch_anchor(const void *q, void *workspace, void *anchor, int B, int T, int H,
+                         int sink_start, hipStream_t stream);
+// Virtual summaries of every 64-token K/V block for P anchors.
+hipError_t launch_reweight(const void *anchors, const void *k, const void *v, void *ak, void *av,
+                           float *lm, int B, int P, int T, int H, float scale, int pre_round,
+                           hipStream_t stream);
 
 }  // namespace sa

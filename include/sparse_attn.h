@@ -264,6 +264,85 @@ sa_status dense_sink_fwd(const void *q, const void *k, const void *v,
                          void *workspace, size_t workspace_bytes,
                          void *stream);
 
+/* ---- Spark virtual summaries and the approximate branch --------------------
+ *
+ * Defined by: page "Sol-Attn and Spark for MiniMax-H3", Spark primitives (the
+ * spark_reweight paragraph: per anchor and physical 64-token K/V block,
+ * softmax-weighted keys and values and lm = logsumexp(a.k/sqrt(128)) -
+ * a.ak/sqrt(128), partial final blocks without padding) and Spark inference
+ * integration (one global representative per head, the mean of all
+ * target-video queries, stored in BF16; summaries merged with exact attention
+ * in one FP32 online-softmax accumulator; log-mass against the stored BF16
+ * summary key by default).  Optional: the Top-K path above does not use
+ * them.
+ */
+
+/* Workspace bytes spark_global_anchor needs: B * H * ceil(sink_start / 256)
+ * * 128 * 8 (fp64 partial sums); 0 if sink_start is not in [1, T]. */
+size_t sa_anchor_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t sink_start);
+
+/*
+ * spark_global_anchor - anchor[b, 0, h, :] = bf16(fp32(mean of Q rows
+ * [0, sink_start) of batch b, head h)); the fp64 sums are exact.
+ *
+ * q           bf16 [B, T, H, 128].  sink_start >= 1 (SA_ERR_INVALID_ARG
+ *             otherwise), sink_tokens = T - sink_start.
+ * anchor      bf16 [B, 1, H, 128] out, 16-byte aligned.
+ * workspace   device scratch of >= sa_anchor_workspace_bytes(...) bytes,
+ *             16-byte aligned.
+ */
+sa_status spark_global_anchor(const void *q, int32_t B, int32_t T, int32_t H, int32_t D,
+                              int32_t sink_start, int32_t sink_tokens, void *anchor,
+                              void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * spark_reweight - virtual summaries of every 64-token K/V block for P
+ * anchors.  For anchor p and block j (keys [64j, min(64j+64, T))):
+ *   z_t = scale * a_p . k_t,  w_t = softmax_t(z),
+ *   ak  = sum_t w_t k_t,  av = sum_t w_t v_t   (bf16, round to nearest even),
+ *   lm  = logsumexp_t(z) - scale * a_p . key  (fp32, natural log), where key
+ *         is ak as stored (logmass_key 0, the pages' default) or the fp32
+ *         weighted key before rounding (logmass_key 1).
+ * fp32 arithmetic throughout.
+ *
+ * anchors     bf16 [B, P, H, 128], contiguous, 16-byte aligned.  P >= 1.
+ * k, v        bf16 [B, T, H, 128].
+ * softmax_scale  0 selects 1/sqrt(128); must equal the scale later given to
+ *             sparse_attn_fwd_spark.
+ * ak, av      bf16 [B, P, H, NB, 128] out (NB = ceil(T / 64)), 16-byte aligned.
+ * lm          fp32 [B, P, H, NB] out.
+ * Errors: SA_ERR_UNSUPPORTED when B*P > 65535 (launch grid).
+ */
+sa_status spark_reweight(const void *anchors, const void *k, const void *v,
+                         int32_t B, int32_t P, int32_t T, int32_t H, int32_t D,
+                         float softmax_scale, int32_t logmass_key,
+                         void *ak, void *av, float *lm, void *stream);
+
+/*
+ * sparse_attn_fwd_spark - sparse_attn_fwd plus the approximate branch: every
+ * video block j < NVB that list(i) leaves out joins the softmax of the rows
+ * of query block i as one virtual key with key ak[b, 0, h, j], value
+ * av[b, 0, h, j] and logit scale * q_t . ak + lm[b, 0, h, j].  Sink blocks
+ * are always exact and never summarised (page "Add key bias to chunked
+ * Sol-Attn producers", Tests and source audit: sink blocks are excluded from
+ * the pooled tail).  Arguments as for sparse_attn_fwd, plus:
+ *
+ * ak, av      bf16 [B, 1, H, NB, 128] (one anchor), as spark_reweight writes.
+ * lm          fp32 [B, 1, H, NB].
+ * Errors: SA_ERR_UNSUPPORTED when NVB > 1024.
+ */
+sa_status sparse_attn_fwd_spark(const void *q, const void *k, const void *v,
+                                int32_t B, int32_t T, int32_t H, int32_t D,
+                                int32_t sink_start, int32_t sink_tokens,
+                                int32_t video_tail_mode,
+                                const float *key_bias, int64_t key_bias_numel,
+                                const int32_t *block_idx, const int32_t *block_cnt,
+                                int32_t max_sel,
+                                const void *ak, const void *av, const float *lm,
+                                float softmax_scale,
+                                void *out, float *lse,
+                                void *stream);
+
 #ifdef __cplusplus
 }
 #endif

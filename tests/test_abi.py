@@ -215,3 +215,70 @@ def test_device_info_rejects_null_pointers(L):
     # checked on the host before any runtime query, so this runs without a GPU
     assert L.sa_device_info(0, None, None) == 1
     assert "must not be NULL" in L.sa_last_error().decode()
+
+
+# ---- Spark summaries and the approximate branch ----------------------------
+
+def test_anchor_workspace_bytes(L):
+    assert L.sa_anchor_workspace_bytes(1, 9505, 56, 9216) == 56 * 36 * 128 * 8
+    assert L.sa_anchor_workspace_bytes(2, 1000, 3, 257) == 2 * 3 * 2 * 128 * 8
+    assert L.sa_anchor_workspace_bytes(1, 1000, 3, 0) == 0
+    assert L.sa_anchor_workspace_bytes(1, 1000, 3, 1001) == 0
+
+
+def _anchor(L, **kw):
+    a = dict(q=FAKE, B=1, T=1000, H=2, D=128, ss=900, st=100, out=FAKE, ws=FAKE, ws_bytes=1 << 20,
+             stream=None)
+    a.update(kw)
+    return L.spark_global_anchor(a["q"], a["B"], a["T"], a["H"], a["D"], a["ss"], a["st"], a["out"],
+                                 a["ws"], a["ws_bytes"], a["stream"])
+
+
+def _reweight(L, **kw):
+    a = dict(a=FAKE, k=FAKE, v=FAKE, B=1, P=1, T=1000, H=2, D=128, scale=0.0, key=0, ak=FAKE,
+             av=FAKE, lm=FAKE, stream=None)
+    a.update(kw)
+    return L.spark_reweight(a["a"], a["k"], a["v"], a["B"], a["P"], a["T"], a["H"], a["D"],
+                            a["scale"], a["key"], a["ak"], a["av"], a["lm"], a["stream"])
+
+
+def _fwd_spark(L, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, B=1, T=1000, H=2, D=128, ss=900, st=100, mode=0, bias=None,
+             bias_n=0, idx=FAKE, cnt=FAKE, max_sel=8, ak=FAKE, av=FAKE, lm=FAKE, scale=0.0,
+             out=FAKE, lse=None, stream=None)
+    a.update(kw)
+    return L.sparse_attn_fwd_spark(a["q"], a["k"], a["v"], a["B"], a["T"], a["H"], a["D"], a["ss"],
+                                   a["st"], a["mode"], a["bias"], a["bias_n"], a["idx"], a["cnt"],
+                                   a["max_sel"], a["ak"], a["av"], a["lm"], a["scale"], a["out"],
+                                   a["lse"], a["stream"])
+
+
+SPARK_CASES = [
+    (_anchor, dict(ss=0, st=1000), INVALID, "sink_start >= 1"),
+    (_anchor, dict(D=64), INVALID, "D must be 128"),
+    (_anchor, dict(out=None), INVALID, "anchor must not be NULL"),
+    (_anchor, dict(ws_bytes=2 * 4 * 128 * 8 - 1), WORKSPACE, "workspace"),
+    (_anchor, dict(ws=None), WORKSPACE, "workspace"),
+    (_reweight, dict(P=0), INVALID, "P (anchors)"),
+    (_reweight, dict(key=2), INVALID, "logmass_key"),
+    (_reweight, dict(lm=None), INVALID, "lm must be"),
+    (_reweight, dict(ak=ctypes.c_void_p((1 << 20) + 2)), INVALID, "ak must be 16-byte aligned"),
+    (_reweight, dict(scale=-0.5), INVALID, "softmax_scale"),
+    (_reweight, dict(B=2, P=40000), UNSUPPORTED, "B*P"),
+    (_fwd_spark, dict(ak=None), INVALID, "ak must not be NULL"),
+    (_fwd_spark, dict(lm=None), INVALID, "lm must be"),
+    (_fwd_spark, dict(mode=5), INVALID, "video_tail_mode"),
+    (_fwd_spark, dict(T=65600, ss=65600, st=0), UNSUPPORTED, "at most 1024"),
+    (_fwd_spark, dict(idx=None), INVALID, "block_idx"),
+]
+
+
+@pytest.mark.parametrize("fn,kw,code,msg", SPARK_CASES,
+                         ids=[f"{f.__name__}-{i}" for i, (f, _, _, _) in enumerate(SPARK_CASES)])
+def test_spark_entry_points_reject(L, fn, kw, code, msg):
+    assert fn(L, **kw) == code
+    assert msg in L.sa_last_error().decode()
+
+
+def test_spark_nothing_to_do_is_ok(L):
+    assert _fwd_spark(L, ss=10, st=990, idx=None, cnt=None, ak=None, av=None, lm=None) == 0

@@ -1,0 +1,190 @@
+"""Spark virtual summaries and the approximate branch: HIP path vs the CPU
+oracle (oracle/spark_summaries.py) on the same seeded bf16 inputs (needs a
+GPU; every call goes through the C ABI).
+
+Anchor: bit-exact.  Summaries: ak / av within one bf16 ulp of the oracle's
+(both round a value they computed in different precision), lm within 1e-4
+of the oracle's log-mass taken against the GPU's own stored key.  Attention:
+max-abs <= 2e-2 and mean-abs <= 2e-3, with the oracle fed the GPU's lists
+and summaries (so the check isolates the merge).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle.sparse_attention as ora
+import oracle.spark_summaries as osp
+import workloads
+from gpu_helpers import MAX_ABS, MEAN_ABS, err_stats, log, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def _bf16_ulp(x):
+    """Spacing of bf16 values at |x| (normal range)."""
+    a = np.maximum(np.abs(np.asarray(x, np.float64)), 2.0 ** -126)
+    return 2.0 ** (np.floor(np.log2(a)) - 7)
+
+
+def _check_summaries(got_ak, got_av, got_lm, a, k, v, heads, name, logmass_key="stored"):
+    """Oracle summaries for the given heads; returns the worst deviations."""
+    a_n = to_np(a)[:, :, heads]
+    k_n, v_n = to_np(k)[:, :, heads], to_np(v)[:, :, heads]
+    ak, av, lm = osp.virtual_summaries(a_n, k_n, v_n, logmass_key=logmass_key)
+    gak = to_np(got_ak)[:, :, heads]
+    gav = to_np(got_av)[:, :, heads]
+    glm = got_lm.cpu().numpy()[:, :, heads]
+    dk = np.abs(gak - ak) / (_bf16_ulp(ak) + 1e-30)
+    dv = np.abs(gav - av) / (_bf16_ulp(av) + 1e-30)
+    small_k = np.abs(gak - ak) <= 1e-3
+    small_v = np.abs(gav - av) <= 1e-3
+    assert np.all((dk <= 1.0) | small_k), f"ak off by {dk.max():.2f} ulp"
+    assert np.all((dv <= 1.0) | small_v), f"av off by {dv.max():.2f} ulp"
+    # log-mass against the GPU's own key: isolates lm from a bf16 rounding flip
+    B, P, H, NB, _ = gak.shape
+    T = k_n.shape[1]
+    lm_own = np.zeros_like(glm, dtype=np.float64)
+    s = 1.0 / np.sqrt(128)
+    for b in range(B):
+        for p in range(P):
+            for h in range(H):
+                for j in range(NB):
+                    keys = k_n[b, 64 * j:min(T, 64 * j + 64), h]
+                    shift = gak[b, p, h, j] if logmass_key == "stored" else ak[b, p, h, j]
+                    lm_own[b, p, h, j] = osp.log_mass(a_n[b, p, h], keys, shift, s)
+    tol = 1e-4 if logmass_key == "stored" else 5e-3
+    e_own = np.abs(glm - lm_own).max()
+    e_ora = np.abs(glm - lm).max()
+    log(f"[{name}] summaries: ak max {dk.max():.2f} ulp, av max {dv.max():.2f} ulp, "
+        f"lm vs own-key {e_own:.2e}, vs oracle {e_ora:.2e}")
+    assert e_own <= tol and e_ora <= 5e-3
+
+
+def _split_case(seed=7):
+    q, k, v, tv = workloads.video_qkv(B=1, H=3, frames=2, ctx_tokens=150, seed=seed, height=16, width=32)
+    return q, k, v, tv - 17
+
+
+def test_anchor_bit_exact():
+    import block_sparse_attention_05_amd as sa
+    for (q, ss) in ((_split_case()[0], 1007), (workloads.mid().q, 8192)):
+        got = sa.spark_global_anchor(q.cuda(), ss)
+        torch.cuda.synchronize()
+        want = osp.global_anchor(to_np(q), ss)
+        assert np.array_equal(to_np(got).view(np.uint32), want.view(np.uint32))
+
+
+@pytest.mark.parametrize("key", ["stored", "pre_round"])
+def test_reweight_matches_oracle(key):
+    import block_sparse_attention_05_amd as sa
+    q, k, v, ss = _split_case()                      # T = 1174: partial final block of 22 keys
+    qc, kc, vc = q.cuda(), k.cuda(), v.cuda()
+    g = torch.Generator().manual_seed(21)
+    anchors = torch.cat([sa.spark_global_anchor(qc, ss),
+                         torch.randn(1, 1, 3, 128, generator=g).to(torch.bfloat16).cuda()], dim=1)
+    ak, av, lm = sa.spark_reweight(anchors.contiguous(), kc, vc, logmass_key=key)
+    torch.cuda.synchronize()
+    assert ak.shape == (1, 2, 3, 19, 128) and lm.shape == (1, 2, 3, 19)
+    _check_summaries(ak, av, lm, anchors.cpu(), k, v, [0, 1, 2], f"reweight_{key}", key)
+
+
+def _spark_parity(q, k, v, ss, ratio, radius, name, key_bias=None, tail_mode="dense"):
+    import block_sparse_attention_05_amd as sa
+    qc, kc, vc = q.cuda(), k.cuda(), v.cuda()
+    kb = None if key_bias is None else key_bias.cuda()
+    out, lse, parts = sa.routed_attention_spark(qc, kc, vc, ss, ratio, radius, video_tail_mode=tail_mode,
+                                                key_bias=kb, return_lse=True, return_parts=True)
+    torch.cuda.synchronize()
+    ak, av, lm = (x.cpu() for x in parts["summaries"])
+    qn, kn, vn = to_np(q), to_np(k), to_np(v)
+    rt = ora.route(qn, kn, ss, ratio, radius, tail_mode=tail_mode)
+    idx, cnt = parts["block_idx"].cpu().numpy(), parts["block_cnt"].cpu().numpy()
+    for b, brow in enumerate(rt.rows):
+        for h, hrow in enumerate(brow):
+            for i, sel in enumerate(hrow):
+                got = idx[b, h, i, :cnt[b, h, i]].tolist()
+                assert got == sel.blocks or sel.near_tie
+                sel.blocks = got
+    want, want_lse, _ = osp.routed_attention_spark(
+        qn, kn, vn, ss, ratio, radius, (to_np(ak), to_np(av), lm.numpy().astype(np.float64)),
+        key_bias=None if key_bias is None else key_bias.numpy(), rt=rt, tail_mode=tail_mode)
+    got = to_np(out)
+    assert np.isfinite(got).all()
+    mx, mean = err_stats(got, want)
+    lmx, _ = err_stats(lse.cpu().numpy(), want_lse)
+    log(f"[{name}] spark out max_abs={mx:.3e} mean_abs={mean:.3e} lse max_abs={lmx:.3e}")
+    assert mx <= MAX_ABS and mean <= MEAN_ABS and lmx <= 1e-2
+    return out, parts
+
+
+def test_spark_split_block_with_bias():
+    q, k, v, ss = _split_case()
+    bias = workloads.sink_key_bias(1, q.shape[1], ss, seed=8)
+    _spark_parity(q, k, v, ss, 0.2, 1, "spark_split", key_bias=bias)
+
+
+def test_spark_pad_mode():
+    q, k, v, ss = _split_case(seed=9)
+    bias = workloads.sink_key_bias(1, q.shape[1], ss, seed=10)
+    _spark_parity(q, k, v, ss, 0.2, 1, "spark_pad", key_bias=bias, tail_mode="pad")
+
+
+def test_spark_many_virtual_tiles_odd_count():
+    # NVB = 130: three virtual tiles (an odd count), lists of 13 + 1 exact
+    # video blocks, radius 0
+    q, k, v = workloads.random_qkv(1, 64 * 130 + 100, 2, seed=11)
+    _spark_parity(q, k, v, 64 * 130, 0.1, 0, "spark_nvb130")
+
+
+def test_spark_ratio_one_bit_identical_to_exact():
+    """Nothing skipped: every virtual key is masked and the result must be
+    the exact path's, bit for bit."""
+    import block_sparse_attention_05_amd as sa
+    q, k, v, ss = _split_case(seed=12)
+    qc, kc, vc = q.cuda(), k.cuda(), v.cuda()
+    bias = workloads.sink_key_bias(1, q.shape[1], ss, seed=13).cuda()
+    idx, cnt = sa.sparse_attn_route(qc, kc, ss, 1.0, 0)
+    summ = sa.spark_reweight(sa.spark_global_anchor(qc, ss), kc, vc)
+    lse_a = torch.zeros(1, 3, q.shape[1], device="cuda")
+    lse_b = torch.zeros(1, 3, q.shape[1], device="cuda")
+    a = sa.sparse_attn_fwd(qc, kc, vc, ss, idx, cnt, key_bias=bias, lse=lse_a)
+    b = sa.sparse_attn_fwd_spark(qc, kc, vc, ss, idx, cnt, summ, key_bias=bias, lse=lse_b)
+    torch.cuda.synchronize()
+    rows = 64 * (ss // 64)
+    assert torch.equal(a[:, :rows], b[:, :rows]) and torch.equal(lse_a[:, :, :rows], lse_b[:, :, :rows])
+
+
+def test_spark_h3_sampled():
+    """Full H3 size: summaries of three heads and 32 sampled query blocks
+    against the oracle."""
+    import block_sparse_attention_05_amd as sa
+    wl = workloads.h3(with_bias=True)
+    q, k, v, kb = wl.q.cuda(), wl.k.cuda(), wl.v.cuda(), wl.key_bias.cuda()
+    ss = wl.sink_start
+    out, lse, parts = sa.routed_attention_spark(q, k, v, ss, wl.topk_ratio, wl.local_radius, key_bias=kb,
+                                                return_lse=True, return_parts=True)
+    torch.cuda.synchronize()
+    anchor = parts["anchor"].cpu()
+    assert np.array_equal(to_np(anchor).view(np.uint32),
+                          osp.global_anchor(to_np(wl.q), ss).view(np.uint32))
+    ak, av, lm = (x.cpu() for x in parts["summaries"])
+    _check_summaries(ak, av, lm, anchor, wl.k, wl.v, [0, 17, 55], "spark_h3")
+    qn, kn, vn = to_np(wl.q), to_np(wl.k), to_np(wl.v)
+    got = to_np(out)
+    glse = lse.cpu().numpy()
+    idx, cnt = parts["block_idx"].cpu().numpy(), parts["block_cnt"].cpu().numpy()
+    rng = np.random.default_rng(5)
+    akn, avn, lmn = to_np(ak), to_np(av), lm.numpy().astype(np.float64)
+    errs, lerrs = [], []
+    nvb = ss // 64
+    for _ in range(32):
+        h, i = int(rng.integers(56)), int(rng.integers(nvb))
+        blocks = idx[0, h, i, :cnt[0, h, i]].tolist()
+        o, l = osp.approx_block_output(qn, kn, vn, 0, h, i, blocks, akn, avn, lmn,
+                                       wl.key_bias.numpy(), nvb)
+        errs.append(np.abs(got[0, 64 * i:64 * i + 64, h] - o))
+        lerrs.append(np.abs(glse[0, h, 64 * i:64 * i + 64] - l))
+    e = np.concatenate([x.ravel() for x in errs])
+    le = np.concatenate([x.ravel() for x in lerrs])
+    log(f"[spark_h3] sampled out max_abs={e.max():.3e} mean_abs={e.mean():.3e} lse max_abs={le.max():.3e}")
+    assert e.max() <= MAX_ABS and e.mean() <= MEAN_ABS and le.max() <= 1e-2
