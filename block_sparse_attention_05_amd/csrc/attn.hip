@@ -81,8 +81,13 @@ constexpr int kKOff = 0;                    // K ring: 2 x 16 KiB
 constexpr int kVOff = 32768;                // V ring: 2 x 16 KiB
 constexpr int kBOff = 65536;                // bias ring: 2 x 256 B
 constexpr int kLdsBytes = 65536 + 512;
-constexpr int kVbOff = kLdsBytes;           // approximate branch: virtual-key logit bias
-constexpr int kVbBytes = kMaxRouteBlocks * 4;
+// Approximate branch: virtual-key logit bias (kMaxRouteBlocks floats), 64
+// zeros (bias of the sink tiles without key_bias), summary row of each
+// virtual key (kMaxRouteBlocks ints).
+constexpr int kVbOff = kLdsBytes;
+constexpr int kVrowOff = kVbOff + kMaxRouteBlocks * 4 + 256;
+constexpr int kVflagOff = kVrowOff + kMaxRouteBlocks * 4;   // one byte per video block
+constexpr int kVbBytes = kMaxRouteBlocks * 9 + 256;
 
 // sched_group_barrier instruction classes
 constexpr int kSchedVALU = 0x002;
@@ -147,10 +152,9 @@ struct Params {
   int nsplit, tiles_per_split;
   float scale_log2;
   // approximate branch: summaries of (b, h) at sum_k/sum_v + bh*nb*128 and
-  // sum_lm + bh*nb; nvt = ceil(nvb/64) virtual tiles
+  // sum_lm + bh*nb
   const uint16_t *sum_k, *sum_v;
   const float *sum_lm;
-  int nvt;
 };
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
@@ -177,7 +181,7 @@ void attn_fwd_kernel(Params p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: SGPR
   const int rw = wave & 1;     // query rows 32*rw .. +31 of the block
   const int kh = wave >> 1;    // keys 32*kh .. +31 of every tile
   const int g = lane >> 5;
@@ -222,12 +226,18 @@ void attn_fwd_kernel(Params p) {
     }
   }
   const int n = t_end - t_begin;  // exact tiles
-  if (kbias == nullptr) n_plain = n;
   // With the approximate branch, nv virtual tiles (64 block summaries each)
-  // come first; then the exact tiles, unbiased ones before biased ones.
-  const int nv = kSpark ? p.nvt : 0;
+  // sit between the exact video tiles and the sink tiles, and every tile
+  // from the first virtual one on is biased: virtual tiles by their
+  // log-mass, sink tiles by key_bias (or zero without it).  The biased tiles
+  // stay a suffix and the partial tile stays last.
+  // The virtual keys are the video blocks the list skips, packed in
+  // ascending order: nvb minus the list's video entries.
+  const int nv = kSpark ? (p.nvb - n_plain + kBlock - 1) / kBlock : 0;
   const int nt = nv + n;
-  const int np_end = nv + n_plain;
+  if (!kSpark && kbias == nullptr) n_plain = n;
+  const int np_end = n_plain;          // tiles [0, np_end) are unbiased
+  auto is_virt = [&](int j) { return kSpark && (uint32_t)(j - np_end) < (uint32_t)nv; };
 
   // Q^T fragments for this lane's query row: d = 16*dc + 8*g + [0, 8).
   // Loaded after the list so that the first tile copies do not wait for them.
@@ -248,10 +258,10 @@ void attn_fwd_kernel(Params p) {
   // The next 64-entry chunk is loaded one call before it is needed, so that
   // the end-of-step wait already covers it: a wait placed by the compiler at
   // the use would also drain the K/V tile loads in flight.
-  // A virtual tile j < nv returns its first summary index 64*j instead.
+  // A virtual tile returns its first summary index instead.
   auto tile_key0 = [&](int j) -> int {
-    if (kSpark) {
-      if (j < nv) return kBlock * j;
+    if (kSpark && j >= np_end) {
+      if (j < np_end + nv) return kBlock * (j - np_end);
       j -= nv;
     }
     const int it = t_begin + j;
@@ -301,20 +311,24 @@ void attn_fwd_kernel(Params p) {
   const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>(LDS_PTR(unsigned char, smem));
   const uint32_t wave_lds = (uint32_t)__builtin_amdgcn_readfirstlane(4096 * wave);
   // Summary rows (approximate branch) are 256 B apart, one (b, h) slab of
-  // nb rows; rows past nb read as zero.  Same LDS placement as K/V rows.
+  // nb rows.  A virtual tile gathers the rows of its 64 virtual keys (the
+  // skipped blocks, listed in LDS); same LDS placement as K/V rows.
   const int64_t sbase = (int64_t)bh * p.nb * kHeadDim;
   const i32x4s rsk = buffer_rsrc(kSpark ? p.sum_k + sbase : p.k, kSpark ? (uint32_t)p.nb * 256u : 0u);
   const i32x4s rsv = buffer_rsrc(kSpark ? p.sum_v + sbase : p.v, kSpark ? (uint32_t)p.nb * 256u : 0u);
-  const uint32_t sk_lane = (uint32_t)((16 * wave + (lane >> 3)) * 256 + 16 * ((lane & 7) ^ (lane >> 3)));
-  const uint32_t sv_lane = (uint32_t)((16 * wave + (lane >> 3)) * 256 + 16 * ((lane & 7) ^ (2 * ((lane >> 3) & 3))));
+  // (The summary-row lane offsets are formed where used, so that they hold
+  // no registers through the exact-tile loops.)
+  const int *vrow = reinterpret_cast<const int *>(smem + kVrowOff);
   auto issue_k = [&](int key0, int slot, bool virt) {
     const uint32_t lb = lds0 + kKOff + (uint32_t)(slot * 16384) + wave_lds;
     if (kSpark && virt) {
-      const uint32_t base = (uint32_t)key0 * 256u + sk_lane;
-      lds_dma_b128<0>(rsk, base, lb);
-      lds_dma_b128<1024>(rsk, base + 128, lb);
-      lds_dma_b128<2048>(rsk, base + 2048, lb);
-      lds_dma_b128<3072>(rsk, base + 2048 + 128, lb);
+      const int r = key0 + 16 * wave + (lane >> 3);
+      const uint32_t sw = 16u * (uint32_t)((lane & 7) ^ (lane >> 3));
+      const uint32_t ba = (uint32_t)vrow[r] * 256u + sw, bb = (uint32_t)vrow[r + 8] * 256u + sw;
+      lds_dma_b128<0>(rsk, ba, lb);
+      lds_dma_b128<1024>(rsk, ba + 128, lb);
+      lds_dma_b128<2048>(rsk, bb, lb);
+      lds_dma_b128<3072>(rsk, bb + 128, lb);
       return;
     }
     const uint32_t base = (uint32_t)key0 * (uint32_t)row_bytes + k_lane;
@@ -326,11 +340,13 @@ void attn_fwd_kernel(Params p) {
   auto issue_v = [&](int key0, int slot, bool virt) {
     const uint32_t lb = lds0 + kVOff + (uint32_t)(slot * 16384) + wave_lds;
     if (kSpark && virt) {
-      const uint32_t base = (uint32_t)key0 * 256u + sv_lane;
-      lds_dma_b128<0>(rsv, base, lb);
-      lds_dma_b128<1024>(rsv, base + 128, lb);
-      lds_dma_b128<2048>(rsv, base + 2048, lb);
-      lds_dma_b128<3072>(rsv, base + 2048 + 128, lb);
+      const int r = key0 + 16 * wave + (lane >> 3);
+      const uint32_t sw = 16u * (uint32_t)((lane & 7) ^ (2 * ((lane >> 3) & 3)));
+      const uint32_t ba = (uint32_t)vrow[r] * 256u + sw, bb = (uint32_t)vrow[r + 8] * 256u + sw;
+      lds_dma_b128<0>(rsv, ba, lb);
+      lds_dma_b128<1024>(rsv, ba + 128, lb);
+      lds_dma_b128<2048>(rsv, bb, lb);
+      lds_dma_b128<3072>(rsv, bb + 128, lb);
       return;
     }
     const uint32_t base = (uint32_t)key0 * (uint32_t)row_bytes + v_lane;
@@ -364,21 +380,27 @@ void attn_fwd_kernel(Params p) {
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
   const float c = p.scale_log2;
 
+  // Bias of biased tile j (approximate branch): the virtual-key bias array
+  // at the tile's first summary index, or the key-bias ring slot, or zeros.
+  const float *vbp = reinterpret_cast<const float *>(smem + kVbOff);
+  const float *sink_b0 = kbias != nullptr ? reinterpret_cast<const float *>(smem + kBOff) : vbp + kMaxRouteBlocks;
+  const int sink_step = kbias != nullptr ? 64 : 0;   // floats between the two ring slots
+  auto bias_src = [&](int j, int vs, int key0) -> const float * {
+    return is_virt(j) ? vbp + key0 : sink_b0 + vs * sink_step;
+  };
+
   // One pipeline step on tile j (scores in s_cur, V in slot VS) that also
-  // computes S(j+1) into s_nxt from K slot VS^1 when DO_QK.  A VIRT tile
-  // (approximate branch) takes its logit bias from the virtual-key bias
-  // array at its first summary index key0.
-  auto step = [&](auto vs_c, auto biased_c, auto masked_c, auto do_qk_c, auto virt_c,
-                  f32x16 &s_cur, f32x16 &s_nxt, int key0) {
+  // computes S(j+1) into s_nxt from K slot VS^1 when DO_QK.  With the
+  // approximate branch a biased step reads its bias at bsel.
+  auto step = [&](auto vs_c, auto biased_c, auto masked_c, auto do_qk_c, f32x16 &s_cur,
+                  f32x16 &s_nxt, int key0, const float *bsel) {
     constexpr int VS = decltype(vs_c)::value;
     constexpr bool BIASED = decltype(biased_c)::value;
     constexpr bool MASKED = decltype(masked_c)::value;
     constexpr bool DO_QK = decltype(do_qk_c)::value;
-    constexpr bool VIRT = decltype(virt_c)::value;
     const unsigned char *vbuf = smem + kVOff + VS * 16384;
     const unsigned char *kbuf = smem + kKOff + (VS ^ 1) * 16384;
-    const float *bs = VIRT ? reinterpret_cast<const float *>(smem + kVbOff) + key0
-                           : reinterpret_cast<const float *>(smem + kBOff + VS * 256);
+    const float *bs = kSpark ? bsel : reinterpret_cast<const float *>(smem + kBOff + VS * 256);
 
     // S(j+1) MFMAs, issued in two groups so that they overlap the max phase
     // and the exponential phase of tile j.  Their K fragments are read from
@@ -512,36 +534,62 @@ void attn_fwd_kernel(Params p) {
   // K(j) lives in K slot j%2 and V(j) in V slot j%2; K is fetched two tiles
   // ahead, V one ahead.  Step j issues V(j+1) and K(j+2) into the slots that
   // step j-1 finished reading, and ends with the barrier that publishes them.
+  // Virtual keys: the video blocks the list skips, ascending.  A byte flag
+  // per video block marks the list's blocks (the first 64 entries are
+  // already in list_v); then every wave walks all 64-block chunks, packs the
+  // unflagged blocks by ballot and writes the chunks c = wave mod 4: summary
+  // row and log-mass bias at the packed position, -inf bias past the last
+  // one.  The zero bias of unbiased sink tiles follows the bias array.
+  // Built after the first tile loads are issued unless those tiles are
+  // virtual themselves.
+  auto build_virtual = [&]() {
+    float *vb = reinterpret_cast<float *>(smem + kVbOff);
+    int *vr = reinterpret_cast<int *>(smem + kVrowOff);
+    unsigned char *fl = smem + kVflagOff;
+    const float *lmp = p.sum_lm + (int64_t)bh * p.nb;
+    for (int x = tid; 4 * x < p.nvb; x += kThreads) reinterpret_cast<uint32_t *>(fl)[x] = 0u;
+    __syncthreads();
+    for (int cb = 64 * wave; cb < t_end; cb += kThreads) {
+      const int e = cb == 0 ? list_v : (cb + lane < t_end ? list[cb + lane] : -1);
+      if (cb + lane < t_end && e >= 0 && e < p.nvb) fl[e] = 1;
+    }
+    __syncthreads();
+    int base = 0;
+    for (int c = 0; c * kBlock < p.nvb; ++c) {
+      const int x = kBlock * c + lane;
+      const bool skip = x < p.nvb && fl[x] == 0;
+      const uint64_t m = __ballot(skip);
+      if ((c & 3) == wave && skip) {
+        const int pos = base + __popcll(m & ((1ull << lane) - 1ull));
+        vr[pos] = x;
+        vb[pos] = lmp[x];
+      }
+      base += __popcll(m);
+    }
+    for (int x = base + tid; x < nv * kBlock; x += kThreads) {
+      vr[x] = 0;
+      vb[x] = -INFINITY;
+    }
+    if (tid < kBlock) vb[kMaxRouteBlocks + tid] = 0.f;
+  };
+  const bool virt_first = is_virt(0) || is_virt(1);
+  if (kSpark && virt_first) {
+    build_virtual();
+    __syncthreads();
+  }
+
   f32x16 s0, s1;
   int k_cur = 0, k_nxt = 0;
   if (nt > 0) {
     k_cur = tile_key0(0);
-    issue_k(k_cur, 0, 0 < nv);
-    issue_v(k_cur, 0, 0 < nv);
+    issue_k(k_cur, 0, is_virt(0));
+    issue_v(k_cur, 0, is_virt(0));
     if (nt > 1) {
       k_nxt = tile_key0(1);
-      issue_k(k_nxt, 1, 1 < nv);
+      issue_k(k_nxt, 1, is_virt(1));
     }
   }
-  if (kSpark && nv > 0) {
-    // Virtual-key bias: lm of every video block the list skips, -inf for
-    // the blocks it holds exactly and for indices past nvb.  Wave w fills
-    // virtual tiles w, w+4, ...: lane x tests its block against every list
-    // entry (the first 64 are already in list_v) and the barrier that ends
-    // the prologue publishes the array.
-    float *vb = reinterpret_cast<float *>(smem + kVbOff);
-    const float *lmp = p.sum_lm + (int64_t)bh * p.nb;
-    for (int vt = __builtin_amdgcn_readfirstlane(wave); vt < nv; vt += kThreads / 64) {
-      const int x = kBlock * vt + lane;
-      bool exact = false;
-      for (int cb = 0; cb < t_end; cb += 64) {
-        const int chunk = cb == 0 ? list_v : (cb + lane < t_end ? list[cb + lane] : -1);
-        const int ne = t_end - cb < 64 ? t_end - cb : 64;
-        for (int ei = 0; ei < ne; ++ei) exact |= __builtin_amdgcn_readlane(chunk, ei) == x;
-      }
-      vb[x] = (x < p.nvb && !exact) ? lmp[x] : -INFINITY;
-    }
-  }
+  if (kSpark && !virt_first) build_virtual();  // published by the barrier below
   __builtin_amdgcn_s_waitcnt(kVmcntZero);
   __syncthreads();
   if (nt > 0) {
@@ -558,73 +606,58 @@ void attn_fwd_kernel(Params p) {
 
   // Steady-state step j < n-1 (S(j+1) computed); the last step is peeled and
   // is the only one that masks keys past T.
-  auto run_step = [&](auto vs_c, auto biased, auto virt, f32x16 &s_cur, f32x16 &s_nxt, int j) {
+  auto run_step = [&](auto vs_c, auto biased, f32x16 &s_cur, f32x16 &s_nxt, int j) {
+    constexpr int VS = decltype(vs_c)::value;
     const int key_j = k_cur;
-    issue_v(k_nxt, decltype(vs_c)::value ^ 1, j + 1 < nv);
+    issue_v(k_nxt, VS ^ 1, is_virt(j + 1));
     int k_nn = 0;
     if (j + 2 < nt) {
       k_nn = tile_key0(j + 2);
-      issue_k(k_nn, decltype(vs_c)::value, j + 2 < nv);
+      issue_k(k_nn, VS, is_virt(j + 2));
     }
-    step(vs_c, biased, Bool<false>{}, Bool<true>{}, virt, s_cur, s_nxt, key_j);
+    const float *bsel = kSpark ? bias_src(j, VS, key_j) : nullptr;
+    step(vs_c, biased, Bool<false>{}, Bool<true>{}, s_cur, s_nxt, key_j, bsel);
     k_cur = k_nxt;
     k_nxt = k_nn;
     __builtin_amdgcn_s_waitcnt(kVmcntZero);
     __syncthreads();
   };
   auto last_step = [&](auto vs_c, f32x16 &s_cur, f32x16 &s_nxt) {
+    constexpr int VS = decltype(vs_c)::value;
     const int key_j = k_cur;
-    if (kSpark && nt - 1 < nv) {  // no exact tile at all: the last one is virtual
-      step(vs_c, Bool<true>{}, Bool<false>{}, Bool<false>{}, Bool<true>{}, s_cur, s_nxt, key_j);
-      __syncthreads();
-      return;
-    }
-    const bool masked = key_j + kBlock > T;
+    const bool masked = !is_virt(nt - 1) && key_j + kBlock > T;
+    const float *bsel = kSpark ? bias_src(nt - 1, VS, key_j) : nullptr;
     if (nt - 1 >= np_end) {
-      if (masked) step(vs_c, Bool<true>{}, Bool<true>{}, Bool<false>{}, Bool<false>{}, s_cur, s_nxt, key_j);
-      else step(vs_c, Bool<true>{}, Bool<false>{}, Bool<false>{}, Bool<false>{}, s_cur, s_nxt, key_j);
+      if (masked) step(vs_c, Bool<true>{}, Bool<true>{}, Bool<false>{}, s_cur, s_nxt, key_j, bsel);
+      else step(vs_c, Bool<true>{}, Bool<false>{}, Bool<false>{}, s_cur, s_nxt, key_j, bsel);
     } else {
-      if (masked) step(vs_c, Bool<false>{}, Bool<true>{}, Bool<false>{}, Bool<false>{}, s_cur, s_nxt, key_j);
-      else step(vs_c, Bool<false>{}, Bool<false>{}, Bool<false>{}, Bool<false>{}, s_cur, s_nxt, key_j);
+      if (masked) step(vs_c, Bool<false>{}, Bool<true>{}, Bool<false>{}, s_cur, s_nxt, key_j, bsel);
+      else step(vs_c, Bool<false>{}, Bool<false>{}, Bool<false>{}, s_cur, s_nxt, key_j, bsel);
     }
     __syncthreads();
   };
-  // Steps j < n_plain are unbiased and the rest biased.  Each loop body holds
+  // Steps j < np_end are unbiased and the rest biased.  Each loop body holds
   // one step variant only: a runtime choice between the two inside a loop
   // makes the compiler route the O accumulators through copies every step.
-  // Any tile kind, chosen at run time (phase transitions only).
-  auto run_any = [&](auto vs_c, f32x16 &s_cur, f32x16 &s_nxt, int j) {
-    if (kSpark && j < nv) run_step(vs_c, Bool<true>{}, Bool<true>{}, s_cur, s_nxt, j);
-    else if (j < np_end) run_step(vs_c, Bool<false>{}, Bool<false>{}, s_cur, s_nxt, j);
-    else run_step(vs_c, Bool<true>{}, Bool<false>{}, s_cur, s_nxt, j);
-  };
   int j = 0;
-  if (kSpark) {
-    for (; j + 2 < nt && j + 2 <= nv; j += 2) {
-      run_step(Int<0>{}, Bool<true>{}, Bool<true>{}, s0, s1, j);
-      run_step(Int<1>{}, Bool<true>{}, Bool<true>{}, s1, s0, j + 1);
-    }
-    if (j + 2 < nt && j < nv) {  // j + 1 == nv
-      run_any(Int<0>{}, s0, s1, j);
-      run_any(Int<1>{}, s1, s0, j + 1);
-      j += 2;
-    }
-  }
   for (; j + 2 < nt && j + 2 <= np_end; j += 2) {
-    run_step(Int<0>{}, Bool<false>{}, Bool<false>{}, s0, s1, j);
-    run_step(Int<1>{}, Bool<false>{}, Bool<false>{}, s1, s0, j + 1);
+    run_step(Int<0>{}, Bool<false>{}, s0, s1, j);
+    run_step(Int<1>{}, Bool<false>{}, s1, s0, j + 1);
   }
-  if (j + 2 < nt && j < np_end) {  // j + 1 == np_end (and j >= nv)
-    run_step(Int<0>{}, Bool<false>{}, Bool<false>{}, s0, s1, j);
-    run_step(Int<1>{}, Bool<true>{}, Bool<false>{}, s1, s0, j + 1);
+  if (j + 2 < nt && j < np_end) {  // j + 1 == np_end
+    run_step(Int<0>{}, Bool<false>{}, s0, s1, j);
+    run_step(Int<1>{}, Bool<true>{}, s1, s0, j + 1);
     j += 2;
   }
   for (; j + 2 < nt; j += 2) {
-    run_step(Int<0>{}, Bool<true>{}, Bool<false>{}, s0, s1, j);
-    run_step(Int<1>{}, Bool<true>{}, Bool<false>{}, s1, s0, j + 1);
+    run_step(Int<0>{}, Bool<true>{}, s0, s1, j);
+    run_step(Int<1>{}, Bool<true>{}, s1, s0, j + 1);
   }
   if (j + 1 < nt) {
-    run_any(Int<0>{}, s0, s1, j);
+    if (j >= np_end)
+      run_step(Int<0>{}, Bool<true>{}, s0, s1, j);
+    else
+      run_step(Int<0>{}, Bool<false>{}, s0, s1, j);
     last_step(Int<1>{}, s1, s0);
   } else if (j < nt) {
     last_step(Int<0>{}, s0, s1);
@@ -783,7 +816,6 @@ Params make_params(const AttnArgs &a, int qb0, int nqb) {
   p.sum_k = static_cast<const uint16_t *>(a.sum_k);
   p.sum_v = static_cast<const uint16_t *>(a.sum_v);
   p.sum_lm = a.sum_lm;
-  p.nvt = 0;
   return p;
 }
 
@@ -824,7 +856,6 @@ hipError_t launch_attn_sparse_spark(const AttnArgs &a, hipStream_t stream) {
     return hipErrorInvalidValue;
   Params p = make_params(a, 0, a.nvq);
   p.row_hi = a.rows_end;
-  p.nvt = (a.nvb + kBlock - 1) / kBlock;
   const int total = a.B * a.H * a.nvq;
   hipLaunchKernelGGL((attn_fwd_kernel<false, true>), dim3(total), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
