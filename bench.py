@@ -17,7 +17,12 @@ on one stream with events between them: the per-stage times, the
 attention-only rate and the sparse kernel's roofline come from that pass,
 so each kernel is timed alone.
 
-A third measurement (``spark`` in the JSON line, skipped by ``--no-spark``)
+A third measurement (``fused_route``, skipped by ``--no-fused``) times the
+call with the Top-K selection inside the attention kernel (pool, fused
+sparse rows, dense rows, one stream) and reports whether its lists equal the
+route kernel's.
+
+A fourth measurement (``spark`` in the JSON line, skipped by ``--no-spark``)
 times the Spark variant of the same call on the same inputs: global anchor,
 virtual summaries, route, sparse rows with one virtual key per skipped video
 block, dense rows, back to back on one stream with events between the
@@ -61,6 +66,49 @@ def effective_flops_from_lists(cnt, idx, T, nvb, H, B):
                 sparse_pairs += 64 * int(keys_in_block[idx[b, h, i, :cnt[b, h, i]]].sum())
     dense_pairs = B * H * (T - 64 * nvb) * T
     return 4 * 128 * sparse_pairs, 4 * 128 * dense_pairs
+
+
+def fused_measure(sa, wl, q, k, v, kb, idx, cnt, out, dws, steps, sparse_flops):
+    """Per-stage and whole-call times with the route inside the attention
+    kernel (pool, fused sparse rows, dense rows; one stream), and whether its
+    lists equal the route kernel's."""
+    ss = wl.sink_start
+    ws = sa.sparse_attn_pool(q, k, ss)
+    _, (fidx, fcnt) = sa.sparse_attn_fwd_fused(q, k, v, ss, wl.topk_ratio, wl.local_radius, ws,
+                                               key_bias=kb, out=out, return_route=True)
+    torch.cuda.synchronize()
+    same_lists = bool(torch.equal(fidx, idx) and torch.equal(fcnt, cnt))
+    stream = torch.cuda.current_stream(q.device)
+    stages = [
+        ("pool", lambda: sa.sparse_attn_pool(q, k, ss, workspace=ws)),
+        ("sparse_fwd_fused", lambda: sa.sparse_attn_fwd_fused(q, k, v, ss, wl.topk_ratio, wl.local_radius,
+                                                              ws, key_bias=kb, out=out)),
+        ("dense_fwd", lambda: sa.dense_sink_fwd(q, k, v, ss, key_bias=kb, out=out, workspace=dws)),
+    ]
+    for _ in range(3):
+        for _, fn in stages:
+            fn()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(steps)]
+    for i in range(steps):
+        evs[i][0].record(stream)
+        for j, (_, fn) in enumerate(stages):
+            fn()
+            evs[i][j + 1].record(stream)
+    torch.cuda.synchronize()
+    st = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(len(stages))] for e in evs])
+    call = np.array([e[0].elapsed_time(e[-1]) for e in evs])
+    med = np.median(st, axis=0)
+    names = [n for n, _ in stages]
+    f_ms = float(st[:, names.index("sparse_fwd_fused")].mean())
+    return {
+        "path": "pool + sparse rows with the Top-K selected inside the attention kernel + dense rows, "
+                "one stream",
+        "ms_per_call_median": round(float(np.median(call)), 4),
+        "stages_ms_median": {n: round(float(x), 4) for n, x in zip(names, med)},
+        "lists_equal_route_kernel": same_lists,
+        "sparse_fwd_fused_tflops": round(sparse_flops / (f_ms * 1e-3) / 1e12, 3),
+    }
 
 
 def spark_measure(sa, wl, q, k, v, kb, idx, cnt, ws, out, dws, steps, sparse_flops, dense_flops):
@@ -175,6 +223,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-spark", action="store_true",
                     help="skip the Spark approximate-branch measurement")
+    ap.add_argument("--no-fused", action="store_true",
+                    help="skip the fused-route measurement")
     ap.add_argument("--one-stream", action="store_true",
                     help="run the dense rows after the sparse rows on one stream")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -317,6 +367,9 @@ def main():
                      "launch_ms_mean": round(sparse_ms, 4),
                      "traffic": traffic_for_current_kernel()},
     }
+    if not args.no_fused:
+        res["fused_route"] = fused_measure(sa, wl, q, k, v, kb, idx, cnt, out, dws, args.steps,
+                                           sparse_flops)
     if not args.no_spark:
         res["spark"] = spark_measure(sa, wl, q, k, v, kb, idx, cnt, ws, out, dws, args.steps,
                                      sparse_flops, dense_flops)

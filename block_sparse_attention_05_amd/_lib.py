@@ -46,6 +46,11 @@ SIGNATURES = {
     "dense_sink_fwd": (ctypes.c_int, [
         _vp, _vp, _vp, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32,
         _vp, _c_int64, _c_float, _vp, _vp, _vp, _c_size, _vp]),
+    "sparse_attn_pool": (ctypes.c_int, [
+        _vp, _vp, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32, _vp, _c_size, _vp]),
+    "sparse_attn_fwd_fused": (ctypes.c_int, [
+        _vp, _vp, _vp, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32,
+        _c_float, _c_int32, _vp, _c_int64, _vp, _c_size, _c_float, _vp, _vp, _vp, _c_int32, _vp, _vp]),
     "sa_anchor_workspace_bytes": (_c_size, [_c_int32, _c_int32, _c_int32, _c_int32]),
     "spark_global_anchor": (ctypes.c_int, [
         _vp, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32, _vp, _vp, _c_size, _vp]),
@@ -445,4 +450,79 @@ def routed_attention_spark(q, k, v, sink_start: int, topk_ratio: float = 0.1, lo
         res.append(lse)
     if return_parts:
         res.append(dict(anchor=anchor, summaries=summaries, block_idx=block_idx, block_cnt=block_cnt))
+    return res[0] if len(res) == 1 else tuple(res)
+
+
+# ---- fused route ------------------------------------------------------------
+
+def sparse_attn_pool(q: torch.Tensor, k: torch.Tensor, sink_start: int, *,
+                     video_tail_mode: str = "dense",
+                     workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Pooled Q and K means into a route workspace (uint8 device tensor,
+    allocated if None), which is returned."""
+    _check_qkv(q, k)
+    B, T, H, D = q.shape
+    mode = _mode(video_tail_mode)
+    n = lib().sa_route_workspace_bytes(B, T, H, sink_start, mode)
+    if workspace is None:
+        workspace = torch.empty(max(n, 16), dtype=torch.uint8, device=q.device)
+    _check(lib().sparse_attn_pool(_ptr(q), _ptr(k), B, T, H, D, sink_start, T - sink_start, mode,
+                                  _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                  _stream(q.device)))
+    return workspace
+
+
+def sparse_attn_fwd_fused(q, k, v, sink_start: int, topk_ratio: float, local_radius: int,
+                          workspace: torch.Tensor, *, video_tail_mode: str = "dense",
+                          key_bias: Optional[torch.Tensor] = None, softmax_scale: float = 0.0,
+                          out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                          return_route: bool = False):
+    """Sparse rows with the route inside the attention kernel, from the
+    pooled means in ``workspace`` (see sparse_attn_pool).  With
+    ``return_route`` the selected lists are returned too."""
+    _check_qkv(q, k, v)
+    B, T, H, D = q.shape
+    mode = _mode(video_tail_mode)
+    if out is None:
+        out = torch.empty_like(q)
+    _check_qkv(q, out)
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != B * H * T):
+        raise ValueError("lse must be contiguous float32 [B,H,T]")
+    if workspace.device != q.device:
+        raise ValueError("workspace must be on the device of q")
+    kb, kb_n = _bias(key_bias, B, T, q.device)
+    idx = cnt = None
+    max_sel = 0
+    if return_route:
+        nvq = lib().sa_num_query_blocks(T, sink_start, mode)
+        max_sel = max(1, lib().sa_max_selected(T, sink_start, mode, topk_ratio, local_radius))
+        idx = torch.empty((B, H, max(nvq, 0), max_sel), dtype=torch.int32, device=q.device)
+        cnt = torch.empty((B, H, max(nvq, 0)), dtype=torch.int32, device=q.device)
+    _check(lib().sparse_attn_fwd_fused(
+        _ptr(q), _ptr(k), _ptr(v), B, T, H, D, sink_start, T - sink_start, mode, float(topk_ratio),
+        int(local_radius), _ptr(kb), kb_n, _ptr(workspace), workspace.numel() * workspace.element_size(),
+        float(softmax_scale), _ptr(out), _ptr(lse), _ptr(idx), int(max_sel), _ptr(cnt), _stream(q.device)))
+    return (out, (idx, cnt)) if return_route else out
+
+
+def routed_attention_fused(q, k, v, sink_start: int, topk_ratio: float = 0.1, local_radius: int = 0, *,
+                           video_tail_mode: str = "dense", key_bias: Optional[torch.Tensor] = None,
+                           softmax_scale: float = 0.0, return_lse: bool = False,
+                           return_route: bool = False):
+    """One call with the route fused into attention: pool, fused sparse rows,
+    dense rows, on the current stream."""
+    ws = sparse_attn_pool(q, k, sink_start, video_tail_mode=video_tail_mode)
+    B, T, H, _ = q.shape
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device) if return_lse else None
+    out = torch.empty_like(q)
+    r = sparse_attn_fwd_fused(q, k, v, sink_start, topk_ratio, local_radius, ws,
+                              video_tail_mode=video_tail_mode, key_bias=key_bias,
+                              softmax_scale=softmax_scale, out=out, lse=lse, return_route=return_route)
+    dense_sink_fwd(q, k, v, sink_start, video_tail_mode=video_tail_mode, key_bias=key_bias,
+                   softmax_scale=softmax_scale, out=out, lse=lse)
+    res = [out]
+    if return_lse:
+        res.append(lse)
+    if return_route:
+        res.append(r[1])
     return res[0] if len(res) == 1 else tuple(res)

@@ -420,4 +420,108 @@ sa_status sparse_attn_fwd_spark(const void *q, const void *k, const void *v, int
   return ok();
 }
 
+// ---- fused route ------------------------------------------------------------
+
+sa_status sparse_attn_pool(const void *q, const void *k, int32_t B, int32_t T, int32_t H, int32_t D,
+                           int32_t sink_start, int32_t sink_tokens, int32_t video_tail_mode,
+                           void *workspace, size_t workspace_bytes, void *stream) {
+  sa_status st = check_shape(B, T, H, D, sink_start, sink_tokens, video_tail_mode);
+  if (st != SA_OK) return st;
+  if ((st = check_bf16(q, "q")) != SA_OK) return st;
+  if ((st = check_bf16(k, "k")) != SA_OK) return st;
+  const Split sp = split_rows(T, sink_start, video_tail_mode);
+  if (sp.nvb > sa::kMaxRouteBlocks)
+    return fail(SA_ERR_UNSUPPORTED, "at most %d video blocks can be routed (got %d)",
+                sa::kMaxRouteBlocks, sp.nvb);
+  if (sp.nvq == 0) return ok();
+  const size_t need_ws = sa_route_workspace_bytes(B, T, H, sink_start, video_tail_mode);
+  if (workspace_bytes < need_ws)
+    return fail(SA_ERR_WORKSPACE, "workspace must hold %zu bytes (got %zu)", need_ws,
+                workspace_bytes);
+  if (workspace == nullptr || !aligned(workspace, 16))
+    return fail(SA_ERR_WORKSPACE, "workspace must be a 16-byte aligned device pointer");
+  double *qbar = static_cast<double *>(workspace);
+  float *kbar = reinterpret_cast<float *>(qbar + (size_t)B * H * (((size_t)sp.nvq + 15) / 16 * 16) * sa::kHeadDim);
+  hipError_t e = sa::launch_pool(q, k, qbar, kbar, B, T, H, sp.nvq, sp.nvb, sp.rows_end,
+                                 static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SA_ERR_HIP, "pool launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+sa_status sparse_attn_fwd_fused(const void *q, const void *k, const void *v, int32_t B, int32_t T,
+                                int32_t H, int32_t D, int32_t sink_start, int32_t sink_tokens,
+                                int32_t video_tail_mode, float topk_ratio, int32_t local_radius,
+                                const float *key_bias, int64_t key_bias_numel,
+                                const void *workspace, size_t workspace_bytes, float softmax_scale,
+                                void *out, float *lse, int32_t *block_idx, int32_t max_sel,
+                                int32_t *block_cnt, void *stream) {
+  sa_status st = check_shape(B, T, H, D, sink_start, sink_tokens, video_tail_mode);
+  if (st != SA_OK) return st;
+  if ((st = check_bf16(q, "q")) != SA_OK) return st;
+  if ((st = check_bf16(k, "k")) != SA_OK) return st;
+  if ((st = check_bf16(v, "v")) != SA_OK) return st;
+  if ((st = check_bf16(out, "out")) != SA_OK) return st;
+  if ((st = check_bias(key_bias, key_bias_numel, B, T)) != SA_OK) return st;
+  float scale_log2 = 0.f;
+  if ((st = check_scale(softmax_scale, &scale_log2)) != SA_OK) return st;
+  if (lse != nullptr && !aligned(lse, 4)) return fail(SA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  if (!(topk_ratio > 0.f && topk_ratio <= 1.f))
+    return fail(SA_ERR_INVALID_ARG, "topk_ratio must lie in (0, 1]");
+  if (local_radius < 0) return fail(SA_ERR_INVALID_ARG, "local_radius must be >= 0");
+  const Split sp = split_rows(T, sink_start, video_tail_mode);
+  if (sp.nvb > sa::kMaxRouteBlocks)
+    return fail(SA_ERR_UNSUPPORTED, "at most %d video blocks can be routed (got %d)",
+                sa::kMaxRouteBlocks, sp.nvb);
+  const int32_t need_sel = sa_max_selected(T, sink_start, video_tail_mode, topk_ratio, local_radius);
+  if ((block_idx == nullptr) != (block_cnt == nullptr))
+    return fail(SA_ERR_INVALID_ARG, "block_idx and block_cnt must both be given or both be NULL");
+  if (block_idx != nullptr) {
+    if (max_sel < need_sel)
+      return fail(SA_ERR_INVALID_ARG, "max_sel must be >= %d (got %d)", need_sel, max_sel);
+    if (!aligned(block_idx, 4) || !aligned(block_cnt, 4))
+      return fail(SA_ERR_INVALID_ARG, "block_idx and block_cnt must be 4-byte aligned");
+  } else {
+    max_sel = need_sel;
+  }
+  if (max_sel > sa::kMaxRouteBlocks)
+    return fail(SA_ERR_UNSUPPORTED, "the fused route holds lists of at most %d blocks (need %d)",
+                sa::kMaxRouteBlocks, max_sel);
+  if (sp.nvq == 0) return ok();
+  const size_t need_ws = sa_route_workspace_bytes(B, T, H, sink_start, video_tail_mode);
+  if (workspace_bytes < need_ws)
+    return fail(SA_ERR_WORKSPACE, "workspace must hold %zu bytes (got %zu)", need_ws,
+                workspace_bytes);
+  if (workspace == nullptr || !aligned(workspace, 16))
+    return fail(SA_ERR_WORKSPACE, "workspace must be a 16-byte aligned device pointer");
+
+  const double *qbar = static_cast<const double *>(workspace);
+  const float *kbar = reinterpret_cast<const float *>(qbar + (size_t)B * H * (((size_t)sp.nvq + 15) / 16 * 16) * sa::kHeadDim);
+  sa::AttnArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.lse = lse;
+  a.key_bias = key_bias;
+  a.B = B;
+  a.T = T;
+  a.H = H;
+  a.nb = sa_num_blocks(T);
+  a.nvb = sp.nvb;
+  a.nvq = sp.nvq;
+  a.rows_end = sp.rows_end;
+  a.max_sel = max_sel;
+  a.scale_log2 = scale_log2;
+  a.qbar = qbar;
+  a.kbar = kbar;
+  a.budget = sa_topk_budget(sp.nvb, topk_ratio);
+  a.radius = local_radius < sp.nvb ? local_radius : sp.nvb;
+  a.list_out = block_idx;
+  a.cnt_out = block_cnt;
+  hipError_t e = sa::launch_attn_sparse_fused(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess)
+    return fail(SA_ERR_HIP, "sparse attention (fused route) launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 }  // extern "C"

@@ -55,6 +55,7 @@
 
 #include "device_util.h"
 #include "kernels.h"
+#include "select.h"
 
 namespace sa {
 namespace {
@@ -88,6 +89,13 @@ constexpr int kVbOff = kLdsBytes;
 constexpr int kVrowOff = kVbOff + kMaxRouteBlocks * 4 + 256;
 constexpr int kVflagOff = kVrowOff + kMaxRouteBlocks * 4;   // one byte per video block
 constexpr int kVbBytes = kMaxRouteBlocks * 9 + 256;
+// Fused route: the query block's pooled mean (128 fp64), its scores
+// against every key block, its list and the list length.
+constexpr int kFqOff = kLdsBytes;
+constexpr int kFsOff = kFqOff + kHeadDim * 8;
+constexpr int kFlOff = kFsOff + kMaxRouteBlocks * 4;
+constexpr int kFnOff = kFlOff + kMaxRouteBlocks * 4;
+constexpr int kFusedBytes = kHeadDim * 8 + kMaxRouteBlocks * 8 + 16;
 
 // sched_group_barrier instruction classes
 constexpr int kSchedVALU = 0x002;
@@ -155,6 +163,12 @@ struct Params {
   // sum_lm + bh*nb
   const uint16_t *sum_k, *sum_v;
   const float *sum_lm;
+  // fused route: pooled means (route workspace layout), budget, radius, and
+  // optional copies of the lists it selects
+  const double *qbar;
+  const float *kbar;
+  int budget, radius;
+  int32_t *list_out, *cnt_out;
 };
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
@@ -162,12 +176,13 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-template <bool kDense, bool kSpark = false>
+template <bool kDense, bool kSpark = false, bool kFused = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_kernel(Params p) {
   // K ring (2 tiles) | V ring (2 tiles) | natural-log key bias ring (2 tiles)
-  // [| virtual-key bias, approximate branch]
-  __shared__ __align__(16) unsigned char smem[kLdsBytes + (kSpark ? kVbBytes : 0)];
+  // [| virtual-key bias, approximate branch] [| fused route]
+  __shared__ __align__(16) unsigned char smem[kLdsBytes + (kSpark ? kVbBytes : 0) +
+                                              (kFused ? kFusedBytes : 0)];
 
   const int total = p.B * p.H * p.nqb * p.nsplit;
   const int w = xcd_remap(blockIdx.x, total);
@@ -211,11 +226,64 @@ void attn_fwd_kernel(Params p) {
     n_plain = pe > t_begin ? pe - t_begin : 0;
   } else {
     const int64_t li = (int64_t)bh * p.nqb + qbi;
-    list = p.block_idx + li * p.max_sel;
-    // The first 64 entries are read together with the count (the two loads
-    // do not depend on each other).
-    const int first = lane < p.max_sel ? list[lane] : 0;
-    const int n = p.block_cnt[li];
+    int first, n;
+    if (kFused) {
+      // Route of this query block inside the workgroup (same rule as the
+      // route kernel): scores s_j = fp32 of the fp64 dot product of the
+      // fp32 means (fp32 products are exact in fp64), then one wavefront
+      // selects and emits the list into LDS.
+      double *qs = reinterpret_cast<double *>(smem + kFqOff);
+      float *sc = reinterpret_cast<float *>(smem + kFsOff);
+      int32_t *lst = reinterpret_cast<int32_t *>(smem + kFlOff);
+      int32_t *lcnt = reinterpret_cast<int32_t *>(smem + kFnOff);
+      const int ntq = (p.nqb + 15) >> 4, ntk = (p.nvb + 15) >> 4;
+      if (tid < kHeadDim / 2) {  // channels 2*tid, 2*tid + 1
+        const double2 w2 = reinterpret_cast<const double2 *>(p.qbar)
+            [(((int64_t)bh * ntq + (qb >> 4)) * 16 + (tid & 15)) * 64 + 16 * (tid >> 4) + (qb & 15)];
+        qs[2 * tid] = w2.x;
+        qs[2 * tid + 1] = w2.y;
+      }
+      __syncthreads();
+      const float4 *kt = reinterpret_cast<const float4 *>(p.kbar) + (int64_t)bh * ntk * 8 * 64;
+      for (int jb = tid; jb < p.nvb; jb += kThreads) {
+        const float4 *kj = kt + (int64_t)(jb >> 4) * 8 * 64 + (jb & 15);
+        double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
+#pragma unroll 8
+        for (int u = 0; u < kHeadDim / 4; ++u) {  // channels 4u .. 4u+3
+          const float4 kv = kj[(u & 7) * 64 + 16 * (u >> 3)];
+          a0 = __builtin_fma(qs[4 * u + 0], (double)kv.x, a0);
+          a1 = __builtin_fma(qs[4 * u + 1], (double)kv.y, a1);
+          a2 = __builtin_fma(qs[4 * u + 2], (double)kv.z, a2);
+          a3 = __builtin_fma(qs[4 * u + 3], (double)kv.w, a3);
+        }
+        sc[jb] = (float)((a0 + a1) + (a2 + a3));
+      }
+      __syncthreads();
+      if (wave == 0) {
+        // slots per lane sized to nvb (the selection loops over all of them)
+        auto sel = [&](auto e_c) {
+          return select_and_emit<decltype(e_c)::value>(sc, qb, p.nvb, p.nb, p.budget, p.radius,
+                                                      p.max_sel, lst, nullptr, lane);
+        };
+        const int c = p.nvb <= 128 ? sel(Int<2>{}) : p.nvb <= 192 ? sel(Int<3>{})
+                    : p.nvb <= 256 ? sel(Int<4>{}) : sel(Int<kMaxRouteBlocks / 64>{});
+        if (lane == 0) *lcnt = c;
+        if (p.list_out != nullptr) {
+          for (int x = lane; x < p.max_sel; x += 64) p.list_out[li * p.max_sel + x] = lst[x];
+          if (lane == 0) p.cnt_out[li] = c;
+        }
+      }
+      __syncthreads();
+      list = lst;
+      first = lane < p.max_sel ? lst[lane] : 0;
+      n = *lcnt;
+    } else {
+      list = p.block_idx + li * p.max_sel;
+      // The first 64 entries are read together with the count (the two
+      // loads do not depend on each other).
+      first = lane < p.max_sel ? list[lane] : 0;
+      n = p.block_cnt[li];
+    }
     t_end = n < 0 ? 0 : (n > p.max_sel ? p.max_sel : n);
     list_v = lane < t_end ? first : 0;
     // entries below nvb come first; count them over all 64-entry chunks
@@ -816,6 +884,12 @@ Params make_params(const AttnArgs &a, int qb0, int nqb) {
   p.sum_k = static_cast<const uint16_t *>(a.sum_k);
   p.sum_v = static_cast<const uint16_t *>(a.sum_v);
   p.sum_lm = a.sum_lm;
+  p.qbar = a.qbar;
+  p.kbar = a.kbar;
+  p.budget = a.budget;
+  p.radius = a.radius;
+  p.list_out = a.list_out;
+  p.cnt_out = a.cnt_out;
   return p;
 }
 
@@ -858,6 +932,18 @@ hipError_t launch_attn_sparse_spark(const AttnArgs &a, hipStream_t stream) {
   p.row_hi = a.rows_end;
   const int total = a.B * a.H * a.nvq;
   hipLaunchKernelGGL((attn_fwd_kernel<false, true>), dim3(total), dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_sparse_fused(const AttnArgs &a, hipStream_t stream) {
+  if (a.nvq <= 0) return hipSuccess;
+  if (a.nvb > kMaxRouteBlocks || a.max_sel > kMaxRouteBlocks || a.qbar == nullptr ||
+      (a.nvb > 0 && a.kbar == nullptr))
+    return hipErrorInvalidValue;
+  Params p = make_params(a, 0, a.nvq);
+  p.row_hi = a.rows_end;
+  const int total = a.B * a.H * a.nvq;
+  hipLaunchKernelGGL((attn_fwd_kernel<false, false, true>), dim3(total), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -38,6 +38,12 @@ struct AttnArgs {
   // approximate branch (nullable): one summary per (b, h, K/V block)
   const void *sum_k, *sum_v;  // bf16 [B, 1, H, nb, 128]
   const float *sum_lm;        // fp32 [B, 1, H, nb], natural log
+  // fused route (nullable): pooled means in the route workspace layout,
+  // Top-K budget and forced radius, optional copies of the lists
+  const double *qbar;
+  const float *kbar;
+  int budget, radius;
+  int32_t *list_out, *cnt_out;
 };
 
 // Sparse rows [0, rows_end) of query blocks [0, nvq) over their block lists.
@@ -45,6 +51,10 @@ hipError_t launch_attn_sparse(const AttnArgs &a, hipStream_t stream);
 // The same plus one virtual key (sum_k, sum_v, additive logit sum_lm) per
 // video block that a row's list skips.  Needs nvb <= kMaxRouteBlocks.
 hipError_t launch_attn_sparse_spark(const AttnArgs &a, hipStream_t stream);
+// Sparse rows with the route fused in: every workgroup scores its query
+// block against the pooled key means and selects its own list (the route
+// kernel's rule), then attends.  Needs nvb, max_sel <= kMaxRouteBlocks.
+hipError_t launch_attn_sparse_fused(const AttnArgs &a, hipStream_t stream);
 // Dense rows [rows_end, T) over all keys.  With a workspace of at least
 // dense_workspace_bytes() the key range of each query block is split over
 // dense_splits() workgroups whose partial results are merged by a second

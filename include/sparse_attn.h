@@ -264,6 +264,59 @@ sa_status dense_sink_fwd(const void *q, const void *k, const void *v,
                          void *workspace, size_t workspace_bytes,
                          void *stream);
 
+/* ---- fused route ------------------------------------------------------------
+ *
+ * Defined by: page "Sol-Attn and Spark for MiniMax-H3", Spark inference
+ * integration (Top-K selected inside each CTA, removing the external cutoff
+ * tensor and pass; the selection is an exact FP32 boundary selection).
+ */
+
+/*
+ * sparse_attn_pool - the pooling step of sparse_attn_route alone: the Q
+ * means of query blocks [0, NVQ) and the K means of blocks [0, NVB), left in
+ * the workspace in the layout sparse_attn_route documents.  Same arguments,
+ * errors and workspace size as sparse_attn_route.  With NVQ == 0 nothing is
+ * enqueued.
+ */
+sa_status sparse_attn_pool(const void *q, const void *k,
+                           int32_t B, int32_t T, int32_t H, int32_t D,
+                           int32_t sink_start, int32_t sink_tokens,
+                           int32_t video_tail_mode,
+                           void *workspace, size_t workspace_bytes,
+                           void *stream);
+
+/*
+ * sparse_attn_fwd_fused - sparse_attn_fwd with the route inside the
+ * attention kernel: every workgroup computes s_ij for its query block i from
+ * the pooled means that sparse_attn_pool left in `workspace` (fp32 of the
+ * fp64 dot product of the fp32 means, summed in a different order than the
+ * route kernel, so a score can differ from it by one ulp at most) and
+ * selects list(i) with the rule of sparse_attn_route, then attends.  Same
+ * output as sparse_attn_route + sparse_attn_fwd up to such one-ulp score
+ * differences, which can only change a selection at a near-tie.
+ *
+ * topk_ratio, local_radius   as for sparse_attn_route.
+ * workspace     the workspace sparse_attn_pool filled (read only).
+ * block_idx, block_cnt  nullable (both or neither): when given, the lists
+ *               are written there too, [B, H, NVQ, max_sel] and [B, H, NVQ],
+ *               in sparse_attn_route's format; max_sel >= sa_max_selected().
+ *               When NULL, max_sel is ignored.
+ * Other arguments as for sparse_attn_fwd.
+ * Errors: SA_ERR_UNSUPPORTED when NVB > 1024 or a list can exceed 1024
+ * blocks (the workgroup keeps the list in LDS).
+ */
+sa_status sparse_attn_fwd_fused(const void *q, const void *k, const void *v,
+                                int32_t B, int32_t T, int32_t H, int32_t D,
+                                int32_t sink_start, int32_t sink_tokens,
+                                int32_t video_tail_mode,
+                                float topk_ratio, int32_t local_radius,
+                                const float *key_bias, int64_t key_bias_numel,
+                                const void *workspace, size_t workspace_bytes,
+                                float softmax_scale,
+                                void *out, float *lse,
+                                int32_t *block_idx, int32_t max_sel, int32_t *block_cnt,
+                                void *stream);
+
 /* ---- Spark virtual summaries and the approximate branch --------------------
  *
  * Defined by: page "Sol-Attn and Spark for MiniMax-H3", Spark primitives (the

@@ -282,3 +282,54 @@ def test_spark_entry_points_reject(L, fn, kw, code, msg):
 
 def test_spark_nothing_to_do_is_ok(L):
     assert _fwd_spark(L, ss=10, st=990, idx=None, cnt=None, ak=None, av=None, lm=None) == 0
+
+
+# ---- fused route ------------------------------------------------------------
+
+def _pool(L, **kw):
+    a = dict(q=FAKE, k=FAKE, B=1, T=1000, H=2, D=128, ss=900, st=100, mode=0, ws=FAKE,
+             ws_bytes=1 << 20, stream=None)
+    a.update(kw)
+    return L.sparse_attn_pool(a["q"], a["k"], a["B"], a["T"], a["H"], a["D"], a["ss"], a["st"],
+                              a["mode"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+def _fused(L, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, B=1, T=1000, H=2, D=128, ss=900, st=100, mode=0, ratio=0.25,
+             radius=1, bias=None, bias_n=0, ws=FAKE, ws_bytes=1 << 20, scale=0.0, out=FAKE, lse=None,
+             idx=None, max_sel=0, cnt=None, stream=None)
+    a.update(kw)
+    return L.sparse_attn_fwd_fused(a["q"], a["k"], a["v"], a["B"], a["T"], a["H"], a["D"], a["ss"],
+                                   a["st"], a["mode"], a["ratio"], a["radius"], a["bias"], a["bias_n"],
+                                   a["ws"], a["ws_bytes"], a["scale"], a["out"], a["lse"], a["idx"],
+                                   a["max_sel"], a["cnt"], a["stream"])
+
+
+FUSED_CASES = [
+    (_pool, dict(D=96), INVALID, "D must be 128"),
+    (_pool, dict(ws_bytes=100), WORKSPACE, "workspace"),
+    (_pool, dict(mode=1, T=930, ss=900, st=30), INVALID, "pad mode needs"),
+    (_pool, dict(T=65600, ss=65600, st=0), UNSUPPORTED, "video blocks"),
+    (_fused, dict(ratio=0.0), INVALID, "topk_ratio"),
+    (_fused, dict(radius=-2), INVALID, "local_radius"),
+    (_fused, dict(idx=FAKE), INVALID, "both be given"),
+    (_fused, dict(idx=FAKE, cnt=FAKE, max_sel=3), INVALID, "max_sel"),
+    (_fused, dict(ws=None), WORKSPACE, "workspace"),
+    (_fused, dict(ws_bytes=64), WORKSPACE, "workspace"),
+    (_fused, dict(out=None), INVALID, "out must not be NULL"),
+    (_fused, dict(T=65600, ss=65600, st=0), UNSUPPORTED, "video blocks"),
+    # 900 video blocks at ratio 1: lists of 900 + 1 blocks fit, 1024 + ... do not
+    (_fused, dict(T=64 * 1100, ss=64 * 1000, st=64 * 100, ratio=1.0), UNSUPPORTED, "at most 1024"),
+]
+
+
+@pytest.mark.parametrize("fn,kw,code,msg", FUSED_CASES,
+                         ids=[f"{f.__name__}-{i}" for i, (f, _, _, _) in enumerate(FUSED_CASES)])
+def test_fused_entry_points_reject(L, fn, kw, code, msg):
+    assert fn(L, **kw) == code
+    assert msg in L.sa_last_error().decode()
+
+
+def test_fused_nothing_to_do_is_ok(L):
+    assert _pool(L, ss=10, st=990, ws=None, ws_bytes=0) == 0
+    assert _fused(L, ss=10, st=990, ws=None, ws_bytes=0) == 0
