@@ -305,6 +305,18 @@ def main():
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
 
+    # per-call distribution of the same schedule: an event pair around every
+    # call (the events sit on the main stream, which joins the side stream)
+    cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for a0, a1 in cev:
+        a0.record(stream)
+        step()
+        a1.record(stream)
+    torch.cuda.synchronize()
+    calls = np.array([a0.elapsed_time(a1) for a0, a1 in cev])
+
     # per-stage timing: the three calls back to back on the main stream, with
     # events between them, so that each kernel is timed alone
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
@@ -349,6 +361,9 @@ def main():
                    "sink_tokens": T - ss, "topk_ratio": wl.topk_ratio, "local_radius": wl.local_radius,
                    "key_bias": kb is not None, "inputs": "smooth-field+noise Q/K, N(0,1) V, seed 2"},
         "ms_per_call": round(ms, 4),
+        "ms_per_call_median_p10_p90": [round(float(np.median(calls)), 4),
+                                       round(float(np.percentile(calls, 10)), 4),
+                                       round(float(np.percentile(calls, 90)), 4)],
         "frac_of_bf16_peak": round(tflops / BF16_PEAK_TFLOPS, 4),
         "effective_gflop": round(total_flops / 1e9, 3),
         "stages_ms_median_one_stream": {"route": round(float(med[0]), 4), "sparse_fwd": round(float(med[1]), 4),

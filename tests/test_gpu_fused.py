@@ -113,3 +113,11 @@ def test_fused_h3_with_bias():
     """Full H3 size: lists against the oracle and the route kernel; outputs
     bit-identical to the unfused call where the lists agree."""
     _fused_vs_unfused(workloads.h3(with_bias=True), "fused_h3_bias", check_oracle_outputs=False)
+
+
+def test_fused_batch2_radius2_pad_with_bias():
+    q, k, v = workloads.random_qkv(2, 1100, 3, seed=17)
+    bias = workloads.sink_key_bias(2, 1100, 1000, seed=18)
+    wl = workloads.Workload("fused_B2", q, k, v, sink_start=1000, topk_ratio=0.3, local_radius=2,
+                            key_bias=bias, tail_mode="pad")
+    _fused_vs_unfused(wl, "fused_B2_pad")

@@ -391,3 +391,12 @@ def test_h3_dense_stream_overlap_bit_identical():
         torch.cuda.synchronize()
         assert torch.equal(out, ref_out)
         assert torch.equal(lse, ref_lse)
+
+
+def test_pad_batch2_radius2_with_bias():
+    # B = 2: both batch elements share sink_start (split at 40 rows of block 15)
+    q, k, v = workloads.random_qkv(2, 1100, 3, seed=17)
+    bias = workloads.sink_key_bias(2, 1100, 1000, seed=18)
+    wl = workloads.Workload("pad_B2_H3_r2", q, k, v, sink_start=1000, topk_ratio=0.3, local_radius=2,
+                            key_bias=bias, tail_mode="pad")
+    _full_parity(wl)

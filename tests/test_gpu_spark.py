@@ -130,10 +130,10 @@ def test_spark_pad_mode():
 
 
 def test_spark_many_virtual_tiles_odd_count():
-    # NVB = 130: three virtual tiles (an odd count), lists of 13 + 1 exact
-    # video blocks, radius 0
-    q, k, v = workloads.random_qkv(1, 64 * 130 + 100, 2, seed=11)
-    _spark_parity(q, k, v, 64 * 130, 0.1, 0, "spark_nvb130")
+    # NVB = 200, budget 10 + the self block: 189 skipped blocks pack into
+    # three virtual tiles (an odd count, the last one partial)
+    q, k, v = workloads.random_qkv(1, 64 * 200 + 100, 2, seed=11)
+    _spark_parity(q, k, v, 64 * 200, 0.05, 0, "spark_nvb200")
 
 
 def test_spark_ratio_one_bit_identical_to_exact():
@@ -188,3 +188,9 @@ def test_spark_h3_sampled():
     le = np.concatenate([x.ravel() for x in lerrs])
     log(f"[spark_h3] sampled out max_abs={e.max():.3e} mean_abs={e.mean():.3e} lse max_abs={le.max():.3e}")
     assert e.max() <= MAX_ABS and e.mean() <= MEAN_ABS and le.max() <= 1e-2
+
+
+def test_spark_batch2_radius2_pad_with_bias():
+    q, k, v = workloads.random_qkv(2, 1100, 3, seed=19)
+    bias = workloads.sink_key_bias(2, 1100, 1000, seed=20)
+    _spark_parity(q, k, v, 1000, 0.3, 2, "spark_B2_pad", key_bias=bias, tail_mode="pad")
