@@ -357,16 +357,19 @@ void attn_fwd_kernel(Params p) {
   // 1 KiB; block 2*kg + hf holds keys 8*kg .. +7 and bytes 128*hf .. +127 of
   // each key row, one 128-byte row per key, in 16-byte pieces (key k' = key%8,
   // chunk c = 0..7) placed with an XOR swizzle:
-  //   K: piece (k', c) at 128*k' + 16*(c ^ k');
+  //   K: piece (k', c) at 128*k' + 16*(c ^ k' ^ (kg & 1));
   //   V: piece (k', c) at 128*k' + 16*(c ^ 2*(k' & 3)).
   // One buffer_load ... lds instruction writes 1 KiB (16 B per lane, in lane
   // order), so each group of 8 lanes fetches the full 128-byte cache line
   // half of one key row (8 lines per instruction).  The swizzles make the
-  // MFMA operand reads conflict-free: each group of 8 lanes of the K
-  // fragment read (8 keys, one chunk) covers all 32 banks, and each 16-lane
-  // group of ds_read_b64_tr_b16 on V (4 keys x 32 B) covers them too.  With
-  // these, the K fragment of MFMA lane l (key 32kh + l%32, channels
-  // 16dc + 8(l/32) .. +7) sits at (k_rd0 ^ 32*(dc%4)) + 1024*(dc/4), and the
+  // MFMA operand reads conflict-free on the 64 four-byte banks: a K fragment
+  // read (ds_read_b128) serves 16 lanes per cycle, 8 keys of an even and 8
+  // of an odd key group; within a group the k' swizzle spreads one chunk of
+  // the 8 keys over half of the banks and the kg parity sends the two groups
+  // to opposite halves.  Each 16-lane group of ds_read_b64_tr_b16 on V
+  // (4 keys x 32 B) covers 32 distinct banks.  With these, the K fragment of
+  // MFMA lane l (key 32kh + l%32, channels 16dc + 8(l/32) .. +7) sits at
+  // (k_rd0 ^ 32*(dc%4)) + 1024*(dc/4), and the
   // ds_read_b64_tr_b16 source of lane l (key 32kh + 16kc + 8u + 4g + r,
   // channels 32dt + 16dh + 4j .. +3; g = l/32, dh = (l/16)%2, r = (l%16)/4,
   // j = l%4) at (v_rd0 ^ 64*(dt%2)) + 4096*kc + 2048*u + 1024*(dt/2).  Wave w loads
@@ -395,15 +398,17 @@ void attn_fwd_kernel(Params p) {
       const uint32_t ba = (uint32_t)vrow[r] * 256u + sw, bb = (uint32_t)vrow[r + 8] * 256u + sw;
       lds_dma_b128<0>(rsk, ba, lb);
       lds_dma_b128<1024>(rsk, ba + 128, lb);
-      lds_dma_b128<2048>(rsk, bb, lb);
-      lds_dma_b128<3072>(rsk, bb + 128, lb);
+      lds_dma_b128<2048>(rsk, bb ^ 16u, lb);
+      lds_dma_b128<3072>(rsk, (bb ^ 16u) + 128, lb);
       return;
     }
     const uint32_t base = (uint32_t)key0 * (uint32_t)row_bytes + k_lane;
     lds_dma_b128<0>(rk, base, lb);
     lds_dma_b128<1024>(rk, base + 128, lb);
-    lds_dma_b128<2048>(rk, base + rows8, lb);
-    lds_dma_b128<3072>(rk, base + rows8 + 128, lb);
+    // odd key group: chunk parity flipped (the chunk term is the only part
+    // of the offset below 256)
+    lds_dma_b128<2048>(rk, (base ^ 16u) + rows8, lb);
+    lds_dma_b128<3072>(rk, (base ^ 16u) + rows8 + 128, lb);
   };
   auto issue_v = [&](int key0, int slot, bool virt) {
     const uint32_t lb = lds0 + kVOff + (uint32_t)(slot * 16384) + wave_lds;
@@ -432,7 +437,8 @@ void attn_fwd_kernel(Params p) {
   uint32_t k_rd0, v_rd0;
   {
     const uint32_t kp = (uint32_t)(c32 & 7);
-    k_rd0 = (uint32_t)(2048 * (4 * kh + (c32 >> 3))) + 128 * kp + 16 * ((uint32_t)g ^ kp);
+    k_rd0 = (uint32_t)(2048 * (4 * kh + (c32 >> 3))) + 128 * kp +
+            16 * ((uint32_t)g ^ kp ^ (uint32_t)((c32 >> 3) & 1));
     const uint32_t r = (uint32_t)((lane & 15) >> 2), dh = (uint32_t)((lane >> 4) & 1), j = (uint32_t)(lane & 3);
     v_rd0 = (uint32_t)(8192 * kh + 512 * g) + 128 * r + 8 * (j & 1) + 16 * ((2 * dh + (j >> 1)) ^ (2 * r));
   }

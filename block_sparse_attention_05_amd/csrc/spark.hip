@@ -66,16 +66,28 @@ __global__ __launch_bounds__(kAnchorThreads) void anchor_partial_kernel(
   }
 }
 
-// anchor[b, 0, h, d] = bf16(fp32(sum / sink_start)).
-__global__ __launch_bounds__(kHeadDim) void anchor_finish_kernel(const double *__restrict__ part,
-                                                                 uint16_t *__restrict__ anchor,
-                                                                 int H, int ntiles, int sink_start) {
-  const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+// anchor[b, 0, h, d] = bf16(fp32(sum / sink_start)).  Thread (part, d) of
+// 256 adds every fourth partial sum of channel d (four independent loads in
+// flight per thread), then the four parts are added in a fixed order; all of
+// these fp64 sums are exact.
+constexpr int kFinishThreads = 4 * kHeadDim;
+__global__ __launch_bounds__(kFinishThreads) void anchor_finish_kernel(const double *__restrict__ part,
+                                                                       uint16_t *__restrict__ anchor,
+                                                                       int H, int ntiles, int sink_start) {
+  __shared__ double red[4][kHeadDim];
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int d = threadIdx.x & (kHeadDim - 1), q4 = threadIdx.x >> 7;
   const double *pp = part + ((int64_t)b * H + h) * ntiles * kHeadDim + d;
   double s = 0.0;
-  for (int t = 0; t < ntiles; ++t) s += pp[(int64_t)t * kHeadDim];
-  const float m = (float)(s / (double)sink_start);
-  anchor[((int64_t)b * H + h) * kHeadDim + d] = bf16_bits(m);
+#pragma unroll 4
+  for (int t = q4; t < ntiles; t += 4) s += pp[(int64_t)t * kHeadDim];
+  red[q4][d] = s;
+  __syncthreads();
+  if (q4 == 0) {
+    const double tot = (red[0][d] + red[1][d]) + (red[2][d] + red[3][d]);
+    const float m = (float)(tot / (double)sink_start);
+    anchor[((int64_t)b * H + h) * kHeadDim + d] = bf16_bits(m);
+  }
 }
 
 // One wavefront per (b, anchor p, h, K/V block j).  Lane (r0, c) =
@@ -233,7 +245,7 @@ hipError_t launch_anchor(const void *q, void *workspace, void *anchor, int B, in
                      static_cast<const uint4 *>(q), part, T, H, sink_start);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(anchor_finish_kernel, dim3(H, B), dim3(kHeadDim), 0, stream, part,
+  hipLaunchKernelGGL(anchor_finish_kernel, dim3(H, B), dim3(kFinishThreads), 0, stream, part,
                      static_cast<uint16_t *>(anchor), H, tiles, sink_start);
   return hipGetLastError();
 }
