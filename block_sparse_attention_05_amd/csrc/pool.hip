@@ -56,9 +56,16 @@ __global__ __launch_bounds__(kPoolThreads) void pool_means_kernel(
     acc[6] += (double)bf16_lo(w.w);
     acc[7] += (double)bf16_hi(w.w);
   };
-  if (rows == kBlock) {
-#pragma unroll 16
-    for (int t = 0; t < kBlock; ++t) add(src[(int64_t)t * chunks]);
+  if (rows == kBlock) {  // two batches of 32 loads in flight
+    uint4 w[32];
+#pragma unroll
+    for (int t = 0; t < 32; ++t) w[t] = src[(int64_t)t * chunks];
+#pragma unroll
+    for (int t = 0; t < 32; ++t) add(w[t]);
+#pragma unroll
+    for (int t = 0; t < 32; ++t) w[t] = src[(int64_t)(t + 32) * chunks];
+#pragma unroll
+    for (int t = 0; t < 32; ++t) add(w[t]);
   } else {
     for (int t = 0; t < rows; ++t) add(src[(int64_t)t * chunks]);
   }
