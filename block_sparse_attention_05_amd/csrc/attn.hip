@@ -905,13 +905,28 @@ int dense_splits(int B, int H, int nb, int nvb) {
   const int nq = nb - nvb;
   if (nq <= 0) return 1;
   const int64_t units = (int64_t)B * H * nq;
-  constexpr int64_t kTargetWorkgroups = 1024;   // ~4 per CU
-  int s = (int)((kTargetWorkgroups + units - 1) / units);
-  const int max_s = nb / 8 > 1 ? nb / 8 : 1;   // at least 8 tiles per split
-  s = s < 1 ? 1 : (s > max_s ? max_s : s);
-  // equalise tiles per split
-  const int per = (nb + s - 1) / s;
-  return (nb + per - 1) / per;
+  // Choose the key split that minimises (rounds of resident workgroups) x
+  // (tiles per split + the fixed cost of a workgroup, about 8 tile steps:
+  // prologue, merge, partial-result stores).  Two workgroups fit a CU and
+  // the device has 256 CUs.  Splits keep at least 8 tiles each; among equal
+  // costs the fewer splits win (less partial traffic for the combine).
+  constexpr int64_t kSlots = 2 * 256;
+  constexpr int64_t kFixedTiles = 8;
+  const int max_s = nb / 8 > 1 ? nb / 8 : 1;
+  int best = 1;
+  int64_t best_cost = -1;
+  for (int s = 1; s <= max_s; ++s) {
+    const int per = (nb + s - 1) / s;
+    const int se = (nb + per - 1) / per;          // splits after equalising
+    if (se != s) continue;
+    const int64_t rounds = (units * se + kSlots - 1) / kSlots;
+    const int64_t cost = rounds * (per + kFixedTiles);
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      best = se;
+    }
+  }
+  return best;
 }
 
 size_t dense_workspace_bytes(int B, int H, int nb, int nvb) {

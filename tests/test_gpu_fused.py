@@ -121,3 +121,10 @@ def test_fused_batch2_radius2_pad_with_bias():
     wl = workloads.Workload("fused_B2", q, k, v, sink_start=1000, topk_ratio=0.3, local_radius=2,
                             key_bias=bias, tail_mode="pad")
     _fused_vs_unfused(wl, "fused_B2_pad")
+
+
+def test_fused_max_route_blocks():
+    """NVB = 1024: 1024 scores per workgroup and lists of 110 entries; lists
+    against the oracle and the route kernel, outputs bit-identical to the
+    unfused call where the lists agree."""
+    _fused_vs_unfused(workloads.max_blocks(), "fused_maxblocks", check_oracle_outputs=False)

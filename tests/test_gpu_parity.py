@@ -367,6 +367,12 @@ def test_long_sampled():
     _sampled_parity(workloads.long(), n_blocks=32, dense_heads=2, seed=2)
 
 
+def test_max_route_blocks_sampled():
+    """NVB = 1024 (the widest route row): every list against the oracle,
+    lists of 110 entries walked in two chunks, sampled outputs."""
+    _sampled_parity(workloads.max_blocks(), n_blocks=24, dense_heads=1, seed=3)
+
+
 def test_h3_deterministic_repeat():
     """Full-size call repeated: outputs, LSE and lists must be bit-identical
     (catches races between tile loads and LDS reads)."""

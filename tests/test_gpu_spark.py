@@ -157,8 +157,17 @@ def test_spark_ratio_one_bit_identical_to_exact():
 def test_spark_h3_sampled():
     """Full H3 size: summaries of three heads and 32 sampled query blocks
     against the oracle."""
+    _spark_sampled(workloads.h3(with_bias=True), [0, 17, 55], "spark_h3")
+
+
+def test_spark_max_route_blocks_sampled():
+    """NVB = 1024: about 918 skipped blocks per row packed into 15 virtual
+    tiles, lists of 110 entries; summaries and 24 sampled query blocks."""
+    _spark_sampled(workloads.max_blocks(), [0, 1], "spark_maxblocks", n_blocks=24)
+
+
+def _spark_sampled(wl, heads, name, n_blocks=32):
     import block_sparse_attention_05_amd as sa
-    wl = workloads.h3(with_bias=True)
     q, k, v, kb = wl.q.cuda(), wl.k.cuda(), wl.v.cuda(), wl.key_bias.cuda()
     ss = wl.sink_start
     out, lse, parts = sa.routed_attention_spark(q, k, v, ss, wl.topk_ratio, wl.local_radius, key_bias=kb,
@@ -168,7 +177,7 @@ def test_spark_h3_sampled():
     assert np.array_equal(to_np(anchor).view(np.uint32),
                           osp.global_anchor(to_np(wl.q), ss).view(np.uint32))
     ak, av, lm = (x.cpu() for x in parts["summaries"])
-    _check_summaries(ak, av, lm, anchor, wl.k, wl.v, [0, 17, 55], "spark_h3")
+    _check_summaries(ak, av, lm, anchor, wl.k, wl.v, heads, name)
     qn, kn, vn = to_np(wl.q), to_np(wl.k), to_np(wl.v)
     got = to_np(out)
     glse = lse.cpu().numpy()
@@ -177,8 +186,9 @@ def test_spark_h3_sampled():
     akn, avn, lmn = to_np(ak), to_np(av), lm.numpy().astype(np.float64)
     errs, lerrs = [], []
     nvb = ss // 64
-    for _ in range(32):
-        h, i = int(rng.integers(56)), int(rng.integers(nvb))
+    H = wl.q.shape[2]
+    for _ in range(n_blocks):
+        h, i = int(rng.integers(H)), int(rng.integers(nvb))
         blocks = idx[0, h, i, :cnt[0, h, i]].tolist()
         o, l = osp.approx_block_output(qn, kn, vn, 0, h, i, blocks, akn, avn, lmn,
                                        wl.key_bias.numpy(), nvb)
@@ -186,7 +196,7 @@ def test_spark_h3_sampled():
         lerrs.append(np.abs(glse[0, h, 64 * i:64 * i + 64] - l))
     e = np.concatenate([x.ravel() for x in errs])
     le = np.concatenate([x.ravel() for x in lerrs])
-    log(f"[spark_h3] sampled out max_abs={e.max():.3e} mean_abs={e.mean():.3e} lse max_abs={le.max():.3e}")
+    log(f"[{name}] sampled out max_abs={e.max():.3e} mean_abs={e.mean():.3e} lse max_abs={le.max():.3e}")
     assert e.max() <= MAX_ABS and e.mean() <= MEAN_ABS and le.max() <= 1e-2
 
 

@@ -138,6 +138,17 @@ def long():
                     topk_ratio=0.1, local_radius=1)
 
 
+def max_blocks():
+    """The widest routing the library accepts: 1024 video blocks (64 frames
+    of 32 x 32 tokens) and 200 context tokens, two heads, ratio 0.1 with
+    radius 1 and key_bias.  Lists hold 103 + 3 + 4 = 110 entries, so the
+    attention kernel walks them in two 64-entry chunks."""
+    q, k, v, tv = video_qkv(B=1, H=2, frames=64, ctx_tokens=200, seed=30)
+    bias = sink_key_bias(1, q.shape[1], tv, seed=31)
+    return Workload("maxblocks_B1_H2_T65736_keybias", q, k, v, sink_start=tv, topk_ratio=0.1,
+                    local_radius=1, key_bias=bias)
+
+
 def h3_heads(H, seed=2, with_bias=False):
     """H3 sequence shape (9 x 32 x 32 video + 289 context) with fewer heads."""
     q, k, v, tv = video_qkv(B=1, H=H, frames=9, ctx_tokens=289, seed=seed)
@@ -147,4 +158,4 @@ def h3_heads(H, seed=2, with_bias=False):
 
 
 NAMED = {"tiny": tiny, "mid": mid, "h3": h3,
-         "h3_bias": lambda: h3(with_bias=True), "long": long}
+         "h3_bias": lambda: h3(with_bias=True), "long": long, "max_blocks": max_blocks}
