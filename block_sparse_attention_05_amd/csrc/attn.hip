@@ -551,6 +551,10 @@ void attn_fwd_kernel(Params p) {
     const float m_sub = (m_used == -INFINITY) ? 0.f : m_used;
 
     // -- block B: P of tile j (+ remaining S(j+1) MFMAs) --
+    // The exponential and PV phases run at raised wave priority: when the
+    // other workgroup's wave on this SIMD is in its max phase, issuing copies
+    // or waiting at its barrier, this wave's VALU and MFMA work goes first.
+    __builtin_amdgcn_s_setprio(1);
     if (DO_QK) qk_part(Int<3>{}, Int<8>{});
     bf16x8 pf[2];
 #pragma unroll
@@ -602,6 +606,7 @@ void attn_fwd_kernel(Params p) {
         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kc], o[dt], 0, 0, 0);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // ---- pipeline -----------------------------------------------------------

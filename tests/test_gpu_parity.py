@@ -399,6 +399,54 @@ def test_h3_dense_stream_overlap_bit_identical():
         assert torch.equal(lse, ref_lse)
 
 
+def test_h3_graph_capture_replays_match_eager():
+    """The whole call (route, sparse rows, dense rows on a forked stream)
+    captured in one HIP graph.  The library records no memset and allocates
+    nothing, so every replay must give the eager call's bits; the outputs are
+    cleared by eager kernels, with synchronisations, between replays."""
+    import block_sparse_attention_05_amd as sa
+    wl = workloads.h3(with_bias=True)
+    dev = torch.device("cuda:0")
+    q, k, v, kb = (x.to(dev) for x in (wl.q, wl.k, wl.v, wl.key_bias))
+    B, T, H, _ = q.shape
+    ss, ratio, radius = wl.sink_start, wl.topk_ratio, wl.local_radius
+    nvb = sa.sa_num_sparse_blocks(T, ss)
+    max_sel = sa.sa_max_selected(T, ss, ratio, radius)
+    idx = torch.empty((B, H, nvb, max_sel), dtype=torch.int32, device=dev)
+    cnt = torch.empty((B, H, nvb), dtype=torch.int32, device=dev)
+    ws = torch.empty(sa.sa_route_workspace_bytes(B, T, H, ss), dtype=torch.uint8, device=dev)
+    dws = torch.empty(sa.sa_dense_workspace_bytes(B, T, H, ss), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+    side = torch.cuda.Stream(dev)
+
+    def call():
+        cur = torch.cuda.current_stream(dev)
+        side.wait_stream(cur)
+        sa.sparse_attn_route(q, k, ss, ratio, radius, block_idx=idx, block_cnt=cnt, workspace=ws)
+        with torch.cuda.stream(side):
+            sa.dense_sink_fwd(q, k, v, ss, key_bias=kb, out=out, lse=lse, workspace=dws)
+        sa.sparse_attn_fwd(q, k, v, ss, idx, cnt, key_bias=kb, out=out, lse=lse)
+        cur.wait_stream(side)
+
+    call()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (out, lse, idx, cnt)]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for t in (out, lse, idx, cnt):
+            t.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, got, want in zip(("out", "lse", "idx", "cnt"), (out, lse, idx, cnt), ref):
+            assert torch.equal(got, want), (rep, name)
+        log(f"[graph] replay {rep} equals the eager call")
+
+
 def test_pad_batch2_radius2_with_bias():
     # B = 2: both batch elements share sink_start (split at 40 rows of block 15)
     q, k, v = workloads.random_qkv(2, 1100, 3, seed=17)
