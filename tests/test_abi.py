@@ -77,6 +77,31 @@ def test_shape_helpers_match_oracle(L):
     assert L.sa_dense_workspace_bytes(1, 9505, 56, 9216) % (64 * 130 * 4) == 0
 
 
+def _dense_splits(L, B, T, H, ss):
+    per_split = B * H * (-(-T // 64) - ss // 64) * 64 * 130 * 4
+    n = L.sa_dense_workspace_bytes(B, T, H, ss)
+    assert n % per_split == 0
+    return n // per_split
+
+
+def test_dense_split_choice(L):
+    # H3: 280 dense (head, block) units.  5 splits of 30 tiles = 1400
+    # workgroups in three rounds of 512 slots; 4 splits (38 tiles) leave the
+    # third round 19% full, 7 (22 tiles) and 9 (17) need 4 and 5 rounds.
+    assert _dense_splits(L, 1, 9505, 56, 9216) == 5
+    # Mid (8 heads): 32 units; 15 splits of 9 tiles (480 workgroups) fit one round
+    assert _dense_splits(L, 1, 8448, 8, 8192) == 15
+    # the same sequence with 56 heads: 224 units, 2 splits of 66 tiles in one round
+    assert _dense_splits(L, 1, 8448, 56, 8192) == 2
+    # a few units: split down to the 8-tile minimum (202 tiles -> 23 x 9)
+    assert _dense_splits(L, 1, 64 * 200 + 100, 2, 64 * 200) == 23
+    # every split keeps at least 8 tiles
+    for T, H, ss in ((1100, 3, 1000), (33280, 24, 32768), (65736, 2, 65536), (9505, 1, 9216)):
+        s = _dense_splits(L, 1, T, H, ss)
+        nb = -(-T // 64)
+        assert s == 0 or -(-nb // s) >= 8 or s == 1
+
+
 def _or_minus_one(fn, *args):
     try:
         return fn(*args)
