@@ -301,7 +301,9 @@ void attn_fwd_kernel(Params p) {
   // stay a suffix and the partial tile stays last.
   // The virtual keys are the video blocks the list skips, packed in
   // ascending order: nvb minus the list's video entries.
-  const int nv = kSpark ? (p.nvb - n_plain + kBlock - 1) / kBlock : 0;
+  // (A caller list with repeated video entries can count more of them than
+  // there are video blocks; no virtual tile then.)
+  const int nv = (kSpark && p.nvb > n_plain) ? (p.nvb - n_plain + kBlock - 1) / kBlock : 0;
   const int nt = nv + n;
   if (!kSpark && kbias == nullptr) n_plain = n;
   const int np_end = n_plain;          // tiles [0, np_end) are unbiased

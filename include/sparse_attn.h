@@ -221,7 +221,11 @@ sa_status sparse_attn_route(const void *q, const void *k,
  * block_idx, block_cnt, max_sel  as produced by sparse_attn_route with the
  *               same B, T, H, sink_start, video_tail_mode ([B, H, NVQ, ...]).
  *               Entries outside [0, NB) are skipped and counts are clamped
- *               to max_sel.
+ *               to max_sel.  Lists from elsewhere must have the same form:
+ *               ascending and without repeats, so that the sink blocks
+ *               [NVB, NB) come last and the partial block (if any) is the
+ *               last entry.  Other lists give unspecified values in the
+ *               sparse rows; every access still stays inside the tensors.
  * softmax_scale 0 selects 1/sqrt(128).
  * out           bf16 [B, T, H, 128]; only the sparse rows are written.
  * lse           nullable fp32 [B, H, T]; only the sparse rows are written.
