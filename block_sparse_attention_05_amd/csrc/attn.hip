@@ -11,7 +11,8 @@
 // one key range of such a block: split-KV), four wavefronts: wave w owns query
 // rows 32*(w&1)..+31 and keys 32*(w>>1)..+31 of every 64-key tile, with its
 // own online-softmax state; the two key halves of each row are merged at the
-// end.
+// end, each of the two waves of a row finishing and storing half of its
+// columns.
 //
 // Only rows in [row_lo, row_hi) are written.  That is how a query block split
 // by the video boundary is served: in the pad video tail mode (same page, H3
@@ -745,86 +746,103 @@ void attn_fwd_kernel(Params p) {
   }
 
   // ---- merge the two key halves of every row ------------------------------
-  // waves 2,3 hand (m, l, O^T) to waves 0,1 through LDS.
+  // Each wave finishes half of the columns of its 32 rows (the kh = 0 wave
+  // d in [0, 64), the kh = 1 wave d in [64, 128)): it hands the other half of
+  // its O^T and its (m, l) to its partner through LDS, merges, normalises and
+  // stores.  Both waves merge in the same order, key half 0 first, so the two
+  // halves of a row get the same max and sum.
   float l_tot = add_with_partner(l_run);
-  float4 *xo = reinterpret_cast<float4 *>(smem);              // [rw][16 quads][64 lanes]
-  float2 *xml = reinterpret_cast<float2 *>(smem + 32768);     // [rw][32 rows]
-  if (kh == 1) {
+  float4 *xo = reinterpret_cast<float4 *>(smem);              // [rw][kh][8 quads][64 lanes]
+  float2 *xml = reinterpret_cast<float2 *>(smem + kVOff);     // [kh][rw][32 rows]
+  auto hand_over = [&](auto ds_c) {   // the partner's column tiles ds, ds + 1
+    constexpr int DS = decltype(ds_c)::value;
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq)
-        xo[(rw * 16 + dt * 4 + rq) * 64 + lane] =
-            make_float4(o[dt][4 * rq], o[dt][4 * rq + 1], o[dt][4 * rq + 2], o[dt][4 * rq + 3]);
-    if (g == 0) xml[rw * 32 + c32] = make_float2(m_used, l_tot);
-  }
+        xo[((rw * 2 + kh) * 8 + u * 4 + rq) * 64 + lane] =
+            make_float4(o[DS + u][4 * rq], o[DS + u][4 * rq + 1], o[DS + u][4 * rq + 2], o[DS + u][4 * rq + 3]);
+  };
+  if (kh == 0)
+    hand_over(Int<2>{});
+  else
+    hand_over(Int<0>{});
+  if (g == 0) xml[(kh * 2 + rw) * 32 + c32] = make_float2(m_used, l_tot);
   __syncthreads();
-  if (kh == 1) return;
-  {
-    const float2 mlb = xml[rw * 32 + c32];
-    const float m = fmaxf(m_used, mlb.x);
-    const float msub = (m == -INFINITY) ? 0.f : m;
-    const float aa = __builtin_amdgcn_exp2f(m_used - msub);
-    const float ab = __builtin_amdgcn_exp2f(mlb.x - msub);
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        const float4 ob = xo[(rw * 16 + dt * 4 + rq) * 64 + lane];
-        o[dt][4 * rq + 0] = o[dt][4 * rq + 0] * aa + ob.x * ab;
-        o[dt][4 * rq + 1] = o[dt][4 * rq + 1] * aa + ob.y * ab;
-        o[dt][4 * rq + 2] = o[dt][4 * rq + 2] * aa + ob.z * ab;
-        o[dt][4 * rq + 3] = o[dt][4 * rq + 3] * aa + ob.w * ab;
-      }
-    l_tot = l_tot * aa + mlb.y * ab;
-    m_used = m;
-  }
 
-  if (kDense && p.nsplit > 1) {
-    if (tq >= T) return;
-    // partial (unnormalised O, max, sum) of this key range
-    const int64_t prow = ((int64_t)wq * p.nsplit + split) * kBlock + (rw * 32 + c32);
-    float *po = p.part_o + prow * kHeadDim;
+  auto finish = [&](auto dt_c) {   // this wave's column tiles dt0, dt0 + 1
+    constexpr int DT0 = decltype(dt_c)::value;
+    constexpr bool MINE_FIRST = DT0 == 0;   // this wave holds key half 0
+    const float2 mlb = xml[((kh ^ 1) * 2 + rw) * 32 + c32];
+    const float m0 = MINE_FIRST ? m_used : mlb.x, l0 = MINE_FIRST ? l_tot : mlb.y;
+    const float m1 = MINE_FIRST ? mlb.x : m_used, l1 = MINE_FIRST ? mlb.y : l_tot;
+    const float m = fmaxf(m0, m1);
+    const float msub = (m == -INFINITY) ? 0.f : m;
+    const float a0 = __builtin_amdgcn_exp2f(m0 - msub);
+    const float a1 = __builtin_amdgcn_exp2f(m1 - msub);
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) {
-        const int d0 = 32 * dt + 8 * rq + 4 * g;
-        *reinterpret_cast<float4 *>(po + d0) =
-            make_float4(o[dt][4 * rq + 0], o[dt][4 * rq + 1], o[dt][4 * rq + 2], o[dt][4 * rq + 3]);
+        const float4 ob = xo[((rw * 2 + (kh ^ 1)) * 8 + u * 4 + rq) * 64 + lane];
+        const float pb[4] = {ob.x, ob.y, ob.z, ob.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float x0 = MINE_FIRST ? o[DT0 + u][4 * rq + e] : pb[e];
+          const float x1 = MINE_FIRST ? pb[e] : o[DT0 + u][4 * rq + e];
+          o[DT0 + u][4 * rq + e] = __builtin_fmaf(x0, a0, x1 * a1);
+        }
       }
-    if (g == 0) *reinterpret_cast<float2 *>(p.part_ml + 2 * prow) = make_float2(m_used, l_tot);
-    return;
-  }
-  // The wave's 32 bf16 rows go through LDS (a free part of the V ring, rows
-  // of 256 B with the 16-byte chunks XOR-swizzled by row) and out as whole
-  // rows: each store instruction writes four full 256-byte rows.
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  unsigned char *stage = smem + kVOff + 8192 + rw * 8192;
+    l_tot = __builtin_fmaf(l0, a0, l1 * a1);
+    m_used = m;
+
+    if (kDense && p.nsplit > 1) {
+      if (tq >= T) return;
+      // partial (unnormalised O, max, sum) of this key range
+      const int64_t prow = ((int64_t)wq * p.nsplit + split) * kBlock + (rw * 32 + c32);
+      float *po = p.part_o + prow * kHeadDim;
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt) {
+      for (int u = 0; u < 2; ++u)
 #pragma unroll
-    for (int rq = 0; rq < 4; ++rq) {
-      uint2 val;
-      val.x = pack_bf16x2(o[dt][4 * rq + 0] * inv, o[dt][4 * rq + 1] * inv);
-      val.y = pack_bf16x2(o[dt][4 * rq + 2] * inv, o[dt][4 * rq + 3] * inv);
-      *reinterpret_cast<uint2 *>(stage + c32 * 256 + 16 * ((4 * dt + rq) ^ (c32 & 15)) + 8 * g) = val;
+        for (int rq = 0; rq < 4; ++rq) {
+          const int d0 = 32 * (DT0 + u) + 8 * rq + 4 * g;
+          *reinterpret_cast<float4 *>(po + d0) = make_float4(o[DT0 + u][4 * rq + 0], o[DT0 + u][4 * rq + 1],
+                                                             o[DT0 + u][4 * rq + 2], o[DT0 + u][4 * rq + 3]);
+        }
+      if (MINE_FIRST && g == 0) *reinterpret_cast<float2 *>(p.part_ml + 2 * prow) = make_float2(m_used, l_tot);
+      return;
     }
-  }
-  {
-    const int row0 = qb * kBlock + rw * 32;
-    uint16_t *ob = p.out + bbase + h * kHeadDim;
-    const int ch = lane & 15;
+    // The wave's 32 half rows (128 B) go through LDS (a free part of the V
+    // ring, 16-byte chunks XOR-swizzled by row) and out as whole half rows:
+    // each store instruction writes eight 128-byte half rows.
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    unsigned char *stage = smem + kVOff + 8192 + (rw * 2 + kh) * 4096;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = 4 * i + (lane >> 4);
-      const uint4 val = *reinterpret_cast<const uint4 *>(stage + r * 256 + 16 * (ch ^ (r & 15)));
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        uint2 val;
+        val.x = pack_bf16x2(o[DT0 + u][4 * rq + 0] * inv, o[DT0 + u][4 * rq + 1] * inv);
+        val.y = pack_bf16x2(o[DT0 + u][4 * rq + 2] * inv, o[DT0 + u][4 * rq + 3] * inv);
+        *reinterpret_cast<uint2 *>(stage + c32 * 128 + 16 * ((4 * u + rq) ^ (c32 & 7)) + 8 * g) = val;
+      }
+    const int row0 = qb * kBlock + rw * 32;
+    uint16_t *ob = p.out + bbase + h * kHeadDim + 64 * kh;
+    const int ch = lane & 7;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 8 * i + (lane >> 3);
+      const uint4 val = *reinterpret_cast<const uint4 *>(stage + r * 128 + 16 * (ch ^ (r & 7)));
       if (row0 + r >= p.row_lo && row0 + r < p.row_hi)
         *reinterpret_cast<uint4 *>(ob + (int64_t)(row0 + r) * rs + 8 * ch) = val;
     }
-  }
-  if (p.lse != nullptr && g == 0 && tq >= p.row_lo && tq < p.row_hi)
-    p.lse[((int64_t)b * p.H + h) * T + tq] = (m_used + __log2f(l_tot)) * kLn2;
+    if (MINE_FIRST && p.lse != nullptr && g == 0 && tq >= p.row_lo && tq < p.row_hi)
+      p.lse[((int64_t)b * p.H + h) * T + tq] = (m_used + __log2f(l_tot)) * kLn2;
+  };
+  if (kh == 0)
+    finish(Int<0>{});
+  else
+    finish(Int<2>{});
 }
 
 // Merge the split-KV partials of the dense rows: one thread per (row, 4
