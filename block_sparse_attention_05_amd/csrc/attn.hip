@@ -310,19 +310,12 @@ void attn_fwd_kernel(Params p) {
   const int np_end = n_plain;          // tiles [0, np_end) are unbiased
   auto is_virt = [&](int j) { return kSpark && (uint32_t)(j - np_end) < (uint32_t)nv; };
 
-  // Q^T fragments for this lane's query row: d = 16*dc + 8*g + [0, 8).
-  // Loaded after the list so that the first tile copies do not wait for them.
+  // Q^T fragments for this lane's query row: d = 16*dc + 8*g + [0, 8).  The
+  // block's 64 Q rows are copied once into V slot 1 (free until step 0) with
+  // the first tiles, in the K tile layout, and each wave reads its fragments
+  // from there after the prologue's barrier.
   const int tq = qb * kBlock + rw * 32 + c32;
   bf16x8 qf[8];
-  {
-    const uint4 *qp = reinterpret_cast<const uint4 *>(p.q + bbase + (int64_t)tq * rs + h * kHeadDim);
-#pragma unroll
-    for (int dc = 0; dc < 8; ++dc) {
-      uint4 x = make_uint4(0, 0, 0, 0);
-      if (tq < T) x = qp[2 * dc + g];
-      qf[dc] = __builtin_bit_cast(bf16x8, x);
-    }
-  }
 
   // First token of tile t_begin + j; calls come with j = 0, 1, 2, ... in
   // order.  An invalid list entry maps to T (reads as zero, fully masked).
@@ -352,6 +345,7 @@ void attn_fwd_kernel(Params p) {
   // ---- loads --------------------------------------------------------------
   const uint32_t slab = (uint32_t)T * (uint32_t)row_bytes;
   const i32x4s rk = buffer_rsrc(p.k + bbase, slab);
+  const i32x4s rqd = buffer_rsrc(p.q + bbase, slab);
   const i32x4s rv = buffer_rsrc(p.v + bbase, slab);
   const i32x4s rb = buffer_rsrc(kbias ? (const void *)kbias : (const void *)p.k, kbias ? T * 4u : 0u);
   const int sink0 = p.nvb * kBlock;
@@ -671,9 +665,26 @@ void attn_fwd_kernel(Params p) {
       issue_k(k_nxt, 1, is_virt(1));
     }
   }
+  {   // Q rows of the block into V slot 1, K tile layout
+    const uint32_t base = (uint32_t)(qb * kBlock) * (uint32_t)row_bytes + k_lane;
+    const uint32_t lb = lds0 + kVOff + 16384u + wave_lds;
+    lds_dma_b128<0>(rqd, base, lb);
+    lds_dma_b128<1024>(rqd, base + 128, lb);
+    lds_dma_b128<2048>(rqd, (base ^ 16u) + rows8, lb);
+    lds_dma_b128<3072>(rqd, (base ^ 16u) + rows8 + 128, lb);
+  }
   if (kSpark && !virt_first) build_virtual();  // published by the barrier below
   __builtin_amdgcn_s_waitcnt(kVmcntZero);
   __syncthreads();
+  {
+    const int qr = rw * 32 + c32, kg = qr >> 3, kp = qr & 7;
+#pragma unroll
+    for (int dc = 0; dc < 8; ++dc) {
+      const int ci = 2 * dc + g, hf = ci >> 3, cc = ci & 7;
+      qf[dc] = *reinterpret_cast<const bf16x8 *>(smem + kVOff + 16384 + 1024 * (2 * kg + hf) + 128 * kp +
+                                                 16 * (cc ^ kp ^ (kg & 1)));
+    }
+  }
   if (nt > 0) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) s0[r] = 0.f;
