@@ -296,7 +296,8 @@ void attn_fwd_kernel(Params p) {
   }
   const int n = t_end - t_begin;  // exact tiles
   // With the approximate branch, nv virtual tiles (64 block summaries each)
-  // sit between the exact video tiles and the sink tiles, and every tile
+  // sit between the exact video tiles and the sink tiles (see below for the
+  // order without key_bias), and every tile
   // from the first virtual one on is biased: virtual tiles by their
   // log-mass, sink tiles by key_bias (or zero without it).  The biased tiles
   // stay a suffix and the partial tile stays last.
@@ -307,6 +308,10 @@ void attn_fwd_kernel(Params p) {
   const int nv = (kSpark && p.nvb > n_plain) ? (p.nvb - n_plain + kBlock - 1) / kBlock : 0;
   const int nt = nv + n;
   if (!kSpark && kbias == nullptr) n_plain = n;
+  // Approximate branch without key_bias: sink tiles carry no bias, so the
+  // complete ones run with the video tiles, before the virtual tiles; only a
+  // partial last block (always the last list entry) follows those.
+  if (kSpark && kbias == nullptr && nv > 0) n_plain = (T % kBlock != 0) ? n - 1 : n;
   const int np_end = n_plain;          // tiles [0, np_end) are unbiased
   auto is_virt = [&](int j) { return kSpark && (uint32_t)(j - np_end) < (uint32_t)nv; };
 
