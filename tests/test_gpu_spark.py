@@ -136,6 +136,20 @@ def test_spark_many_virtual_tiles_odd_count():
     _spark_parity(q, k, v, 64 * 200, 0.05, 0, "spark_nvb200")
 
 
+def test_spark_no_bias_whole_sink_blocks():
+    """Without key_bias the complete sink tiles run ahead of the virtual
+    tiles; here T is a multiple of 64, so no partial block follows them."""
+    q, k, v = workloads.random_qkv(1, 64 * 40, 2, seed=23)
+    _spark_parity(q, k, v, 64 * 36, 0.1, 0, "spark_nobias_T64")
+
+
+def test_spark_no_bias_split_block():
+    """Without key_bias, with the video boundary inside a block and a
+    partial last block (the only tile after the virtual ones)."""
+    q, k, v, ss = _split_case(seed=24)
+    _spark_parity(q, k, v, ss, 0.2, 1, "spark_nobias_split")
+
+
 def test_spark_ratio_one_bit_identical_to_exact():
     """Nothing skipped: every virtual key is masked and the result must be
     the exact path's, bit for bit."""
