@@ -296,9 +296,9 @@ void attn_fwd_kernel(Params p) {
   }
   const int n = t_end - t_begin;  // exact tiles
   // With the approximate branch, nv virtual tiles (64 block summaries each)
-  // sit between the exact video tiles and the sink tiles (see below for the
-  // order without key_bias), and every tile
-  // from the first virtual one on is biased: virtual tiles by their
+  // sit between the exact video tiles and the sink tiles (without key_bias,
+  // between the complete sink tiles and a partial last block), and every
+  // tile from the first virtual one on is biased: virtual tiles by their
   // log-mass, sink tiles by key_bias (or zero without it).  The biased tiles
   // stay a suffix and the partial tile stays last.
   // The virtual keys are the video blocks the list skips, packed in
