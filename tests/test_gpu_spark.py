@@ -147,7 +147,8 @@ def test_spark_no_bias_split_block():
     """Without key_bias, with the video boundary inside a block and a
     partial last block (the only tile after the virtual ones)."""
     q, k, v, ss = _split_case(seed=24)
-    _spark_parity(q, k, v, ss, 0.2, 1, "spark_nobias_split")
+    for mode in ("dense", "pad"):
+        _spark_parity(q, k, v, ss, 0.2, 1, f"spark_nobias_split_{mode}", tail_mode=mode)
 
 
 def test_spark_ratio_one_bit_identical_to_exact():
