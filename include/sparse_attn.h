@@ -215,9 +215,13 @@ sa_status sparse_attn_route(const void *q, const void *k,
  * Evaluated as an online softmax in base 2 with fp32 accumulation on bf16
  * MFMA; P is rounded to bf16 for the PV product.
  *
- * key_bias      nullable fp32 [B, T], key_bias_numel must equal B*T.  Values
- *               on non-sink keys are ignored (callers must keep biased keys
- *               in sink blocks).
+ * key_bias      nullable fp32 [B, T], key_bias_numel must equal B*T.  The
+ *               pages require biased keys to lie in sink blocks; this
+ *               library reads the bias on sink keys only and ignores any
+ *               value below 64*NVB (checking it would need a device
+ *               reduction and a host wait).  The Python binding checks the
+ *               precondition before calling and raises on a non-zero value
+ *               there.
  * block_idx, block_cnt, max_sel  as produced by sparse_attn_route with the
  *               same B, T, H, sink_start, video_tail_mode ([B, H, NVQ, ...]).
  *               Entries outside [0, NB) are skipped and counts are clamped

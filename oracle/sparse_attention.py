@@ -84,7 +84,7 @@ __all__ = [
     "BLOCK", "HEAD_DIM", "NEAR_TIE_REL", "TAIL_MODES", "block_counts",
     "query_blocks", "sparse_rows_end", "topk_budget", "forced_blocks",
     "max_selected", "pool_means", "pad_query_block", "route_scores",
-    "select_row", "RowSelection", "Route", "route", "attend", "key_bias_vector",
+    "select_row", "RowSelection", "list_accepted", "Route", "route", "attend", "key_bias_vector",
     "sparse_block_output", "dense_rows_output", "routed_attention",
     "effective_flops",
 ]
@@ -241,6 +241,34 @@ def select_row(scores_row: np.ndarray, i: int, nvb: int, nb: int,
             band = (lo - tol, hi + tol)
     blocks = sorted(set(routed) | fset | set(range(nvb, nb)))
     return RowSelection(routed, forced, blocks, near, band)
+
+
+def list_accepted(got: Sequence[int], sel: RowSelection, scores_row: np.ndarray, nvb: int) -> bool:
+    """Whether a block list computed elsewhere is a correct selection for
+    the row that ``sel`` describes (several lists are correct only in a
+    near-tie row).
+
+    The list must equal ``sel.blocks``; in a near-tie row it may differ, but
+    only by routed candidates whose scores (``scores_row``, the fp32 route
+    scores of this row) lie inside ``sel.band``: same length, ascending, the
+    forced and sink blocks unchanged.  This is the selection rule of
+    ``select_row`` read with the k-th and (k+1)-th scores treated as equal
+    (the boundary selection is an exact FP32 one, page "Sol-Attn and Spark
+    for MiniMax-H3", Spark inference integration; two roundings of the same
+    sum may land one ulp apart)."""
+    got = [int(j) for j in got]
+    if got == sel.blocks:
+        return True
+    if not sel.near_tie or len(got) != len(sel.blocks):
+        return False
+    if any(a >= b for a, b in zip(got, got[1:])):
+        return False
+    lo, hi = sel.band
+    fixed = set(sel.forced)
+    for j in set(got) ^ set(sel.blocks):
+        if not (0 <= j < nvb) or j in fixed or not (lo <= float(scores_row[j]) <= hi):
+            return False
+    return True
 
 
 @dataclasses.dataclass

@@ -21,7 +21,7 @@ def to_np(t):
     return t.detach().float().cpu().numpy()
 
 
-def run_gpu(wl, *, key_bias=None, ratio=None, radius=None, scores=True, lse=True):
+def run_gpu(wl, *, key_bias=None, ratio=None, radius=None, scores=True, lse=True, check_bias=True):
     import block_sparse_attention_05_amd as sa
     dev = torch.device("cuda:0")
     q, k, v = (x.to(dev) for x in (wl.q, wl.k, wl.v))
@@ -39,8 +39,9 @@ def run_gpu(wl, *, key_bias=None, ratio=None, radius=None, scores=True, lse=True
     out = torch.full_like(q, float("nan"))
     ls = torch.full((B, H, T), float("nan"), device=dev) if lse else None
     sa.sparse_attn_fwd(q, k, v, wl.sink_start, idx, cnt, video_tail_mode=mode, key_bias=kb,
-                       out=out, lse=ls)
-    sa.dense_sink_fwd(q, k, v, wl.sink_start, video_tail_mode=mode, key_bias=kb, out=out, lse=ls)
+                       out=out, lse=ls, check_bias=check_bias)
+    sa.dense_sink_fwd(q, k, v, wl.sink_start, video_tail_mode=mode, key_bias=kb, out=out, lse=ls,
+                      check_bias=check_bias)
     torch.cuda.synchronize()
     return dict(out=out.cpu(), lse=None if ls is None else ls.cpu(), idx=idx.cpu(), cnt=cnt.cpu(),
                 scores=None if sc is None else sc.cpu())
@@ -48,15 +49,16 @@ def run_gpu(wl, *, key_bias=None, ratio=None, radius=None, scores=True, lse=True
 
 def compare_lists(idx, cnt, rt):
     """Lists must equal the oracle's except in near-tie rows, where every
-    differing block must have an oracle score inside the tie band.
-    Returns (rows, mismatched rows, near-tie rows, unexplained rows)."""
-    idx = idx.numpy()
-    cnt = cnt.numpy()
-    B, H, nvb, max_sel = idx.shape
+    differing block must have an oracle score inside the tie band
+    (``oracle.list_accepted``).  Returns (rows, mismatched rows, near-tie
+    rows, unexplained rows)."""
+    idx = idx.numpy() if hasattr(idx, "numpy") else np.asarray(idx)
+    cnt = cnt.numpy() if hasattr(cnt, "numpy") else np.asarray(cnt)
+    B, H, nvq, max_sel = idx.shape
     rows = mism = ties = unexplained = 0
     for b in range(B):
         for h in range(H):
-            for i in range(nvb):
+            for i in range(nvq):
                 rows += 1
                 sel = rt.rows[b][h][i]
                 c = int(cnt[b, h, i])
@@ -67,13 +69,20 @@ def compare_lists(idx, cnt, rt):
                 if got == sel.blocks:
                     continue
                 mism += 1
-                diff = set(got) ^ set(sel.blocks)
-                lo, hi = sel.band
-                ok = sel.near_tie and len(got) == len(sel.blocks) and all(
-                    j < rt.nvb and j not in sel.forced and lo <= rt.scores[b, h, i, j] <= hi for j in diff)
-                if not ok:
+                if not ora.list_accepted(got, sel, rt.scores[b, h, i], rt.nvb):
                     unexplained += 1
     return rows, mism, ties, unexplained
+
+
+def adopt_lists(idx, cnt, rt):
+    """Point the oracle's route at the GPU's lists (after compare_lists has
+    accepted them), so that attention is compared on the same key sets."""
+    idx = idx.numpy() if hasattr(idx, "numpy") else np.asarray(idx)
+    cnt = cnt.numpy() if hasattr(cnt, "numpy") else np.asarray(cnt)
+    for b, brow in enumerate(rt.rows):
+        for h, hrow in enumerate(brow):
+            for i, sel in enumerate(hrow):
+                sel.blocks = idx[b, h, i, :cnt[b, h, i]].tolist()
 
 
 def err_stats(got, want):

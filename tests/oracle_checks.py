@@ -164,6 +164,34 @@ def check_near_tie_flag():
     assert sel2.routed == [1, 3] and not sel2.near_tie
 
 
+def check_list_accepted():
+    """Which lists from elsewhere count as correct: only the oracle's own list
+    in an ordinary row; in a near-tie row also a list that swaps blocks whose
+    scores lie inside the band, and nothing else."""
+    budget = ra.topk_budget(6, 1.0 / 3.0)
+    tied = np.array([9.0, 3.0, 1.0, np.float32(1.0000001), -2.0, 0.5], dtype=np.float32)
+    sel = ra.select_row(tied, 0, 6, 8, budget, 0)       # blocks 6, 7 are sinks
+    assert sel.blocks == [0, 1, 3, 6, 7] and sel.near_tie
+    assert ra.list_accepted([0, 1, 3, 6, 7], sel, tied, 6)
+    assert ra.list_accepted([0, 1, 2, 6, 7], sel, tied, 6)        # 1.0 for 1.0000001
+    assert not ra.list_accepted([0, 1, 5, 6, 7], sel, tied, 6)    # 0.5 is outside the band
+    assert not ra.list_accepted([0, 2, 3, 6, 7], sel, tied, 6)    # drops the clear winner 1
+    assert not ra.list_accepted([1, 2, 3, 6, 7], sel, tied, 6)    # drops the forced block 0
+    assert not ra.list_accepted([0, 1, 2, 3, 6, 7], sel, tied, 6)  # too long
+    assert not ra.list_accepted([0, 1, 2, 6], sel, tied, 6)       # drops a sink
+    assert not ra.list_accepted([0, 2, 1, 6, 7], sel, tied, 6)    # not ascending
+    # the forced block 0 scores inside the band too: it still may not be swapped out
+    forced_tied = tied.copy()
+    forced_tied[0] = 1.0
+    sel3 = ra.select_row(forced_tied, 0, 6, 8, budget, 0)
+    assert sel3.blocks == [0, 1, 3, 6, 7] and sel3.near_tie
+    assert not ra.list_accepted([1, 2, 3, 6, 7], sel3, forced_tied, 6)
+    apart = np.array([9.0, 3.0, 1.0, 1.5, -2.0, 0.5], dtype=np.float32)
+    sel2 = ra.select_row(apart, 0, 6, 8, budget, 0)
+    assert ra.list_accepted(sel2.blocks, sel2, apart, 6)
+    assert not ra.list_accepted([0, 1, 2, 6, 7], sel2, apart, 6)  # no leniency without a tie
+
+
 def check_list_structure():
     rng = np.random.default_rng(22)
     nvb, nb = 20, 24
@@ -353,6 +381,11 @@ def check_golden_pages_numbers():
     assert len(ra.forced_blocks(10, nvb, 0)) == items["exact_radius_0_forced_blocks"]
     assert len(ra.forced_blocks(10, nvb, 1)) == items["exact_radius_1_forced_blocks"]
     assert ra.topk_budget(nvb, items["default_topk_ratio"]) == 15
+    # the pages keep sequences below the crossover dense; every configured
+    # routed workload (Mid 8448, H3 9505, Long 33280 tokens) lies above it
+    # and the small parity case (1024 tokens) below
+    cross = items["dense_crossover_tokens"]
+    assert cross == 8192 and 1024 < cross < min(8192 + 256, T, 32 * 1024 + 512)
 
 
 # ------------------------------------------------------- pad video tail ---
@@ -622,6 +655,7 @@ def check_spark_token_mask_path():
 ALL_CHECKS = [
     check_pool_exact, check_pool_permutation_invariant, check_scores_exact,
     check_budget, check_topk_bruteforce, check_signed_zero_tie, check_near_tie_flag,
+    check_list_accepted,
     check_list_structure, check_route_glue, check_ratio_one_equals_sdpa,
     check_all_dense_when_no_video_block, check_token_mask_path,
     check_zero_bias_is_no_bias, check_bias_ln_m_duplicates_key, check_bias_removes_key,

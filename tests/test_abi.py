@@ -358,3 +358,30 @@ def test_fused_entry_points_reject(L, fn, kw, code, msg):
 def test_fused_nothing_to_do_is_ok(L):
     assert _pool(L, ss=10, st=990, ws=None, ws_bytes=0) == 0
     assert _fused(L, ss=10, st=990, ws=None, ws_bytes=0) == 0
+
+
+def test_binding_key_bias_precondition():
+    """The binding enforces the pages' rule that biased keys lie in sink
+    blocks (keys >= 64*NVB), on CPU tensors here: zero (also -0.0) passes, any
+    non-zero or NaN value on a routed key raises, anything on sink keys
+    passes, and the element count must be B*T."""
+    import torch
+    import block_sparse_attention_05_amd as sa
+    B, T, ss = 2, 300, 200          # NVB = 3: keys [0, 192) are routed, [192, 300) sinks
+    kb = torch.zeros(B, T)
+    kb[:, 192:] = -1.5
+    sa.check_key_bias(kb, B, T, ss)
+    kb[1, 191] = -0.0
+    sa.check_key_bias(kb, B, T, ss)
+    sa.check_key_bias(kb.reshape(-1), B, T, ss)
+    for val in (-1e-30, 2.0, float("nan")):
+        bad = kb.clone()
+        bad[1, 191] = val
+        with pytest.raises(ValueError, match="sink blocks"):
+            sa.check_key_bias(bad, B, T, ss)
+        with pytest.raises(ValueError, match="sink blocks"):
+            sa.check_key_bias(bad.reshape(-1), B, T, ss)
+    # no routed keys at all: nothing to check
+    sa.check_key_bias(torch.full((B, T), 3.0), B, T, 40)
+    with pytest.raises(ValueError, match="B\\*T"):
+        sa.check_key_bias(torch.zeros(B, T - 1), B, T, ss)

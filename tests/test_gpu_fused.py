@@ -13,7 +13,7 @@ import torch
 
 import oracle.sparse_attention as ora
 import workloads
-from gpu_helpers import MAX_ABS, MEAN_ABS, compare_lists, err_stats, log, to_np
+from gpu_helpers import MAX_ABS, MEAN_ABS, adopt_lists, compare_lists, err_stats, log, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -44,10 +44,7 @@ def _fused_vs_unfused(wl, name, check_oracle_outputs=True):
         for b, h, i in d.nonzero().tolist():
             assert rt.rows[b][h][i].near_tie, (b, h, i)
     if check_oracle_outputs:
-        for b, brow in enumerate(rt.rows):
-            for h, hrow in enumerate(brow):
-                for i, sel in enumerate(hrow):
-                    sel.blocks = idx_f[b, h, i, :cnt_f[b, h, i]].tolist()
+        adopt_lists(idx_f.cpu(), cnt_f.cpu(), rt)
         want, want_lse, _ = ora.routed_attention(qn, kn, vn, wl.sink_start, wl.topk_ratio,
                                                  wl.local_radius,
                                                  key_bias=None if wl.key_bias is None else wl.key_bias.numpy(),
@@ -110,9 +107,10 @@ def test_fused_exact_ties_lower_index(nvb, ratio, radius):
 
 
 def test_fused_h3_with_bias():
-    """Full H3 size: lists against the oracle and the route kernel; outputs
-    bit-identical to the unfused call where the lists agree."""
-    _fused_vs_unfused(workloads.h3(with_bias=True), "fused_h3_bias", check_oracle_outputs=False)
+    """Full H3 size: lists against the oracle and the route kernel; every
+    output element against the oracle, and bit-identical to the unfused call
+    where the lists agree."""
+    _fused_vs_unfused(workloads.h3(with_bias=True), "fused_h3_bias")
 
 
 def test_fused_batch2_radius2_pad_with_bias():
@@ -125,6 +123,6 @@ def test_fused_batch2_radius2_pad_with_bias():
 
 def test_fused_max_route_blocks():
     """NVB = 1024: 1024 scores per workgroup and lists of 110 entries; lists
-    against the oracle and the route kernel, outputs bit-identical to the
-    unfused call where the lists agree."""
-    _fused_vs_unfused(workloads.max_blocks(), "fused_maxblocks", check_oracle_outputs=False)
+    against the oracle and the route kernel, every output element against the
+    oracle and bit-identical to the unfused call where the lists agree."""
+    _fused_vs_unfused(workloads.max_blocks(), "fused_maxblocks")

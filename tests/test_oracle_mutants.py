@@ -13,7 +13,7 @@ import oracle_checks as oc
 _orig = {name: getattr(ra, name) for name in (
     "pool_means", "route_scores", "topk_budget", "select_row", "attend",
     "key_bias_vector", "sparse_block_output", "dense_rows_output", "forced_blocks",
-    "route", "pad_query_block", "sparse_rows_end")}
+    "route", "pad_query_block", "sparse_rows_end", "list_accepted")}
 
 
 def pool_63(x, nvb, end=None):            # off-by-one block length
@@ -232,6 +232,18 @@ def anchor_block_rows(q, sink_start):               # complete video blocks only
 
 
 # (oracle function, mutant, the pin expected to catch it)
+def accept_any_in_tie_row(got, sel, scores_row, nvb):    # no band check at all
+    return list(got) == sel.blocks or sel.near_tie
+
+
+def accept_band_ignoring_forced(got, sel, scores_row, nvb):
+    if list(got) == sel.blocks:
+        return True
+    lo, hi = sel.band
+    return sel.near_tie and len(got) == len(sel.blocks) and list(got) == sorted(set(got)) and all(
+        j >= nvb or lo <= float(scores_row[j]) <= hi for j in set(got) ^ set(sel.blocks))
+
+
 MUTANTS = [
     ("pool_means", pool_63, oc.check_pool_exact),
     ("pool_means", pool_f32_sum, oc.check_pool_exact),
@@ -260,6 +272,8 @@ MUTANTS = [
     ("sparse_rows_end", sparse_end_whole_block, oc.check_pad_route_and_mask),
     ("sparse_rows_end", sparse_end_whole_block, oc.check_pad_modes_agree_where_they_must),
     ("forced_blocks", forced_one_sided, oc.check_pad_route_and_mask),
+    ("list_accepted", accept_any_in_tie_row, oc.check_list_accepted),
+    ("list_accepted", accept_band_ignoring_forced, oc.check_list_accepted),
 ]
 
 SP_MUTANTS = [
