@@ -12,5 +12,5 @@ from ._lib import (  # noqa: F401
     spark_reweight, sparse_attn_fwd_spark, routed_attention_spark, sparse_attn_pool,
     sparse_attn_fwd_fused, routed_attention_fused,
     sa_topk_budget,
-    sparse_attn_fwd, sparse_attn_route,
+    sparse_attn_fwd, sparse_attn_route, sparse_attn_route_noalloc,
 )

@@ -40,6 +40,9 @@ SIGNATURES = {
     "sparse_attn_route": (ctypes.c_int, [
         _vp, _vp, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32,
         _c_float, _c_int32, _vp, _c_int32, _vp, _vp, _vp, _c_size, _vp]),
+    "sparse_attn_route_noalloc": (ctypes.c_int, [
+        _vp, _vp, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32,
+        _c_float, _c_int32, _vp, _c_int32, _vp, _vp, _vp]),
     "sparse_attn_fwd": (ctypes.c_int, [
         _vp, _vp, _vp, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32,
         _vp, _c_int64, _vp, _vp, _c_int32, _c_float, _vp, _vp, _vp]),
@@ -248,6 +251,36 @@ def sparse_attn_route(q: torch.Tensor, k: torch.Tensor, sink_start: int,
         _ptr(q), _ptr(k), B, T, H, D, sink_start, T - sink_start, mode, float(topk_ratio),
         int(local_radius), _ptr(block_idx), int(max_sel), _ptr(block_cnt), _ptr(route_scores),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(dev)))
+    return block_idx, block_cnt
+
+
+def sparse_attn_route_noalloc(q: torch.Tensor, k: torch.Tensor, sink_start: int,
+                              topk_ratio: float, local_radius: int, block_idx: torch.Tensor,
+                              block_cnt: torch.Tensor, *, video_tail_mode: str = "dense",
+                              route_scores: Optional[torch.Tensor] = None):
+    """sparse_attn_route with the pooled means in the library's static device
+    scratch: the caller supplies every output and nothing is allocated (at
+    most SA_STATIC_SCRATCH_BYTES of means; calls overlapping on one GPU
+    race)."""
+    _check_qkv(q, k)
+    B, T, H, D = q.shape
+    dev = q.device
+    for name, t in (("block_idx", block_idx), ("block_cnt", block_cnt)):
+        if t.dtype != torch.int32 or not t.is_contiguous() or t.device != dev:
+            raise ValueError(f"{name} must be a contiguous int32 tensor on {dev}")
+    if route_scores is not None and (route_scores.dtype != torch.float32 or not route_scores.is_contiguous()
+                                     or route_scores.device != dev):
+        raise ValueError("route_scores must be contiguous float32 on the device of q")
+    mode = _mode(video_tail_mode)
+    nvq = lib().sa_num_query_blocks(T, sink_start, mode)
+    max_sel = block_idx.shape[-1] if block_idx.dim() == 4 else 0
+    if nvq > 0 and (block_idx.dim() != 4 or tuple(block_idx.shape[:3]) != (B, H, nvq)
+                    or block_cnt.numel() != B * H * nvq):
+        raise ValueError("block_idx must be [B,H,NVQ,max_sel] and block_cnt [B,H,NVQ]")
+    _check(lib().sparse_attn_route_noalloc(
+        _ptr(q), _ptr(k), B, T, H, D, sink_start, T - sink_start, mode, float(topk_ratio),
+        int(local_radius), _ptr(block_idx), int(max_sel), _ptr(block_cnt), _ptr(route_scores),
+        _stream(dev)))
     return block_idx, block_cnt
 
 

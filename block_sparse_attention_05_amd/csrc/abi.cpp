@@ -28,6 +28,18 @@ sa_status ok() {
   return SA_OK;
 }
 
+}  // namespace
+
+sa_status sa::set_error(sa_status st, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+namespace {
+
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 // Routed query blocks (NVQ) and the end of the sparse rows for a valid
@@ -166,12 +178,13 @@ sa_status sa_device_info(int32_t device, int32_t *cu_count, int32_t *clock_khz) 
   return ok();
 }
 
-sa_status sparse_attn_route(const void *q, const void *k, int32_t B, int32_t T, int32_t H,
-                            int32_t D, int32_t sink_start, int32_t sink_tokens,
-                            int32_t video_tail_mode, float topk_ratio, int32_t local_radius,
-                            int32_t *block_idx, int32_t max_sel, int32_t *block_cnt,
-                            float *route_scores, void *workspace, size_t workspace_bytes,
-                            void *stream) {
+}  // extern "C"
+
+sa_status sa::check_route_args(const void *q, const void *k, int32_t B, int32_t T, int32_t H,
+                               int32_t D, int32_t sink_start, int32_t sink_tokens,
+                               int32_t video_tail_mode, float topk_ratio, int32_t local_radius,
+                               const int32_t *block_idx, int32_t max_sel,
+                               const int32_t *block_cnt, const float *route_scores) {
   sa_status st = check_shape(B, T, H, D, sink_start, sink_tokens, video_tail_mode);
   if (st != SA_OK) return st;
   if ((st = check_bf16(q, "q")) != SA_OK) return st;
@@ -180,24 +193,41 @@ sa_status sparse_attn_route(const void *q, const void *k, int32_t B, int32_t T, 
     return fail(SA_ERR_INVALID_ARG, "topk_ratio must lie in (0, 1]");
   if (local_radius < 0) return fail(SA_ERR_INVALID_ARG, "local_radius must be >= 0");
   const Split sp = split_rows(T, sink_start, video_tail_mode);
-  const int32_t nvb = sp.nvb;
-  const int32_t nb = sa_num_blocks(T);
   if ((int64_t)B * H > 65535)
     return fail(SA_ERR_UNSUPPORTED, "routing supports B*H up to 65535 (got %lld)",
                 (long long)B * H);
-  if (nvb > sa::kMaxRouteBlocks)
+  if (sp.nvb > sa::kMaxRouteBlocks)
     return fail(SA_ERR_UNSUPPORTED, "at most %d video blocks can be routed (got %d)",
-                sa::kMaxRouteBlocks, nvb);
+                sa::kMaxRouteBlocks, sp.nvb);
   const int32_t need_sel =
       sa_max_selected(T, sink_start, video_tail_mode, topk_ratio, local_radius);
   if (max_sel < need_sel)
     return fail(SA_ERR_INVALID_ARG, "max_sel must be >= %d (got %d)", need_sel, max_sel);
-  if (sp.nvq == 0) return ok();
+  if (sp.nvq == 0) return SA_OK;
   if (block_idx == nullptr || block_cnt == nullptr)
     return fail(SA_ERR_INVALID_ARG, "block_idx and block_cnt must not be NULL");
   if (!aligned(block_idx, 4) || !aligned(block_cnt, 4) ||
       (route_scores != nullptr && !aligned(route_scores, 4)))
     return fail(SA_ERR_INVALID_ARG, "block_idx, block_cnt, route_scores must be 4-byte aligned");
+  return SA_OK;
+}
+
+extern "C" {
+
+sa_status sparse_attn_route(const void *q, const void *k, int32_t B, int32_t T, int32_t H,
+                            int32_t D, int32_t sink_start, int32_t sink_tokens,
+                            int32_t video_tail_mode, float topk_ratio, int32_t local_radius,
+                            int32_t *block_idx, int32_t max_sel, int32_t *block_cnt,
+                            float *route_scores, void *workspace, size_t workspace_bytes,
+                            void *stream) {
+  sa_status st = sa::check_route_args(q, k, B, T, H, D, sink_start, sink_tokens, video_tail_mode,
+                                      topk_ratio, local_radius, block_idx, max_sel, block_cnt,
+                                      route_scores);
+  if (st != SA_OK) return st;
+  const Split sp = split_rows(T, sink_start, video_tail_mode);
+  const int32_t nvb = sp.nvb;
+  const int32_t nb = sa_num_blocks(T);
+  if (sp.nvq == 0) return ok();
   const size_t need_ws = sa_route_workspace_bytes(B, T, H, sink_start, video_tail_mode);
   if (workspace_bytes < need_ws)
     return fail(SA_ERR_WORKSPACE, "workspace must hold %zu bytes (got %zu)", need_ws,

@@ -6,7 +6,18 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "sparse_attn.h"
+
 namespace sa {
+
+// Sets the thread's sa_last_error() text (printf format) and returns st.
+sa_status set_error(sa_status st, const char *fmt, ...);
+// Every host check of sparse_attn_route except the workspace (sets the
+// error text on failure).
+sa_status check_route_args(const void *q, const void *k, int32_t B, int32_t T, int32_t H, int32_t D,
+                           int32_t sink_start, int32_t sink_tokens, int32_t video_tail_mode,
+                           float topk_ratio, int32_t local_radius, const int32_t *block_idx,
+                           int32_t max_sel, const int32_t *block_cnt, const float *route_scores);
 
 constexpr int kBlock = 64;     // tokens per routing block
 constexpr int kHeadDim = 128;  // head dimension

@@ -193,6 +193,44 @@ sa_status sparse_attn_route(const void *q, const void *k,
                             void *workspace, size_t workspace_bytes,
                             void *stream);
 
+/* ---- routing without allocation ---------------------------------------------
+ *
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.
+ */
+
+/* Size of the library's static device scratch (per GPU, held until the
+ * process ends): 32 MiB, enough for the pooled means of B*H*NVQ16 = 21845
+ * query blocks with as many key blocks (H3: 12.4 MB; 24 heads of 512 blocks:
+ * 18.9 MB). */
+#define SA_STATIC_SCRATCH_BYTES (32u << 20)
+
+/*
+ * sparse_attn_route_noalloc - sparse_attn_route with the pooled means kept
+ * in the library's static device array of SA_STATIC_SCRATCH_BYTES instead of
+ * a caller workspace.  Same arguments (minus workspace), same computation,
+ * same outputs and errors as sparse_attn_route; the caller still owns q, k,
+ * block_idx, block_cnt and route_scores.
+ *
+ * Allocates nothing: no hipMalloc / hipFree and no allocating library call.
+ * The first call on a GPU looks up that GPU's copy of the array (the device
+ * of `stream`, or the current device for the null stream).
+ * Errors: SA_ERR_WORKSPACE when sa_route_workspace_bytes(B, T, H,
+ * sink_start, video_tail_mode) exceeds SA_STATIC_SCRATCH_BYTES (checked
+ * before any device access); SA_ERR_HIP if the lookup fails.
+ * Every call on a GPU shares that GPU's array, which keeps the last call's
+ * contents: calls that overlap on one GPU (concurrent streams or host
+ * threads) race and must be serialised by the caller.
+ */
+sa_status sparse_attn_route_noalloc(const void *q, const void *k,
+                                    int32_t B, int32_t T, int32_t H, int32_t D,
+                                    int32_t sink_start, int32_t sink_tokens,
+                                    int32_t video_tail_mode,
+                                    float topk_ratio, int32_t local_radius,
+                                    int32_t *block_idx, int32_t max_sel, int32_t *block_cnt,
+                                    float *route_scores,
+                                    void *stream);
+
 /* ---- attention ----------------------------------------------------------- */
 
 /*

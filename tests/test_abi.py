@@ -385,3 +385,41 @@ def test_binding_key_bias_precondition():
     sa.check_key_bias(torch.full((B, T), 3.0), B, T, 40)
     with pytest.raises(ValueError, match="B\\*T"):
         sa.check_key_bias(torch.zeros(B, T - 1), B, T, ss)
+
+
+def _route_noalloc(L, **kw):
+    a = dict(q=FAKE, k=FAKE, B=1, T=1024, H=2, D=128, ss=1024, st=0, mode=0, ratio=0.25, radius=0,
+             idx=FAKE, max_sel=5, cnt=FAKE, scores=None, stream=None)
+    a.update(kw)
+    return L.sparse_attn_route_noalloc(a["q"], a["k"], a["B"], a["T"], a["H"], a["D"], a["ss"],
+                                       a["st"], a["mode"], a["ratio"], a["radius"], a["idx"],
+                                       a["max_sel"], a["cnt"], a["scores"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(D=64), INVALID, "D must be 128"),
+    (dict(B=0), INVALID, "positive"),
+    (dict(ratio=0.0), INVALID, "topk_ratio"),
+    (dict(max_sel=4), INVALID, "max_sel"),
+    (dict(idx=None), INVALID, "block_idx"),
+    (dict(T=65600, ss=65600, max_sel=200, ratio=0.1), UNSUPPORTED, "video blocks"),
+    # 1024 routed blocks x 40 heads of means: 63 MB, above the static scratch
+    (dict(H=40, T=65536, ss=65536, max_sel=104, ratio=0.1), WORKSPACE, "static scratch"),
+])
+def test_route_noalloc_rejects_before_touching_a_device(L, kw, code, msg):
+    """Arguments and the static scratch limit are checked on the host first
+    (this runs without a GPU)."""
+    assert _route_noalloc(L, **kw) == code
+    assert msg in L.sa_last_error().decode()
+
+
+def test_static_scratch_limit_matches_header(L):
+    text = open(HEADER).read()
+    m = re.search(r"#define SA_STATIC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    limit = int(m.group(1)) << int(m.group(2))
+    # the largest routed workload (24 heads of 512 blocks) fits; one more
+    # 16-block tile of means per head beyond the limit does not
+    assert L.sa_route_workspace_bytes(1, 33280, 24, 32768, 0) <= limit
+    H = limit // (128 * 12 * 1024) + 1
+    assert L.sa_route_workspace_bytes(1, 65536, H, 65536, 0) > limit
+    assert _route_noalloc(L, H=H, T=65536, ss=65536, max_sel=104, ratio=0.1) == WORKSPACE
