@@ -20,7 +20,8 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libsparse_attn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
-SOURCES = ["abi.cpp", "pool.hip", "route.hip", "attn.hip", "spark.hip", "static_scratch.hip"]
+SOURCES = ["abi.cpp", "pool.hip", "route.hip", "attn.hip", "attn_pair.hip", "spark.hip",
+           "static_scratch.hip"]
 ARCH = "gfx950"
 
 COMMON_FLAGS = [

@@ -54,6 +54,7 @@
 // step is straight-line code.
 #include <type_traits>
 
+#include "attn_common.h"
 #include "device_util.h"
 #include "kernels.h"
 #include "select.h"
@@ -61,24 +62,8 @@
 namespace sa {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef int i32x4s __attribute__((ext_vector_type(4)));
-#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T *)(p))
+using namespace attn;
 
-template <int N>
-using Int = std::integral_constant<int, N>;
-template <bool B>
-using Bool = std::integral_constant<bool, B>;
-
-constexpr int kThreads = 256;
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kRescaleSlack = 8.0f;       // log2 units
-constexpr int kBufferFlags = 0x00020000;    // raw buffer, 32-bit data format
-constexpr int kVmcntZero = 0x0F70;          // s_waitcnt vmcnt(0), other counters untouched
 constexpr int kKOff = 0;                    // K ring: 2 x 16 KiB
 constexpr int kVOff = 32768;                // V ring: 2 x 16 KiB
 constexpr int kBOff = 65536;                // bias ring: 2 x 256 B
@@ -97,55 +82,6 @@ constexpr int kFsOff = kFqOff + kHeadDim * 8;
 constexpr int kFlOff = kFsOff + kMaxRouteBlocks * 4;
 constexpr int kFnOff = kFlOff + kMaxRouteBlocks * 4;
 constexpr int kFusedBytes = kHeadDim * 8 + kMaxRouteBlocks * 8 + 16;
-
-// sched_group_barrier instruction classes
-constexpr int kSchedVALU = 0x002;
-constexpr int kSchedMFMA = 0x008;
-constexpr int kSchedDSRead = 0x100;
-
-// Raw buffer resource: base, no stride, num_records bytes, raw 32-bit format.
-__device__ __forceinline__ i32x4s buffer_rsrc(const void *base, uint32_t num_bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  i32x4s r;
-  r[0] = (int)(uint32_t)a;
-  r[1] = (int)(uint32_t)(a >> 32) & 0xffff;
-  r[2] = (int)num_bytes;
-  r[3] = kBufferFlags;
-  return r;
-}
-
-// Global -> LDS copy of 16 (or 4) bytes per lane: lane l writes LDS byte
-// lds_base + 16*l (4*l).  Offsets at or past num_records read as zero.
-// Issued as inline asm so the compiler does not order later LDS reads of the
-// other ring slot behind it; the caller waits (vmcnt) before the barrier that
-// publishes the data.
-// The LDS address is lds_base + kOff (kOff folded into the M0 write, so the
-// caller keeps one base register per ring slot).  A buffer load into LDS
-// needs one wait state after an SALU write of M0, which the hardware does
-// not check: hence the s_nop.
-template <int kOff>
-__device__ __forceinline__ void lds_dma_b128(const i32x4s &rsrc, uint32_t voffset, uint32_t lds_base) {
-  asm volatile("s_add_u32 m0, %2, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-               :
-               : "v"(voffset), "s"(rsrc), "s"(lds_base), "i"(kOff)
-               : "memory", "m0", "scc");
-}
-__device__ __forceinline__ void lds_dma_b32(const i32x4s &rsrc, uint32_t voffset, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
-               :
-               : "v"(voffset), "s"(rsrc), "s"(lds_base)
-               : "memory", "m0");
-}
-
-// x combined with the same register of lane ^ 32 (v_permlane32_swap).
-__device__ __forceinline__ float max_with_partner(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float add_with_partner(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
 
 struct Params {
   const uint16_t *q, *k, *v;
@@ -171,11 +107,6 @@ struct Params {
   int budget, radius;
   int32_t *list_out, *cnt_out;
 };
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  const bf16x2 v = {(__bf16)a, (__bf16)b};
-  return __builtin_bit_cast(uint32_t, v);
-}
 
 template <bool kDense, bool kSpark = false, bool kFused = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -942,33 +873,7 @@ Params make_params(const AttnArgs &a, int qb0, int nqb) {
 
 }  // namespace
 
-int dense_splits(int B, int H, int nb, int nvb) {
-  const int nq = nb - nvb;
-  if (nq <= 0) return 1;
-  const int64_t units = (int64_t)B * H * nq;
-  // Choose the key split that minimises (rounds of resident workgroups) x
-  // (tiles per split + the fixed cost of a workgroup, about 8 tile steps:
-  // prologue, merge, partial-result stores).  Two workgroups fit a CU and
-  // the device has 256 CUs.  Splits keep at least 8 tiles each; among equal
-  // costs the fewer splits win (less partial traffic for the combine).
-  constexpr int64_t kSlots = 2 * 256;
-  constexpr int64_t kFixedTiles = 8;
-  const int max_s = nb / 8 > 1 ? nb / 8 : 1;
-  int best = 1;
-  int64_t best_cost = -1;
-  for (int s = 1; s <= max_s; ++s) {
-    const int per = (nb + s - 1) / s;
-    const int se = (nb + per - 1) / per;          // splits after equalising
-    if (se != s) continue;
-    const int64_t rounds = (units * se + kSlots - 1) / kSlots;
-    const int64_t cost = rounds * (per + kFixedTiles);
-    if (best_cost < 0 || cost < best_cost) {
-      best_cost = cost;
-      best = se;
-    }
-  }
-  return best;
-}
+int dense_splits(int B, int H, int nb, int nvb) { return dense_pair_splits(B, H, nb, nvb); }
 
 size_t dense_workspace_bytes(int B, int H, int nb, int nvb) {
   const int s = dense_splits(B, H, nb, nvb);
@@ -979,6 +884,7 @@ size_t dense_workspace_bytes(int B, int H, int nb, int nvb) {
 
 hipError_t launch_attn_sparse(const AttnArgs &a, hipStream_t stream) {
   if (a.nvq <= 0) return hipSuccess;
+  if (a.max_sel <= kMaxPairList) return launch_attn_pair_sparse(a, stream);
   Params p = make_params(a, 0, a.nvq);
   p.row_hi = a.rows_end;
   const int total = a.B * a.H * a.nvq;
@@ -1013,20 +919,19 @@ hipError_t launch_attn_dense(const AttnArgs &a, void *workspace, size_t workspac
                              hipStream_t stream) {
   const int nq = a.nb - a.nvb;
   if (nq <= 0 || a.rows_end >= a.T) return hipSuccess;
+  const int s = dense_splits(a.B, a.H, a.nb, a.nvb);
+  if (s <= 1 || workspace == nullptr || workspace_bytes < dense_workspace_bytes(a.B, a.H, a.nb, a.nvb))
+    return launch_attn_pair_dense(a, nullptr, nullptr, 1, stream);
+  const size_t rows = (size_t)a.B * a.H * nq * s * kBlock;
+  float *part_o = static_cast<float *>(workspace);
+  float *part_ml = part_o + rows * kHeadDim;
+  hipError_t e = launch_attn_pair_dense(a, part_o, part_ml, s, stream);
+  if (e != hipSuccess) return e;
   Params p = make_params(a, a.nvb, nq);
   p.row_lo = a.rows_end;
-  const int s = dense_splits(a.B, a.H, a.nb, a.nvb);
-  if (s > 1 && workspace != nullptr && workspace_bytes >= dense_workspace_bytes(a.B, a.H, a.nb, a.nvb)) {
-    p.nsplit = s;
-    p.tiles_per_split = (a.nb + s - 1) / s;
-    const size_t rows = (size_t)a.B * a.H * nq * s * kBlock;
-    p.part_o = static_cast<float *>(workspace);
-    p.part_ml = p.part_o + rows * kHeadDim;
-  }
-  const int total = a.B * a.H * nq * p.nsplit;
-  hipLaunchKernelGGL(attn_fwd_kernel<true>, dim3(total), dim3(kThreads), 0, stream, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.nsplit == 1) return e;
+  p.nsplit = s;
+  p.part_o = part_o;
+  p.part_ml = part_ml;
   hipLaunchKernelGGL(combine_kernel, dim3(a.B * a.H * nq * (kBlock / kCombineRows)),
                      dim3(kCombineThreads), 0, stream, p);
   return hipGetLastError();

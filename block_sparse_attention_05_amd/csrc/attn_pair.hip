@@ -1,0 +1,860 @@
+// Block-sparse flash attention on gfx950 bf16 MFMA with paired query blocks:
+// one workgroup serves two adjacent 64-row query blocks A = 2p and B = 2p+1
+// of one (b, h) and loads each key tile once when both lists hold it.
+//
+// Page "Sol-Attn and Spark for MiniMax-H3", Spark inference integration:
+// selected K/V tiles stream through a single FP32 online-softmax/output
+// accumulator.  Page "Add key bias to chunked Sol-Attn producers", Summary /
+// Contract: the natural-log key bias is converted to log2 units and consumed
+// only by the exact branch (sink keys).
+//
+// Why pairs.  A 64-row query block does 2.1 MFLOP per 64-key tile against
+// 32 KiB of K/V copied from L2 into LDS, 64 FLOP per byte: at the MFMA rate
+// of a CU that needs the whole global-to-LDS copy bandwidth of the CU, which
+// makes the copies the binding resource of a one-block workgroup.  Adjacent
+// query blocks of a video (two 2-row strips of the same frame) select mostly
+// the same key blocks: at the H3 shape two adjacent lists share about 65% of
+// their entries (all sink blocks and most routed ones), so serving both from
+// one tile stream cuts the copied bytes by about a third.
+//
+// Workgroup: four wavefronts; wave w serves rows 32*(w&1) .. +31 of block
+// A (w < 2) or B (w >= 2), over all 32 keys of a half tile per step, so every
+// wave owns whole rows and there is no key-half merge.  A step consumes one
+// 32-key half tile for each block: the same half tile when both lists hold
+// the key block ("shared" entry, 16 KiB of K and V copied), or one half tile
+// of each block's own list ("paired" entry: a key block only A holds next to
+// one only B holds, 32 KiB copied).  Every list entry is two steps (the two
+// 32-key halves of its 64-key block).
+//
+// Schedule.  Wave 0 builds the entry list in LDS before the first tile load:
+// it compacts both lists (entries outside [0, NB) are skipped), splits them
+// into shared and private entries (binary search in the other list), pairs
+// the i-th private entry of A with the i-th of B, and orders the entries in
+// three phases:
+//   U  - both tiles complete and unbiased (every entry when key_bias is NULL
+//        apart from the partial block);
+//   Bi - both tiles complete, at least one a sink tile with key_bias (biased;
+//        the bias of a non-sink tile reads as zero);
+//   G  - general: the partial last block NB-1, and private entries left over
+//        when the lists differ in length (one block has no tile there).
+// U and Bi steps are straight-line code; G steps mask keys past T and skip
+// the softmax of a block without a tile.  The dense path (dense_sink_fwd)
+// takes the implicit list [t_begin, t_end) for both blocks (all shared), in
+// the same three phases.
+//
+// Data movement.  K and V half tiles go from HBM/L2 straight to LDS with
+// buffer_load ... lds in the one-block kernel's tile layout (a slot is the
+// 64-key layout whose key halves hold A's and B's half tiles; a shared entry
+// fills the first half only).  Keys past T fall outside the buffer range and
+// read as zero.  K runs two steps ahead and V one, two slots each.  Q rows
+// are read straight into the MFMA operand registers (each wave reads only
+// its own rows).
+//
+// Math per step and wave (32 rows x 32 keys): S^T = K Q^T on
+// v_mfma_f32_32x32x16_bf16, online softmax in base 2 with lazy rescaling
+// (slack 8), P rounded to bf16, O^T += V^T P^T with V^T from
+// ds_read_b64_tr_b16; the S(j+1) MFMAs of the next step overlap the softmax
+// of this one.  The same arithmetic as the one-block kernel, with the keys of
+// a 64-key tile accumulated in two sequential steps instead of two waves.
+#include "attn_common.h"
+#include "device_util.h"
+#include "kernels.h"
+
+namespace sa {
+namespace {
+
+using namespace attn;
+
+constexpr int kPKOff = 0;                       // K ring: 2 slots x 16 KiB (A half | B half)
+constexpr int kPVOff = 32768;                   // V ring: 2 slots x 16 KiB
+constexpr int kPBOff = 65536;                   // bias ring: 2 slots x 64 floats (A | B)
+constexpr int kPSchOff = 65536 + 512;           // entries: kMaxPairEntries x (block A, block B)
+constexpr int kMaxPairEntries = 2 * kMaxPairList;
+constexpr int kPCntOff = kPSchOff + kMaxPairEntries * 8;   // nU, nBi, nE
+constexpr int kPLdsBytes = kPCntOff + 16;
+// Schedule-build temporaries, inside the K ring (no tile is loaded yet):
+// compacted lists, private entries of A and B, shared entries.
+constexpr int kListBytes = 4 * kMaxPairList;
+constexpr int kLAOff = 0;
+constexpr int kLBOff = kLAOff + kListBytes;
+constexpr int kPAOff = kLBOff + kListBytes;
+constexpr int kPBlOff = kPAOff + kListBytes;
+constexpr int kSHOff = kPBlOff + kListBytes;
+static_assert(kSHOff + kListBytes <= kPVOff, "build temporaries must fit the K ring");
+
+struct PairParams {
+  const uint16_t *q, *k, *v;
+  uint16_t *out;
+  float *lse;
+  const float *key_bias;
+  const int32_t *block_idx, *block_cnt;
+  float *part_o;      // split-KV partial outputs (dense path), nullable
+  float *part_ml;     // split-KV partial (max, sum) per row
+  int B, T, H, nb, nvb, max_sel;
+  int qb0, nqb, npair;
+  int row_lo, row_hi;  // rows written: [row_lo, row_hi)
+  int nsplit, tiles_per_split;
+  float scale_log2;
+};
+
+// Lanes below this one whose bit is set in m.
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+}
+
+// Whether x is among the n ascending values arr[0..n) (LDS).
+__device__ __forceinline__ bool lds_contains(const int *arr, int n, int x) {
+  const int len = n;
+  int lo = 0;
+  while (n > 0) {
+    const int half = n >> 1;
+    if (arr[lo + half] < x) {
+      lo += half + 1;
+      n -= half + 1;
+    } else {
+      n = half;
+    }
+  }
+  return lo < len && arr[lo] == x;
+}
+
+// Entry list of one workgroup, in three passes separated by workgroup
+// barriers (the caller's): compact (waves 0 and 1, one list each), classify
+// (waves 0 and 1) and emit (wave 0).  Scalars: cnt[0..2] = nU, nBi, nE;
+// cnt[3..7] = valid entries of A and B, private entries of A and B, shared
+// entries.
+
+// Pass 1: the valid entries of one list, in order, to dst.  `first` holds entry `lane` of the list
+// (read before anything else), c its length.
+__device__ __forceinline__ void pair_compact(const PairParams &p, int64_t li, int c, int first, int *dst,
+                                             int *n_out, int lane) {
+  c = c < 0 ? 0 : (c > p.max_sel ? p.max_sel : c);
+  const int32_t *lst = p.block_idx + li * p.max_sel;
+  int n = 0;
+  for (int cb = 0; cb < c; cb += 64) {
+    const int e = cb == 0 ? (lane < c ? first : -1) : (cb + lane < c ? lst[cb + lane] : -1);
+    const bool ok = e >= 0 && e < p.nb;
+    const uint64_t m = __ballot(ok);
+    if (ok) dst[n + lanes_below(m)] = e;
+    n += __popcll(m);
+  }
+  if (lane == 0) *n_out = n;
+}
+
+// Pass 2: entries of `own` also in `other` go to sh (when given), the rest
+// to priv.
+__device__ __forceinline__ void pair_classify(const int *own, int n_own, const int *other, int n_other,
+                                              int *priv, int *n_priv_out, int *sh, int *n_sh_out,
+                                              int lane) {
+  int np = 0, ns = 0;
+  for (int cb = 0; cb < n_own; cb += 64) {
+    const int i = cb + lane;
+    const bool in = i < n_own;
+    const int x = in ? own[i] : -1;
+    const bool shared = in && lds_contains(other, n_other, x);
+    const uint64_t mp = __ballot(in && !shared), ms = __ballot(shared);
+    if (in && !shared) priv[np + lanes_below(mp)] = x;
+    if (shared && sh != nullptr) sh[ns + lanes_below(ms)] = x;
+    np += __popcll(mp);
+    ns += __popcll(ms);
+  }
+  if (lane == 0) {
+    *n_priv_out = np;
+    if (sh != nullptr) *n_sh_out = ns;
+  }
+}
+
+// Pass 3: private pairs (and leftovers), then shared entries, sorted into
+// the three phases.
+__device__ __forceinline__ void pair_emit(const PairParams &p, unsigned char *smem, int lane) {
+  const int *PA = reinterpret_cast<const int *>(smem + kPAOff);
+  const int *PB = reinterpret_cast<const int *>(smem + kPBlOff);
+  const int *SH = reinterpret_cast<const int *>(smem + kSHOff);
+  int2 *sch = reinterpret_cast<int2 *>(smem + kPSchOff);
+  int *cnt = reinterpret_cast<int *>(smem + kPCntOff);
+  const int nPA = __builtin_amdgcn_readfirstlane(cnt[5]);
+  const int nPB = __builtin_amdgcn_readfirstlane(cnt[6]);
+  const int nS = __builtin_amdgcn_readfirstlane(cnt[7]);
+  const int partial = (p.T % kBlock) != 0 ? p.nb - 1 : -1;
+  const bool biased = p.key_bias != nullptr;
+  const int nX = nPA > nPB ? nPA : nPB;
+  const int nC = nX + nS;
+  auto entry = [&](int c, int &a, int &b) {
+    if (c < nX) {
+      a = c < nPA ? PA[c] : -1;
+      b = c < nPB ? PB[c] : -1;
+    } else {
+      a = b = SH[c - nX];
+    }
+  };
+  auto phase = [&](int a, int b) -> int {
+    if (a < 0 || b < 0 || a == partial || b == partial) return 2;
+    if (biased && (a >= p.nvb || b >= p.nvb)) return 1;
+    return 0;
+  };
+  if (nC <= 64) {   // one chunk: entries stay in registers between the passes
+    int a = -1, b = -1;
+    if (lane < nC) entry(lane, a, b);
+    const int ph = lane < nC ? phase(a, b) : 3;
+    const uint64_t m0 = __ballot(ph == 0), m1 = __ballot(ph == 1), m2 = __ballot(ph == 2);
+    const int n0 = __popcll(m0), n1 = __popcll(m1);
+    if (ph < 3) {
+      const int pos = ph == 0 ? lanes_below(m0) : ph == 1 ? n0 + lanes_below(m1) : n0 + n1 + lanes_below(m2);
+      sch[pos] = make_int2(a, b);
+    }
+    if (lane == 0) {
+      cnt[0] = n0;
+      cnt[1] = n1;
+      cnt[2] = nC;
+    }
+    return;
+  }
+  int n0 = 0, n1 = 0;
+  for (int cb = 0; cb < nC; cb += 64) {
+    const int c = cb + lane;
+    int a = -1, b = -1;
+    if (c < nC) entry(c, a, b);
+    const int ph = c < nC ? phase(a, b) : 3;
+    n0 += __popcll(__ballot(ph == 0));
+    n1 += __popcll(__ballot(ph == 1));
+  }
+  int r0 = 0, r1 = n0, r2 = n0 + n1;
+  for (int cb = 0; cb < nC; cb += 64) {
+    const int c = cb + lane;
+    int a = -1, b = -1;
+    if (c < nC) entry(c, a, b);
+    const int ph = c < nC ? phase(a, b) : 3;
+    const uint64_t m0 = __ballot(ph == 0), m1 = __ballot(ph == 1), m2 = __ballot(ph == 2);
+    if (ph < 3) {
+      const int pos = ph == 0 ? r0 + lanes_below(m0) : ph == 1 ? r1 + lanes_below(m1) : r2 + lanes_below(m2);
+      sch[pos] = make_int2(a, b);
+    }
+    r0 += __popcll(m0);
+    r1 += __popcll(m1);
+    r2 += __popcll(m2);
+  }
+  if (lane == 0) {
+    cnt[0] = n0;
+    cnt[1] = n1;
+    cnt[2] = nC;
+  }
+}
+
+// kDmaAt: where a steady-state step issues its copies (V of the next step, K
+// of the step after): 0 both before the step's math, 1 both after the max
+// block, 2 K before and V after the max block, 3 K after the max block and V
+// after the exponentials, 4 V before and K after the max block.
+template <bool kDense, int kDmaAt>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_pair_kernel(PairParams p) {
+  __shared__ __align__(16) unsigned char smem[kPLdsBytes];
+
+  const int total = p.B * p.H * p.npair * p.nsplit;
+  const int w = xcd_remap(blockIdx.x, total);
+  const int split = w % p.nsplit;
+  const int wp = w / p.nsplit;
+  const int pi = wp % p.npair;
+  const int bh = wp / p.npair;
+  const int h = bh % p.H;
+  const int b = bh / p.H;
+  const int qbiA = 2 * pi;
+  const bool hasB = qbiA + 1 < p.nqb;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: SGPR
+  const int blk = wave >> 1;   // 0: block A, 1: block B
+  const int rw = wave & 1;     // rows 32*rw .. +31 of the block
+  const int g = lane >> 5;
+  const int c32 = lane & 31;
+  const int T = p.T;
+  const int64_t rs = (int64_t)p.H * kHeadDim;   // elements per token
+  const int row_bytes = p.H * kHeadDim * 2;
+  const int64_t bbase = (int64_t)b * T * rs;
+  const int qbi = qbiA + blk;
+  const int qb = p.qb0 + qbi;
+  const bool active = blk == 0 || hasB;          // a missing block B computes nothing it keeps
+  const int tq = qb * kBlock + rw * 32 + c32;    // this lane's query row
+
+  // The lists go first: wave 0 reads A's count and first 64 entries, wave 1
+  // B's, all four loads in flight together ahead of the Q rows.
+  const int64_t liA = (int64_t)bh * p.nqb + qbiA;
+  int lcnt = 0, lfirst = -1;
+  if (!kDense && wave < 2 && (wave == 0 || hasB)) {
+    const int64_t li = liA + wave;
+    lcnt = p.block_cnt[li];
+    if (lane < p.max_sel) lfirst = p.block_idx[li * p.max_sel + lane];
+  }
+
+  // Q^T fragments of this lane's row (d = 16*dc + 8*g + [0, 8)), read
+  // straight from memory; rows past T read as zero.
+  bf16x8 qf[8];
+  {
+    const bool ok = active && tq < T;
+    const uint16_t *qrow = p.q + bbase + (int64_t)(ok ? tq : 0) * rs + h * kHeadDim + 8 * g;
+#pragma unroll
+    for (int dc = 0; dc < 8; ++dc) {
+      bf16x8 v = {};
+      if (ok) v = *reinterpret_cast<const bf16x8 *>(qrow + 16 * dc);
+      qf[dc] = v;
+    }
+  }
+
+  // ---- schedule ------------------------------------------------------------
+  const bool has_bias = p.key_bias != nullptr;
+  const int nbfull = (T % kBlock) != 0 ? p.nb - 1 : p.nb;   // blocks of 64 keys
+  int nU, nBi, nE;
+  int d_t0 = 0, d_nub = 0;
+  const int2 *sch = reinterpret_cast<const int2 *>(smem + kPSchOff);
+  if (kDense) {
+    const int t_begin = split * p.tiles_per_split;
+    int t_end = t_begin + p.tiles_per_split;
+    t_end = t_end < p.nb ? t_end : p.nb;
+    const int ub_end = t_end < nbfull ? t_end : nbfull;
+    const int nub = ub_end > t_begin ? ub_end - t_begin : 0;
+    int nu = nub;
+    if (has_bias) {
+      nu = p.nvb - t_begin;
+      nu = nu < 0 ? 0 : (nu > nub ? nub : nu);
+    }
+    nU = nu;
+    nBi = nub - nu;
+    nE = nub + ((nbfull < p.nb && p.nb - 1 >= t_begin && p.nb - 1 < t_end) ? 1 : 0);
+    d_t0 = t_begin;
+    d_nub = nub;
+  } else {
+    int *cnt = reinterpret_cast<int *>(smem + kPCntOff);
+    int *LA = reinterpret_cast<int *>(smem + kLAOff);
+    int *LB = reinterpret_cast<int *>(smem + kLBOff);
+    if (wave == 0 || (wave == 1 && hasB))
+      pair_compact(p, liA + wave, __builtin_amdgcn_readfirstlane(lcnt), lfirst, wave ? LB : LA,
+                   cnt + 3 + wave, lane);
+    __syncthreads();
+    if (wave < 2) {
+      const int nA = __builtin_amdgcn_readfirstlane(cnt[3]);
+      if (!hasB) {   // a missing block B: every entry of A is shared
+        if (wave == 0) pair_classify(LA, nA, LA, 0, reinterpret_cast<int *>(smem + kSHOff), cnt + 7,
+                                     nullptr, nullptr, lane);
+        if (wave == 0 && lane == 0) cnt[5] = cnt[6] = 0;
+      } else {
+        const int nB = __builtin_amdgcn_readfirstlane(cnt[4]);
+        if (wave == 0)
+          pair_classify(LA, nA, LB, nB, reinterpret_cast<int *>(smem + kPAOff), cnt + 5,
+                        reinterpret_cast<int *>(smem + kSHOff), cnt + 7, lane);
+        else
+          pair_classify(LB, nB, LA, nA, reinterpret_cast<int *>(smem + kPBlOff), cnt + 6, nullptr,
+                        nullptr, lane);
+      }
+    }
+    __syncthreads();
+    if (wave == 0) pair_emit(p, smem, lane);
+    __syncthreads();
+    nU = __builtin_amdgcn_readfirstlane(cnt[0]);
+    nBi = __builtin_amdgcn_readfirstlane(cnt[1]);
+    nE = __builtin_amdgcn_readfirstlane(cnt[2]);
+  }
+  // Entries in lanes (lane j = entry ch_cb + j of the current 64-entry
+  // chunk), read with v_readlane; entry() is called with e = 0, 1, 2, ...
+  int ch_cb = 0, ch_a = -1, ch_b = -1;
+  if (!kDense && lane < nE) {
+    const int2 v = sch[lane];
+    ch_a = v.x;
+    ch_b = v.y;
+  }
+  auto entry = [&](int e, int &a, int &bb) {
+    if (kDense) {
+      a = bb = e < d_nub ? d_t0 + e : p.nb - 1;
+      return;
+    }
+    if (e - ch_cb >= 64) {
+      ch_cb += 64;
+      const int x = ch_cb + lane;
+      int2 v = make_int2(-1, -1);
+      if (x < nE) v = sch[x];
+      ch_a = v.x;
+      ch_b = v.y;
+    }
+    a = __builtin_amdgcn_readlane(ch_a, e - ch_cb);
+    bb = __builtin_amdgcn_readlane(ch_b, e - ch_cb);
+  };
+  // First key of half tile `half` of block bl; T (no tile) for a missing
+  // block or a half that lies past T.
+  auto hkey = [&](int bl, int half) -> int {
+    const int k0 = bl * kBlock + 32 * half;
+    return (bl < 0 || k0 >= T) ? T : k0;
+  };
+
+  // ---- loads --------------------------------------------------------------
+  const uint32_t slab = (uint32_t)T * (uint32_t)row_bytes;
+  const i32x4s rk = buffer_rsrc(p.k + bbase, slab);
+  const i32x4s rv = buffer_rsrc(p.v + bbase, slab);
+  const float *kbias = has_bias ? p.key_bias + (int64_t)b * T : nullptr;
+  const i32x4s rb = buffer_rsrc(kbias ? (const void *)kbias : (const void *)p.k, kbias ? T * 4u : 0u);
+  const int sink0 = p.nvb * kBlock;
+  const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>(LDS_PTR(unsigned char, smem));
+  const uint32_t rows8 = (uint32_t)(8 * row_bytes);
+  // LDS tile layout: the one-block kernel's.  A 64-key slot is 16 blocks of
+  // 1 KiB; block 2*kg + hf holds keys 8*kg .. +7 (kg = 0..7) and bytes
+  // 128*hf .. +127 of each key row, in 16-byte pieces (key k' = key%8, chunk
+  // c = 0..7) placed with an XOR swizzle:
+  //   K: piece (k', c) at 128*k' + 16*(c ^ k' ^ (kg & 1));
+  //   V: piece (k', c) at 128*k' + 16*(c ^ 2*(k' & 3)).
+  // Key groups 0-3 hold A's half tile (or the shared one), 4-7 B's.  A
+  // paired step has wave w fetch key groups 2w, 2w+1 (keys 16*(w&1) .. +15
+  // of its block's half tile); a shared step has wave w fetch key group w.
+  const uint32_t chk = (uint32_t)((lane & 7) ^ (lane >> 3));
+  const uint32_t row_lane = (uint32_t)(lane >> 3) * (uint32_t)row_bytes + (uint32_t)h * 256u;
+  const uint32_t k_lane_p = row_lane + 16u * chk;
+  const uint32_t k_lane_s = row_lane + 16u * (chk ^ (uint32_t)(wave & 1));
+  const uint32_t v_lane = row_lane + 16u * (uint32_t)((lane & 7) ^ (2 * ((lane >> 3) & 3)));
+  auto issue_k = [&](int kA, int kB, int slot) {
+    const uint32_t lb = lds0 + kPKOff + (uint32_t)(slot * 16384);
+    if (kA != kB) {
+      const int kk = wave < 2 ? kA : kB;
+      if (kk >= T) return;
+      const uint32_t base = (uint32_t)(kk + 16 * (wave & 1)) * (uint32_t)row_bytes + k_lane_p;
+      const uint32_t l = lb + 4096u * (uint32_t)wave;
+      lds_dma_b128<0>(rk, base, l);
+      lds_dma_b128<1024>(rk, base + 128, l);
+      // odd key group: chunk parity flipped (the chunk term is the only part
+      // of the offset below 256)
+      lds_dma_b128<2048>(rk, (base ^ 16u) + rows8, l);
+      lds_dma_b128<3072>(rk, (base ^ 16u) + rows8 + 128, l);
+    } else {
+      if (kA >= T) return;
+      const uint32_t base = (uint32_t)(kA + 8 * wave) * (uint32_t)row_bytes + k_lane_s;
+      const uint32_t l = lb + 2048u * (uint32_t)wave;
+      lds_dma_b128<0>(rk, base, l);
+      lds_dma_b128<1024>(rk, base + 128, l);
+    }
+  };
+  auto issue_v = [&](int kA, int kB, int slot, bool with_bias) {
+    const uint32_t lb = lds0 + kPVOff + (uint32_t)(slot * 16384);
+    if (kA != kB) {
+      const int kk = wave < 2 ? kA : kB;
+      if (kk < T) {
+        const uint32_t base = (uint32_t)(kk + 16 * (wave & 1)) * (uint32_t)row_bytes + v_lane;
+        const uint32_t l = lb + 4096u * (uint32_t)wave;
+        lds_dma_b128<0>(rv, base, l);
+        lds_dma_b128<1024>(rv, base + 128, l);
+        lds_dma_b128<2048>(rv, base + rows8, l);
+        lds_dma_b128<3072>(rv, base + rows8 + 128, l);
+      }
+    } else if (kA < T) {
+      const uint32_t base = (uint32_t)(kA + 8 * wave) * (uint32_t)row_bytes + v_lane;
+      const uint32_t l = lb + 2048u * (uint32_t)wave;
+      lds_dma_b128<0>(rv, base, l);
+      lds_dma_b128<1024>(rv, base + 128, l);
+    }
+    // natural-log bias of both half tiles (lanes 0-31: A's keys, 32-63:
+    // B's); keys of non-sink blocks and past T read as zero
+    if (with_bias && wave == 0) {
+      const int k0 = lane < 32 ? kA : kB;
+      const int key = k0 + (lane & 31);
+      const bool sink = k0 >= sink0 && key < T;
+      lds_dma_b32(rb, sink ? (uint32_t)key * 4u : (uint32_t)T * 4u, lds0 + kPBOff + (uint32_t)(slot * 256));
+    }
+  };
+  // operand read bases (bytes within a slot half); the other operand bases
+  // differ by an XOR of the swizzled chunk bits: K chunk 2*(dc%4) + g lands
+  // at k_rd0 ^ (32*(dc%4)); V for odd dt at v_rd0 ^ 64.
+  uint32_t k_rd0, v_rd0;
+  {
+    const uint32_t kp = (uint32_t)(c32 & 7);
+    k_rd0 = (uint32_t)(2048 * (c32 >> 3)) + 128 * kp + 16 * ((uint32_t)g ^ kp ^ (uint32_t)((c32 >> 3) & 1));
+    const uint32_t r = (uint32_t)((lane & 15) >> 2), dh = (uint32_t)((lane >> 4) & 1), j = (uint32_t)(lane & 3);
+    v_rd0 = (uint32_t)(512 * g) + 128 * r + 8 * (j & 1) + 16 * ((2 * dh + (j >> 1)) ^ (2 * r));
+  }
+
+  // ---- state --------------------------------------------------------------
+  float m_used = -INFINITY;   // running max (log2 units) used for P
+  float l_run = 0.f;          // this lane's share of the row sum
+  f32x16 o[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  const float c = p.scale_log2;
+
+  // Half of a slot this wave reads in a step with tiles (kA, kB): its own
+  // block's half when the entry is paired, else the first half.
+  auto rhalf = [&](int kA, int kB) -> uint32_t { return (blk != 0 && kA != kB) ? 8192u : 0u; };
+
+  // One pipeline step on half tile j (scores in s_cur, V in slot VS, this
+  // wave's first key my_key, read half rh) that also computes S(j+1) into
+  // s_nxt from K slot VS^1, half rh_n, when DO_QK.
+  auto step = [&](auto vs_c, auto biased_c, auto masked_c, auto do_qk_c, f32x16 &s_cur, f32x16 &s_nxt,
+                  int my_key, uint32_t rh, uint32_t rh_n, auto dma_k, auto dma_v) {
+    constexpr int VS = decltype(vs_c)::value;
+    constexpr bool BIASED = decltype(biased_c)::value;
+    constexpr bool MASKED = decltype(masked_c)::value;
+    constexpr bool DO_QK = decltype(do_qk_c)::value;
+    const unsigned char *vbuf = smem + kPVOff + VS * 16384 + rh;
+    const unsigned char *kbuf = smem + kPKOff + (VS ^ 1) * 16384 + rh_n;
+    const float *bs = reinterpret_cast<const float *>(smem + kPBOff + VS * 256 + (rh >> 6));
+
+    auto qk_part = [&](auto lo_c, auto hi_c) {
+      constexpr int LO = decltype(lo_c)::value;
+      constexpr int HI = decltype(hi_c)::value;
+#pragma unroll
+      for (int dc = LO; dc < HI; ++dc) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(kbuf + (k_rd0 ^ (32u * (dc & 3))) + 1024 * (dc >> 2));
+        s_nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[dc], s_nxt, 0, 0, 0);
+      }
+    };
+    auto bias4 = [&](int q4) {
+      const float4 b4 = *reinterpret_cast<const float4 *>(bs + 8 * q4 + 4 * g);
+      return make_float4(b4.x * kLog2e, b4.y * kLog2e, b4.z * kLog2e, b4.w * kLog2e);
+    };
+    // tile max of this lane's logits (log2 units), then the rare rescale
+    auto tile_max = [&]() -> float {
+      float mt;
+      if (BIASED) {
+        mt = -INFINITY;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const float4 bq = bias4(q4);
+          mt = fmaxf(mt, __builtin_fmaf(s_cur[4 * q4 + 0], c, bq.x));
+          mt = fmaxf(mt, __builtin_fmaf(s_cur[4 * q4 + 1], c, bq.y));
+          mt = fmaxf(mt, __builtin_fmaf(s_cur[4 * q4 + 2], c, bq.z));
+          mt = fmaxf(mt, __builtin_fmaf(s_cur[4 * q4 + 3], c, bq.w));
+        }
+      } else {
+        float mx = s_cur[0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s_cur[r]);
+        mt = mx * c;
+      }
+      return max_with_partner(mt);
+    };
+    auto rescale = [&](float mt) {
+      if (__any(mt > m_used + kRescaleSlack)) {
+        const float m_new = fmaxf(m_used, mt);
+        const float alpha = __builtin_amdgcn_exp2f(m_used - m_new);  // 0 when m_used = -inf
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+        m_used = m_new;
+      }
+    };
+    bf16x8 pf[2];
+    auto exps = [&](float m_sub) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        float e[4];
+        if (BIASED) {
+          const float4 bq = bias4(q4);
+          e[0] = __builtin_fmaf(s_cur[4 * q4 + 0], c, bq.x - m_sub);
+          e[1] = __builtin_fmaf(s_cur[4 * q4 + 1], c, bq.y - m_sub);
+          e[2] = __builtin_fmaf(s_cur[4 * q4 + 2], c, bq.z - m_sub);
+          e[3] = __builtin_fmaf(s_cur[4 * q4 + 3], c, bq.w - m_sub);
+        } else {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) e[u] = __builtin_fmaf(s_cur[4 * q4 + u], c, -m_sub);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; u += 2) {
+          const int r = 4 * q4 + u;
+          const bf16x2 pk = {(__bf16)__builtin_amdgcn_exp2f(e[u]), (__bf16)__builtin_amdgcn_exp2f(e[u + 1])};
+          l_run = __builtin_amdgcn_fdot2_f32_bf16(pk, ones, l_run, false);
+          pf[r >> 3][r & 7] = pk[0];
+          pf[r >> 3][(r & 7) + 1] = pk[1];
+        }
+      }
+    };
+    auto pv = [&]() {
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          const unsigned char *src = vbuf + ((dt & 1) ? (v_rd0 ^ 64u) : v_rd0) + 4096 * kc + 1024 * (dt >> 1);
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, src));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, src + 2048));
+          const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kc], o[dt], 0, 0, 0);
+        }
+      }
+    };
+
+    if (MASKED) {
+      // general step: copies and S(j+1) first, then this wave's tile if it
+      // has one
+      dma_k();
+      dma_v();
+      if (DO_QK) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s_nxt[r] = 0.f;
+        qk_part(Int<0>{}, Int<8>{});
+      }
+      if (my_key >= T) return;     // this wave's block has no tile in this step
+      const int kbase = my_key + 4 * g;   // key of s[r] = kbase + 8*(r/4) + r%4
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (kbase + 8 * (r >> 2) + (r & 3) >= T) s_cur[r] = -INFINITY;
+      rescale(tile_max());
+      exps(m_used == -INFINITY ? 0.f : m_used);
+      pv();
+      return;
+    }
+
+    if (kDmaAt == 0 || kDmaAt == 2) dma_k();
+    if (kDmaAt == 0 || kDmaAt == 4) dma_v();
+    // -- block A: max of tile j (+ first S(j+1) MFMAs) --
+    if (DO_QK) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s_nxt[r] = 0.f;
+      qk_part(Int<0>{}, Int<3>{});
+    }
+    const float mt = tile_max();
+    if (DO_QK) {
+      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 3, 0);
+#pragma unroll
+      for (int i = 0; i < 3; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedVALU, 4, 0);
+      }
+    }
+    if (kDmaAt == 1 || kDmaAt == 3 || kDmaAt == 4) dma_k();
+    if (kDmaAt == 1 || kDmaAt == 2) dma_v();
+    rescale(mt);
+    const float m_sub = (m_used == -INFINITY) ? 0.f : m_used;
+
+    // -- block B: P of tile j (+ remaining S(j+1) MFMAs), raised priority --
+    __builtin_amdgcn_s_setprio(1);
+    if (DO_QK) qk_part(Int<3>{}, Int<8>{});
+    exps(m_sub);
+    if (DO_QK) {
+      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 2, 0);
+#pragma unroll
+      for (int i = 0; i < 3; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedVALU, 8, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedVALU, 8, 0);
+      }
+    }
+    if (kDmaAt == 3) dma_v();
+    // -- block C: O^T += V^T P^T over the half tile's 32 keys --
+    pv();
+    __builtin_amdgcn_s_setprio(0);
+  };
+
+  // ---- pipeline -----------------------------------------------------------
+  // Step j = 2e + half works on half `half` of entry e.  K(j) lives in K slot
+  // j%2 and V(j) in V slot j%2; K is fetched two steps ahead, V one ahead.
+  // Step j issues V(j+1) and K(j+2) into the slots step j-1 finished
+  // reading, and ends with the barrier that publishes them.
+  int ea = -1, eb = -1, na = -1, nb2 = -1;
+  if (nE > 0) entry(0, ea, eb);
+  if (nE > 1) entry(1, na, nb2);
+  if (nE > 0) {
+    issue_k(hkey(ea, 0), hkey(eb, 0), 0);
+    issue_v(hkey(ea, 0), hkey(eb, 0), 0, has_bias && nU == 0);
+    issue_k(hkey(ea, 1), hkey(eb, 1), 1);
+  }
+  __builtin_amdgcn_s_waitcnt(kVmcntZero);
+  __syncthreads();
+  f32x16 s0, s1;
+  if (nE > 0) {
+    const unsigned char *kb0 = smem + kPKOff + rhalf(hkey(ea, 0), hkey(eb, 0));
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s0[r] = 0.f;
+#pragma unroll
+    for (int dc = 0; dc < 8; ++dc) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8 *>(kb0 + (k_rd0 ^ (32u * (dc & 3))) + 1024 * (dc >> 2));
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[dc], s0, 0, 0, 0);
+    }
+  }
+  // Step 0 refills K slot 0: every wave must be done reading it.
+  __syncthreads();
+
+  // Both steps of entry e (not the last entry), with (na, nb2) = entry e+1.
+  // PH: 0 unbiased, 1 biased, 2 general (masked; biased when key_bias).
+  auto run_entry = [&](auto biased_c, auto masked_c, int e) {
+    const int a0 = hkey(ea, 0), b0 = hkey(eb, 0), a1 = hkey(ea, 1), b1 = hkey(eb, 1);
+    const int n0a = hkey(na, 0), n0b = hkey(nb2, 0), n1a = hkey(na, 1), n1b = hkey(nb2, 1);
+    const bool nbias = has_bias && e + 1 >= nU;
+    const bool cbias = has_bias && e >= nU;
+    // half 0
+    step(Int<0>{}, biased_c, masked_c, Bool<true>{}, s0, s1, blk ? b0 : a0, rhalf(a0, b0), rhalf(a1, b1),
+         [&] { issue_k(n0a, n0b, 0); }, [&] { issue_v(a1, b1, 1, cbias); });
+    __builtin_amdgcn_s_waitcnt(kVmcntZero);
+    __syncthreads();
+    // half 1
+    step(Int<1>{}, biased_c, masked_c, Bool<true>{}, s1, s0, blk ? b1 : a1, rhalf(a1, b1), rhalf(n0a, n0b),
+         [&] { issue_k(n1a, n1b, 1); }, [&] { issue_v(n0a, n0b, 0, nbias); });
+    __builtin_amdgcn_s_waitcnt(kVmcntZero);
+    __syncthreads();
+    ea = na;
+    eb = nb2;
+    if (e + 2 < nE) entry(e + 2, na, nb2);
+  };
+  // The last entry: half 0 computes S of half 1; half 1 ends the walk.
+  auto last_entry = [&](auto biased_c, auto masked_c, int e) {
+    const int a0 = hkey(ea, 0), b0 = hkey(eb, 0), a1 = hkey(ea, 1), b1 = hkey(eb, 1);
+    const bool cbias = has_bias && e >= nU;
+    step(Int<0>{}, biased_c, masked_c, Bool<true>{}, s0, s1, blk ? b0 : a0, rhalf(a0, b0), rhalf(a1, b1),
+         [] {}, [&] { issue_v(a1, b1, 1, cbias); });
+    __builtin_amdgcn_s_waitcnt(kVmcntZero);
+    __syncthreads();
+    step(Int<1>{}, biased_c, masked_c, Bool<false>{}, s1, s0, blk ? b1 : a1, rhalf(a1, b1), 0u, [] {}, [] {});
+  };
+  // Each loop body holds one step variant only: a runtime choice between
+  // variants inside a loop makes the compiler route the accumulators through
+  // copies every step.
+  int e = 0;
+  const int nUB = nU + nBi;
+  for (; e < nU && e + 1 < nE; ++e) run_entry(Bool<false>{}, Bool<false>{}, e);
+  for (; e < nUB && e + 1 < nE; ++e) run_entry(Bool<true>{}, Bool<false>{}, e);
+  if (has_bias) {
+    for (; e + 1 < nE; ++e) run_entry(Bool<true>{}, Bool<true>{}, e);
+  } else {
+    for (; e + 1 < nE; ++e) run_entry(Bool<false>{}, Bool<true>{}, e);
+  }
+  if (e < nE) {
+    if (e < nU) last_entry(Bool<false>{}, Bool<false>{}, e);
+    else if (e < nUB) last_entry(Bool<true>{}, Bool<false>{}, e);
+    else if (has_bias) last_entry(Bool<true>{}, Bool<true>{}, e);
+    else last_entry(Bool<false>{}, Bool<true>{}, e);
+  }
+
+  // ---- epilogue -----------------------------------------------------------
+  if (!active) return;
+  const float l_tot = add_with_partner(l_run);
+  if (kDense && p.nsplit > 1) {
+    if (tq >= T) return;
+    // partial (unnormalised O, max, sum) of this key range
+    const int64_t prow = (((int64_t)bh * p.nqb + qbi) * p.nsplit + split) * kBlock + (rw * 32 + c32);
+    float *po = p.part_o + prow * kHeadDim;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d0 = 32 * dt + 8 * q4 + 4 * g;
+        *reinterpret_cast<float4 *>(po + d0) =
+            make_float4(o[dt][4 * q4 + 0], o[dt][4 * q4 + 1], o[dt][4 * q4 + 2], o[dt][4 * q4 + 3]);
+      }
+    if (g == 0) *reinterpret_cast<float2 *>(p.part_ml + 2 * prow) = make_float2(m_used, l_tot);
+    return;
+  }
+  // The wave's 32 rows (256 B each) go through LDS (8 KiB of the K ring per
+  // wave, unused since the last step reads no K; 16-byte chunks XOR-swizzled
+  // by row) and out as whole rows: each store instruction writes 4 rows.
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  unsigned char *stage = smem + kPKOff + 8192 * wave;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      uint2 val;
+      val.x = pack_bf16x2(o[dt][4 * q4 + 0] * inv, o[dt][4 * q4 + 1] * inv);
+      val.y = pack_bf16x2(o[dt][4 * q4 + 2] * inv, o[dt][4 * q4 + 3] * inv);
+      *reinterpret_cast<uint2 *>(stage + c32 * 256 + 16 * ((4 * dt + q4) ^ (c32 & 15)) + 8 * g) = val;
+    }
+  const int row0 = qb * kBlock + rw * 32;
+  uint16_t *ob = p.out + bbase + h * kHeadDim;
+  const int ch = lane & 15;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = 4 * i + (lane >> 4);
+    const uint4 val = *reinterpret_cast<const uint4 *>(stage + r * 256 + 16 * (ch ^ (r & 15)));
+    if (row0 + r >= p.row_lo && row0 + r < p.row_hi)
+      *reinterpret_cast<uint4 *>(ob + (int64_t)(row0 + r) * rs + 8 * ch) = val;
+  }
+  if (p.lse != nullptr && g == 0 && tq >= p.row_lo && tq < p.row_hi)
+    p.lse[((int64_t)b * p.H + h) * T + tq] = (m_used + __log2f(l_tot)) * kLn2;
+}
+
+constexpr int kPairDmaAt = 3;
+
+PairParams make_pair_params(const AttnArgs &a, int qb0, int nqb) {
+  PairParams p{};
+  p.q = static_cast<const uint16_t *>(a.q);
+  p.k = static_cast<const uint16_t *>(a.k);
+  p.v = static_cast<const uint16_t *>(a.v);
+  p.out = static_cast<uint16_t *>(a.out);
+  p.lse = a.lse;
+  p.key_bias = a.key_bias;
+  p.block_idx = a.block_idx;
+  p.block_cnt = a.block_cnt;
+  p.B = a.B;
+  p.T = a.T;
+  p.H = a.H;
+  p.nb = a.nb;
+  p.nvb = a.nvb;
+  p.max_sel = a.max_sel;
+  p.qb0 = qb0;
+  p.nqb = nqb;
+  p.npair = (nqb + 1) / 2;
+  p.row_lo = 0;
+  p.row_hi = a.T;
+  p.nsplit = 1;
+  p.tiles_per_split = a.nb;
+  p.scale_log2 = a.scale_log2;
+  return p;
+}
+
+}  // namespace
+
+int dense_pair_splits(int B, int H, int nb, int nvb) {
+  const int nq = nb - nvb;
+  if (nq <= 0) return 1;
+  const int64_t units = (int64_t)B * H * ((nq + 1) / 2);
+  // Choose the key split that minimises (rounds of resident workgroups) x
+  // (key blocks per split + the fixed cost of a workgroup, about 8 blocks:
+  // prologue, stores, partial results).  Two workgroups fit a CU and the
+  // device has 256 CUs.  Splits keep at least 8 blocks each; among equal
+  // costs the fewer splits win (less partial traffic for the combine).
+  constexpr int64_t kSlots = 2 * 256;
+  constexpr int64_t kFixedTiles = 8;
+  const int max_s = nb / 8 > 1 ? nb / 8 : 1;
+  int best = 1;
+  int64_t best_cost = -1;
+  for (int s = 1; s <= max_s; ++s) {
+    const int per = (nb + s - 1) / s;
+    const int se = (nb + per - 1) / per;          // splits after equalising
+    if (se != s) continue;
+    const int64_t rounds = (units * se + kSlots - 1) / kSlots;
+    const int64_t cost = rounds * (per + kFixedTiles);
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      best = se;
+    }
+  }
+  return best;
+}
+
+hipError_t launch_attn_pair_sparse(const AttnArgs &a, hipStream_t stream) {
+  if (a.nvq <= 0) return hipSuccess;
+  if (a.max_sel > kMaxPairList) return hipErrorInvalidValue;
+  PairParams p = make_pair_params(a, 0, a.nvq);
+  p.row_hi = a.rows_end;
+  const int total = a.B * a.H * p.npair;
+  hipLaunchKernelGGL((attn_pair_kernel<false, kPairDmaAt>), dim3(total), dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_pair_dense(const AttnArgs &a, float *part_o, float *part_ml, int nsplit,
+                                  hipStream_t stream) {
+  const int nq = a.nb - a.nvb;
+  PairParams p = make_pair_params(a, a.nvb, nq);
+  p.row_lo = a.rows_end;
+  if (nsplit > 1) {
+    p.nsplit = nsplit;
+    p.tiles_per_split = (a.nb + nsplit - 1) / nsplit;
+    p.part_o = part_o;
+    p.part_ml = part_ml;
+  }
+  const int total = a.B * a.H * p.npair * p.nsplit;
+  hipLaunchKernelGGL((attn_pair_kernel<true, kPairDmaAt>), dim3(total), dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace sa

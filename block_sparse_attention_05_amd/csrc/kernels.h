@@ -22,6 +22,9 @@ sa_status check_route_args(const void *q, const void *k, int32_t B, int32_t T, i
 constexpr int kBlock = 64;     // tokens per routing block
 constexpr int kHeadDim = 128;  // head dimension
 constexpr int kMaxRouteBlocks = 1024;  // widest per-row sort in the route kernel
+// Longest list (max_sel) the paired-block attention kernel serves; longer
+// lists take the one-block kernel.
+constexpr int kMaxPairList = 512;
 
 // Means of the routed blocks: Q blocks [0, nvq) over rows below q_end (a
 // split last block only over its real rows), K blocks [0, nvb), in the route
@@ -74,6 +77,15 @@ hipError_t launch_attn_dense(const AttnArgs &a, void *workspace, size_t workspac
                              hipStream_t stream);
 int dense_splits(int B, int H, int nb, int nvb);
 size_t dense_workspace_bytes(int B, int H, int nb, int nvb);
+
+// Paired query blocks (attn_pair.hip): one workgroup serves query blocks
+// 2p and 2p+1 of a (b, h) and loads a key tile once when both lists hold
+// it.  Sparse rows (needs max_sel <= kMaxPairList), and the dense rows with
+// nsplit key ranges (partials to part_o / part_ml when nsplit > 1).
+hipError_t launch_attn_pair_sparse(const AttnArgs &a, hipStream_t stream);
+hipError_t launch_attn_pair_dense(const AttnArgs &a, float *part_o, float *part_ml, int nsplit,
+                                  hipStream_t stream);
+int dense_pair_splits(int B, int H, int nb, int nvb);
 
 // Spark summaries (spark.hip).
 // Global anchor: mean of the video rows [0, sink_start) of Q per (b, h),

@@ -85,15 +85,15 @@ def _dense_splits(L, B, T, H, ss):
 
 
 def test_dense_split_choice(L):
-    # H3: 280 dense (head, block) units.  5 splits of 30 tiles = 1400
-    # workgroups in three rounds of 512 slots; 4 splits (38 tiles) leave the
-    # third round 19% full, 7 (22 tiles) and 9 (17) need 4 and 5 rounds.
-    assert _dense_splits(L, 1, 9505, 56, 9216) == 5
-    # Mid (8 heads): 32 units; 15 splits of 9 tiles (480 workgroups) fit one round
+    # Workgroups serve pairs of dense query blocks.  H3: 5 dense blocks ->
+    # 3 pairs x 56 heads = 168 units; 3 splits of 50 blocks = 504 workgroups
+    # fit one round of 512 slots, 4 splits (38 blocks) need two.
+    assert _dense_splits(L, 1, 9505, 56, 9216) == 3
+    # Mid (8 heads): 16 units; 15 splits of 9 blocks (240 workgroups), one round
     assert _dense_splits(L, 1, 8448, 8, 8192) == 15
-    # the same sequence with 56 heads: 224 units, 2 splits of 66 tiles in one round
-    assert _dense_splits(L, 1, 8448, 56, 8192) == 2
-    # a few units: split down to the 8-tile minimum (202 tiles -> 23 x 9)
+    # the same sequence with 56 heads: 112 units, 4 splits of 33 blocks in one round
+    assert _dense_splits(L, 1, 8448, 56, 8192) == 4
+    # a few units: split down to the 8-block minimum (202 blocks -> 23 x 9)
     assert _dense_splits(L, 1, 64 * 200 + 100, 2, 64 * 200) == 23
     # every split keeps at least 8 tiles
     for T, H, ss in ((1100, 3, 1000), (33280, 24, 32768), (65736, 2, 65536), (9505, 1, 9216)):

@@ -133,14 +133,20 @@ def test_pad_without_complete_video_block():
 
 
 def test_pad_and_dense_modes_share_bits_where_they_must():
-    """Complete video blocks and context rows are the same computation in
-    both modes (same lists, same kernels, same key splits): equal bits.  With
-    a block-aligned boundary the whole call is equal."""
+    """Where the two modes run the same computation they give the same bits:
+    the lists of the complete video blocks, the outputs of the query-block
+    pairs that are the same in both modes (blocks 0-13; block 14 is alone in
+    dense mode and paired with the split block in pad mode, so its tiles are
+    summed in another order) and the context rows.  With a block-aligned
+    boundary the whole call is equal."""
     a = run_gpu(_split_workload("dense"))
     b = run_gpu(_split_workload("pad"))
     ss = 1024 - 17
     assert torch.equal(a["idx"], b["idx"][:, :, :-1]) and torch.equal(a["cnt"], b["cnt"][:, :, :-1])
-    assert torch.equal(a["out"][:, :960], b["out"][:, :960])
+    assert torch.equal(a["out"][:, :896], b["out"][:, :896])
+    d = (a["out"][:, 896:960].float() - b["out"][:, 896:960].float()).abs().max().item()
+    log(f"[pad vs dense] block 14 max_abs={d:.3e}")
+    assert d <= 1e-2
     assert torch.equal(a["out"][:, ss:], b["out"][:, ss:])
     assert torch.equal(a["lse"][:, :, ss:], b["lse"][:, :, ss:])
     assert not torch.equal(a["out"][:, 960:ss], b["out"][:, 960:ss])

@@ -162,9 +162,13 @@ def test_spark_no_bias_split_block():
         _spark_parity(q, k, v, ss, 0.2, 1, f"spark_nobias_split_{mode}", tail_mode=mode)
 
 
-def test_spark_ratio_one_bit_identical_to_exact():
-    """Nothing skipped: every virtual key is masked and the result must be
-    the exact path's, bit for bit."""
+def test_spark_ratio_one_equals_exact():
+    """Nothing skipped: every virtual key is masked, so the result is the
+    exact path's up to the summation order of the tiles and the points where
+    the running max is rescaled (the approximate branch serves one query
+    block per workgroup, sparse_attn_fwd two), within the oracle tolerance.
+    One leaked virtual key would carry about a block's worth of mass and move
+    LSE and outputs by several hundredths."""
     import block_sparse_attention_05_amd as sa
     q, k, v, ss = _split_case(seed=12)
     qc, kc, vc = q.cuda(), k.cuda(), v.cuda()
@@ -177,7 +181,10 @@ def test_spark_ratio_one_bit_identical_to_exact():
     b = sa.sparse_attn_fwd_spark(qc, kc, vc, ss, idx, cnt, summ, key_bias=bias, lse=lse_b)
     torch.cuda.synchronize()
     rows = 64 * (ss // 64)
-    assert torch.equal(a[:, :rows], b[:, :rows]) and torch.equal(lse_a[:, :, :rows], lse_b[:, :, :rows])
+    d = (a[:, :rows].float() - b[:, :rows].float()).abs().max().item()
+    dl = (lse_a[:, :, :rows] - lse_b[:, :, :rows]).abs().max().item()
+    log(f"[spark ratio 1] vs exact path: out max_abs={d:.3e} lse max_abs={dl:.3e}")
+    assert d <= 1e-2 and dl <= 1e-2
 
 
 def test_spark_h3_full():
