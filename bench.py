@@ -50,8 +50,9 @@ import torch  # noqa: E402
 BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 HBM_PEAK_GBPS = 8000.0
 METRIC = "ms/call and effective TFLOP/s (frac of bf16 peak), B1 H56 T9505 D128 top-k 0.1"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_sparse_h3_traffic.json")
-ATTN_SRC = os.path.join(ROOT, "block_sparse_attention_05_amd", "csrc", "attn.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_pair_sparse_h3_traffic.json")
+ATTN_SRC = os.path.join(ROOT, "block_sparse_attention_05_amd", "csrc", "attn_pair.hip")
+SPARSE_KERNEL = "attn_pair_kernel<false, 3>"
 
 
 def effective_flops_from_lists(cnt, idx, T, nvb, H, B):
@@ -314,6 +315,22 @@ def main():
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
 
+    # the same back-to-back loop once more with an event between consecutive
+    # steps (GPU time of each step in order, gaps between steps included) and
+    # the host's enqueue time per step, to see where the back-to-back mean
+    # and the per-call times part
+    sev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    host_us = []
+    torch.cuda.synchronize()
+    sev[0].record(stream)
+    for i in range(args.steps):
+        h0 = time.perf_counter()
+        step()
+        sev[i + 1].record(stream)
+        host_us.append((time.perf_counter() - h0) * 1e6)
+    torch.cuda.synchronize()
+    seq_ms = [sev[i].elapsed_time(sev[i + 1]) for i in range(args.steps)]
+
     # per-call distribution of the same schedule: an event pair around every
     # call (the events sit on the main stream, which joins the side stream)
     cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -370,6 +387,9 @@ def main():
                    "sink_tokens": T - ss, "topk_ratio": wl.topk_ratio, "local_radius": wl.local_radius,
                    "key_bias": kb is not None, "inputs": "smooth-field+noise Q/K, N(0,1) V, seed 2"},
         "ms_per_call": round(ms, 4),
+        "back_to_back_steps_ms_in_order": [round(x, 4) for x in seq_ms],
+        "host_enqueue_us_per_step_median_max": [round(float(np.median(host_us)), 1),
+                                                round(float(np.max(host_us)), 1)],
         "ms_per_call_median_p10_p90": [round(float(np.median(calls)), 4),
                                        round(float(np.percentile(calls, 10)), 4),
                                        round(float(np.percentile(calls, 90)), 4)],
@@ -385,7 +405,7 @@ def main():
         "attention_only_frac_of_bf16_peak": round(total_flops / ((med[1] + med[2]) * 1e-3) / 1e12
                                                   / BF16_PEAK_TFLOPS, 4),
         "peak_device_tflops": peak_dev,
-        "roofline": {"kernel": "attn_fwd_kernel<sparse>", "bound": "mfma", "achieved": round(achieved, 3),
+        "roofline": {"kernel": SPARSE_KERNEL, "bound": "mfma", "achieved": round(achieved, 3),
                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
                      "algorithmic_gflop_per_launch": round(sparse_flops / 1e9, 3),
                      "launch_ms_mean": round(sparse_ms, 4),

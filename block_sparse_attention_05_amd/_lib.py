@@ -13,7 +13,10 @@ from typing import Optional, Tuple
 
 import torch
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsparse_attn.so")
+# SA_LIBRARY selects another build of the same library (the sanitizer
+# build of the host validation tests); by default the in-tree one.
+LIB_PATH = os.environ.get("SA_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                         "libsparse_attn.so")
 
 SA_OK, SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_WORKSPACE, SA_ERR_HIP = range(5)
 HEAD_DIM = 128

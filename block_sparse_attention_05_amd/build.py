@@ -52,26 +52,42 @@ def _run(cmd, verbose):
     return out
 
 
-def build(verbose: bool = False, extra_flags=()) -> str:
+# Host-side AddressSanitizer + UndefinedBehaviorSanitizer build of the same
+# sources (device code is compiled as usual): `python -m
+# block_sparse_attention_05_amd.build --sanitize` writes it to
+# _build/sanitize/libsparse_attn.so, for the host validation tests.
+SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer",
+                  "-g"]
+SANITIZE_DIR = os.path.join(BUILD_DIR, "sanitize")
+
+
+def build(verbose: bool = False, extra_flags=(), sanitize: bool = False) -> str:
     """Compile every source for gfx950 and link the shared library.
-    Always recompiles.  Returns the library path."""
+    Always recompiles.  Returns the library path.  With ``sanitize`` the
+    host code is built with ASan/UBSan into _build/sanitize/ instead."""
     hipcc = _hipcc()
-    os.makedirs(BUILD_DIR, exist_ok=True)
+    out_dir = SANITIZE_DIR if sanitize else BUILD_DIR
+    lib_path = os.path.join(SANITIZE_DIR, LIB_NAME) if sanitize else LIB_PATH
+    if sanitize:
+        extra_flags = (*extra_flags, *SANITIZE_FLAGS)
+    os.makedirs(out_dir, exist_ok=True)
     objs = []
     jobs = []
     for src in SOURCES:
-        obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+        obj = os.path.join(out_dir, os.path.splitext(src)[0] + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
         cmd = [hipcc, *COMMON_FLAGS, *extra_flags, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
         jobs.append(cmd)
         objs.append(obj)
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
         list(ex.map(lambda c: _run(c, verbose), jobs))
-    tmp = LIB_PATH + ".tmp"
-    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    tmp = lib_path + ".tmp"
+    link_extra = ["-fsanitize=address", "-fsanitize=undefined"] if sanitize else []
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *link_extra, "-o", tmp, *objs], verbose)
+    os.replace(tmp, lib_path)
+    return lib_path
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, sanitize="--sanitize" in sys.argv))

@@ -240,11 +240,13 @@ __device__ __forceinline__ void pair_emit(const PairParams &p, unsigned char *sm
   }
 }
 
+// kPlan: 0 the step's PV MFMAs run after all its exponentials; 1 the
+// exponentials of the second 16 keys run beside the PV MFMAs of the first.
 // kDmaAt: where a steady-state step issues its copies (V of the next step, K
 // of the step after): 0 both before the step's math, 1 both after the max
 // block, 2 K before and V after the max block, 3 K after the max block and V
 // after the exponentials, 4 V before and K after the max block.
-template <bool kDense, int kDmaAt>
+template <bool kDense, int kDmaAt, int kPlan>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_pair_kernel(PairParams p) {
   __shared__ __align__(16) unsigned char smem[kPLdsBytes];
@@ -541,9 +543,11 @@ void attn_pair_kernel(PairParams p) {
       }
     };
     bf16x8 pf[2];
-    auto exps = [&](float m_sub) {
+    // P of keys 16*h .. +15 of this lane's 32 (q4 = 2h, 2h+1) into pf[h]
+    auto exps_half = [&](float m_sub, auto h_c) {
+      constexpr int H0 = 2 * decltype(h_c)::value;
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
+      for (int q4 = H0; q4 < H0 + 2; ++q4) {
         float e[4];
         if (BIASED) {
           const float4 bq = bias4(q4);
@@ -565,18 +569,25 @@ void attn_pair_kernel(PairParams p) {
         }
       }
     };
-    auto pv = [&]() {
+    auto exps = [&](float m_sub) {
+      exps_half(m_sub, Int<0>{});
+      exps_half(m_sub, Int<1>{});
+    };
+    // O^T += V^T P^T over keys 16*kc .. +15 of the half tile
+    auto pv_half = [&](auto kc_c) {
+      constexpr int KC = decltype(kc_c)::value;
 #pragma unroll
-      for (int kc = 0; kc < 2; ++kc) {
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          const unsigned char *src = vbuf + ((dt & 1) ? (v_rd0 ^ 64u) : v_rd0) + 4096 * kc + 1024 * (dt >> 1);
-          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, src));
-          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, src + 2048));
-          const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kc], o[dt], 0, 0, 0);
-        }
+      for (int dt = 0; dt < 4; ++dt) {
+        const unsigned char *src = vbuf + ((dt & 1) ? (v_rd0 ^ 64u) : v_rd0) + 4096 * KC + 1024 * (dt >> 1);
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, src));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, src + 2048));
+        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[KC], o[dt], 0, 0, 0);
       }
+    };
+    auto pv = [&]() {
+      pv_half(Int<0>{});
+      pv_half(Int<1>{});
     };
 
     if (MASKED) {
@@ -622,27 +633,64 @@ void attn_pair_kernel(PairParams p) {
     rescale(mt);
     const float m_sub = (m_used == -INFINITY) ? 0.f : m_used;
 
-    // -- block B: P of tile j (+ remaining S(j+1) MFMAs), raised priority --
+    if (kPlan == 0) {
+      // -- block B: P of tile j (+ remaining S(j+1) MFMAs), raised priority --
+      __builtin_amdgcn_s_setprio(1);
+      if (DO_QK) qk_part(Int<3>{}, Int<8>{});
+      exps(m_sub);
+      if (DO_QK) {
+        __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 2, 0);
+#pragma unroll
+        for (int i = 0; i < 3; ++i) {
+          __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(kSchedVALU, 8, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(kSchedVALU, 8, 0);
+        }
+      }
+      if (kDmaAt == 3) dma_v();
+      // -- block C: O^T += V^T P^T over the half tile's 32 keys --
+      pv();
+      __builtin_amdgcn_s_setprio(0);
+      return;
+    }
+    // kPlan 1: the exponentials of keys 16-31 run beside the PV MFMAs of
+    // keys 0-15, so that every block of the step pairs MFMAs with VALU work.
+    // -- block B: P of keys 0-15 (+ remaining S(j+1) MFMAs) --
     __builtin_amdgcn_s_setprio(1);
     if (DO_QK) qk_part(Int<3>{}, Int<8>{});
-    exps(m_sub);
+    exps_half(m_sub, Int<0>{});
     if (DO_QK) {
       __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 2, 0);
 #pragma unroll
       for (int i = 0; i < 3; ++i) {
         __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
         __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedVALU, 8, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedVALU, 5, 0);
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedVALU, 8, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedVALU, 5, 0);
       }
     }
     if (kDmaAt == 3) dma_v();
-    // -- block C: O^T += V^T P^T over the half tile's 32 keys --
-    pv();
+    // -- block C: PV of keys 0-15 beside P of keys 16-31 --
+    pv_half(Int<0>{});
+    exps_half(m_sub, Int<1>{});
+    __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedVALU, 6, 0);
+    }
+    // -- block D: PV of keys 16-31 --
+    pv_half(Int<1>{});
     __builtin_amdgcn_s_setprio(0);
   };
 
@@ -773,6 +821,7 @@ void attn_pair_kernel(PairParams p) {
 }
 
 constexpr int kPairDmaAt = 3;
+constexpr int kPairPlan = 0;
 
 PairParams make_pair_params(const AttnArgs &a, int qb0, int nqb) {
   PairParams p{};
@@ -837,7 +886,7 @@ hipError_t launch_attn_pair_sparse(const AttnArgs &a, hipStream_t stream) {
   PairParams p = make_pair_params(a, 0, a.nvq);
   p.row_hi = a.rows_end;
   const int total = a.B * a.H * p.npair;
-  hipLaunchKernelGGL((attn_pair_kernel<false, kPairDmaAt>), dim3(total), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((attn_pair_kernel<false, kPairDmaAt, kPairPlan>), dim3(total), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -853,7 +902,7 @@ hipError_t launch_attn_pair_dense(const AttnArgs &a, float *part_o, float *part_
     p.part_ml = part_ml;
   }
   const int total = a.B * a.H * p.npair * p.nsplit;
-  hipLaunchKernelGGL((attn_pair_kernel<true, kPairDmaAt>), dim3(total), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((attn_pair_kernel<true, kPairDmaAt, kPairPlan>), dim3(total), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

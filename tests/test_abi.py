@@ -12,7 +12,8 @@ import oracle.sparse_attention as ora
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "sparse_attn.h")
-LIBPATH = os.path.join(ROOT, "block_sparse_attention_05_amd", "libsparse_attn.so")
+LIBPATH = os.environ.get("SA_LIBRARY") or os.path.join(ROOT, "block_sparse_attention_05_amd",
+                                                       "libsparse_attn.so")
 
 pytestmark = pytest.mark.skipif(not os.path.exists(LIBPATH), reason="library not built")
 
