@@ -908,6 +908,7 @@ hipError_t launch_attn_sparse_fused(const AttnArgs &a, hipStream_t stream) {
   if (a.nvb > kMaxRouteBlocks || a.max_sel > kMaxRouteBlocks || a.qbar == nullptr ||
       (a.nvb > 0 && a.kbar == nullptr))
     return hipErrorInvalidValue;
+  if (a.max_sel <= kMaxPairList) return launch_attn_pair_fused(a, stream);
   Params p = make_params(a, 0, a.nvq);
   p.row_hi = a.rows_end;
   const int total = a.B * a.H * a.nvq;

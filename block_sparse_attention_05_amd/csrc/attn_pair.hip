@@ -59,6 +59,7 @@
 #include "attn_common.h"
 #include "device_util.h"
 #include "kernels.h"
+#include "select.h"
 
 namespace sa {
 namespace {
@@ -82,6 +83,14 @@ constexpr int kPBlOff = kPAOff + kListBytes;
 constexpr int kSHOff = kPBlOff + kListBytes;
 static_assert(kSHOff + kListBytes <= kPVOff, "build temporaries must fit the K ring");
 
+// Fused route: the two query blocks' pooled means (fp64), their scores and
+// their selected lists, inside the V ring (unused until the first tile
+// loads).
+constexpr int kFqOff = kPVOff;                                  // 2 x 128 fp64
+constexpr int kFsOff = kFqOff + 2 * kHeadDim * 8;               // 2 x kMaxRouteBlocks fp32
+constexpr int kFlOff = kFsOff + 2 * kMaxRouteBlocks * 4;        // 2 x kMaxPairList int32
+static_assert(kFlOff + 2 * kMaxPairList * 4 <= kPVOff + 32768, "fused route scratch must fit the V ring");
+
 struct PairParams {
   const uint16_t *q, *k, *v;
   uint16_t *out;
@@ -95,6 +104,12 @@ struct PairParams {
   int row_lo, row_hi;  // rows written: [row_lo, row_hi)
   int nsplit, tiles_per_split;
   float scale_log2;
+  // fused route: pooled means in the route workspace layout, budget, forced
+  // radius, optional copies of the selected lists
+  const double *qbar;
+  const float *kbar;
+  int budget, radius;
+  int32_t *list_out, *cnt_out;
 };
 
 // Lanes below this one whose bit is set in m.
@@ -124,12 +139,12 @@ __device__ __forceinline__ bool lds_contains(const int *arr, int n, int x) {
 // cnt[3..7] = valid entries of A and B, private entries of A and B, shared
 // entries.
 
-// Pass 1: the valid entries of one list, in order, to dst.  `first` holds entry `lane` of the list
-// (read before anything else), c its length.
-__device__ __forceinline__ void pair_compact(const PairParams &p, int64_t li, int c, int first, int *dst,
-                                             int *n_out, int lane) {
+// Pass 1: the valid entries of one list (lst, global or LDS), in order, to
+// dst.  `first` holds entry `lane` of the list (read before anything else),
+// c its length.
+__device__ __forceinline__ void pair_compact(const PairParams &p, const int32_t *lst, int c, int first,
+                                             int *dst, int *n_out, int lane) {
   c = c < 0 ? 0 : (c > p.max_sel ? p.max_sel : c);
-  const int32_t *lst = p.block_idx + li * p.max_sel;
   int n = 0;
   for (int cb = 0; cb < c; cb += 64) {
     const int e = cb == 0 ? (lane < c ? first : -1) : (cb + lane < c ? lst[cb + lane] : -1);
@@ -246,7 +261,7 @@ __device__ __forceinline__ void pair_emit(const PairParams &p, unsigned char *sm
 // of the step after): 0 both before the step's math, 1 both after the max
 // block, 2 K before and V after the max block, 3 K after the max block and V
 // after the exponentials, 4 V before and K after the max block.
-template <bool kDense, int kDmaAt, int kPlan>
+template <bool kDense, bool kFused, int kDmaAt, int kPlan>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_pair_kernel(PairParams p) {
   __shared__ __align__(16) unsigned char smem[kPLdsBytes];
@@ -282,7 +297,7 @@ void attn_pair_kernel(PairParams p) {
   // B's, all four loads in flight together ahead of the Q rows.
   const int64_t liA = (int64_t)bh * p.nqb + qbiA;
   int lcnt = 0, lfirst = -1;
-  if (!kDense && wave < 2 && (wave == 0 || hasB)) {
+  if (!kDense && !kFused && wave < 2 && (wave == 0 || hasB)) {
     const int64_t li = liA + wave;
     lcnt = p.block_cnt[li];
     if (lane < p.max_sel) lfirst = p.block_idx[li * p.max_sel + lane];
@@ -328,9 +343,72 @@ void attn_pair_kernel(PairParams p) {
     int *cnt = reinterpret_cast<int *>(smem + kPCntOff);
     int *LA = reinterpret_cast<int *>(smem + kLAOff);
     int *LB = reinterpret_cast<int *>(smem + kLBOff);
+    const int32_t *lst = p.block_idx + (liA + wave) * p.max_sel;
+    if (kFused) {
+      // Route of both query blocks inside the workgroup, with the rule of
+      // the route kernel: s_j = fp32 of the fp64 dot product of the fp32
+      // means (fp32 products are exact in fp64), then waves 0 and 1 select
+      // and emit A's and B's lists into LDS.
+      double *qs = reinterpret_cast<double *>(smem + kFqOff);
+      float *sc = reinterpret_cast<float *>(smem + kFsOff);
+      int32_t *fl = reinterpret_cast<int32_t *>(smem + kFlOff);
+      const int ntq = (p.nqb + 15) >> 4, ntk = (p.nvb + 15) >> 4;
+      if (tid < kHeadDim) {   // block A (threads 0-63) or B (64-127), channels 2t, 2t+1
+        const int t = tid & 63;
+        const int qq = p.qb0 + qbiA + (tid >> 6);
+        double2 w2 = make_double2(0.0, 0.0);
+        if (tid < 64 || hasB)
+          w2 = reinterpret_cast<const double2 *>(p.qbar)
+              [(((int64_t)bh * ntq + (qq >> 4)) * 16 + (t & 15)) * 64 + 16 * (t >> 4) + (qq & 15)];
+        qs[(tid >> 6) * kHeadDim + 2 * t] = w2.x;
+        qs[(tid >> 6) * kHeadDim + 2 * t + 1] = w2.y;
+      }
+      __syncthreads();
+      const float4 *kt = reinterpret_cast<const float4 *>(p.kbar) + (int64_t)bh * ntk * 8 * 64;
+      for (int jb = tid; jb < p.nvb; jb += kThreads) {
+        const float4 *kj = kt + (int64_t)(jb >> 4) * 8 * 64 + (jb & 15);
+        double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0, b0 = 0.0, b1 = 0.0, b2 = 0.0, b3 = 0.0;
+#pragma unroll 4
+        for (int u = 0; u < kHeadDim / 4; ++u) {  // channels 4u .. 4u+3
+          const float4 kv = kj[(u & 7) * 64 + 16 * (u >> 3)];
+          a0 = __builtin_fma(qs[4 * u + 0], (double)kv.x, a0);
+          a1 = __builtin_fma(qs[4 * u + 1], (double)kv.y, a1);
+          a2 = __builtin_fma(qs[4 * u + 2], (double)kv.z, a2);
+          a3 = __builtin_fma(qs[4 * u + 3], (double)kv.w, a3);
+          b0 = __builtin_fma(qs[kHeadDim + 4 * u + 0], (double)kv.x, b0);
+          b1 = __builtin_fma(qs[kHeadDim + 4 * u + 1], (double)kv.y, b1);
+          b2 = __builtin_fma(qs[kHeadDim + 4 * u + 2], (double)kv.z, b2);
+          b3 = __builtin_fma(qs[kHeadDim + 4 * u + 3], (double)kv.w, b3);
+        }
+        sc[jb] = (float)((a0 + a1) + (a2 + a3));
+        sc[kMaxRouteBlocks + jb] = (float)((b0 + b1) + (b2 + b3));
+      }
+      __syncthreads();
+      if (wave < 2 && (wave == 0 || hasB)) {
+        const int qq = p.qb0 + qbiA + wave;
+        int32_t *out = fl + wave * kMaxPairList;
+        const float *srow = sc + wave * kMaxRouteBlocks;
+        // slots per lane sized to nvb (the selection loops over all of them)
+        auto sel = [&](auto e_c) {
+          return select_and_emit<decltype(e_c)::value>(srow, qq, p.nvb, p.nb, p.budget, p.radius, p.max_sel,
+                                                      out, nullptr, lane);
+        };
+        const int c = p.nvb <= 128 ? sel(Int<2>{}) : p.nvb <= 192 ? sel(Int<3>{})
+                    : p.nvb <= 256 ? sel(Int<4>{}) : sel(Int<kMaxRouteBlocks / 64>{});
+        if (p.list_out != nullptr) {
+          const int64_t li = liA + wave;
+          for (int x = lane; x < p.max_sel; x += 64) p.list_out[li * p.max_sel + x] = out[x];
+          if (lane == 0) p.cnt_out[li] = c;
+        }
+        wave_lds_sync();
+        lcnt = c;
+        lfirst = lane < p.max_sel ? out[lane] : -1;
+        lst = out;
+      }
+    }
     if (wave == 0 || (wave == 1 && hasB))
-      pair_compact(p, liA + wave, __builtin_amdgcn_readfirstlane(lcnt), lfirst, wave ? LB : LA,
-                   cnt + 3 + wave, lane);
+      pair_compact(p, lst, __builtin_amdgcn_readfirstlane(lcnt), lfirst, wave ? LB : LA, cnt + 3 + wave,
+                   lane);
     __syncthreads();
     if (wave < 2) {
       const int nA = __builtin_amdgcn_readfirstlane(cnt[3]);
@@ -847,6 +925,12 @@ PairParams make_pair_params(const AttnArgs &a, int qb0, int nqb) {
   p.nsplit = 1;
   p.tiles_per_split = a.nb;
   p.scale_log2 = a.scale_log2;
+  p.qbar = a.qbar;
+  p.kbar = a.kbar;
+  p.budget = a.budget;
+  p.radius = a.radius;
+  p.list_out = a.list_out;
+  p.cnt_out = a.cnt_out;
   return p;
 }
 
@@ -886,7 +970,20 @@ hipError_t launch_attn_pair_sparse(const AttnArgs &a, hipStream_t stream) {
   PairParams p = make_pair_params(a, 0, a.nvq);
   p.row_hi = a.rows_end;
   const int total = a.B * a.H * p.npair;
-  hipLaunchKernelGGL((attn_pair_kernel<false, kPairDmaAt, kPairPlan>), dim3(total), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((attn_pair_kernel<false, false, kPairDmaAt, kPairPlan>), dim3(total), dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_pair_fused(const AttnArgs &a, hipStream_t stream) {
+  if (a.nvq <= 0) return hipSuccess;
+  if (a.max_sel > kMaxPairList || a.nvb > kMaxRouteBlocks || a.qbar == nullptr ||
+      (a.nvb > 0 && a.kbar == nullptr))
+    return hipErrorInvalidValue;
+  PairParams p = make_pair_params(a, 0, a.nvq);
+  p.row_hi = a.rows_end;
+  const int total = a.B * a.H * p.npair;
+  hipLaunchKernelGGL((attn_pair_kernel<false, true, kPairDmaAt, kPairPlan>), dim3(total), dim3(kThreads), 0,
+                     stream, p);
   return hipGetLastError();
 }
 
@@ -902,7 +999,7 @@ hipError_t launch_attn_pair_dense(const AttnArgs &a, float *part_o, float *part_
     p.part_ml = part_ml;
   }
   const int total = a.B * a.H * p.npair * p.nsplit;
-  hipLaunchKernelGGL((attn_pair_kernel<true, kPairDmaAt, kPairPlan>), dim3(total), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((attn_pair_kernel<true, false, kPairDmaAt, kPairPlan>), dim3(total), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -83,6 +83,10 @@ size_t dense_workspace_bytes(int B, int H, int nb, int nvb);
 // it.  Sparse rows (needs max_sel <= kMaxPairList), and the dense rows with
 // nsplit key ranges (partials to part_o / part_ml when nsplit > 1).
 hipError_t launch_attn_pair_sparse(const AttnArgs &a, hipStream_t stream);
+// The same with the route inside (needs max_sel <= kMaxPairList, nvb <=
+// kMaxRouteBlocks): every workgroup scores both query blocks against the
+// pooled key means and selects their lists (the route kernel's rule).
+hipError_t launch_attn_pair_fused(const AttnArgs &a, hipStream_t stream);
 hipError_t launch_attn_pair_dense(const AttnArgs &a, float *part_o, float *part_ml, int nsplit,
                                   hipStream_t stream);
 int dense_pair_splits(int B, int H, int nb, int nvb);
