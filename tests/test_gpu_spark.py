@@ -2,8 +2,9 @@
 oracle (oracle/spark_summaries.py) on the same seeded bf16 inputs (needs a
 GPU; every call goes through the C ABI).
 
-Anchor: bit-exact.  Summaries: ak / av within one bf16 ulp of the oracle's
-(both round a value they computed in different precision), lm within 1e-4
+Anchor: bit-exact.  Summaries: each ak / av value within one bf16 ulp of the
+oracle's or within 1e-3 absolute (both sides round a value they computed in
+different precision; near zero one ulp is tiny), lm within 1e-4
 of the oracle's log-mass taken against the GPU's own stored key, for every
 head.  Lists: equal to the oracle's except inside near-tie bands.
 Attention: every element of out and LSE, max-abs <= 2e-2 and mean-abs
