@@ -71,17 +71,23 @@ constexpr int kPVOff = 32768;                   // V ring: 2 slots x 16 KiB
 constexpr int kPBOff = 65536;                   // bias ring: 2 slots x 64 floats (A | B)
 constexpr int kPSchOff = 65536 + 512;           // entries: kMaxPairEntries x (block A, block B)
 constexpr int kMaxPairEntries = 2 * kMaxPairList;
-constexpr int kPCntOff = kPSchOff + kMaxPairEntries * 8;   // nU, nBi, nE
-constexpr int kPLdsBytes = kPCntOff + 16;
+constexpr int kPCntOff = kPSchOff + kMaxPairEntries * 8;   // schedule counts and flags
+constexpr int kPCntInts = 12;
+constexpr int kPLdsBytes = kPCntOff + 4 * kPCntInts;
 // Schedule-build temporaries, inside the K ring (no tile is loaded yet):
-// compacted lists, private entries of A and B, shared entries.
+// compacted lists, private entries of A and B, shared entries, each private
+// or shared entry's merge rank (below), and the entries in merged order.
 constexpr int kListBytes = 4 * kMaxPairList;
 constexpr int kLAOff = 0;
 constexpr int kLBOff = kLAOff + kListBytes;
 constexpr int kPAOff = kLBOff + kListBytes;
 constexpr int kPBlOff = kPAOff + kListBytes;
 constexpr int kSHOff = kPBlOff + kListBytes;
-static_assert(kSHOff + kListBytes <= kPVOff, "build temporaries must fit the K ring");
+constexpr int kPARkOff = kSHOff + kListBytes;
+constexpr int kPBRkOff = kPARkOff + kListBytes;
+constexpr int kSHRkOff = kPBRkOff + kListBytes;
+constexpr int kMrgOff = kSHRkOff + kListBytes;          // kMaxPairEntries x int2
+static_assert(kMrgOff + 8 * kMaxPairEntries <= kPVOff, "build temporaries must fit the K ring");
 
 // Fused route: the two query blocks' pooled means (fp64), their scores and
 // their selected lists, inside the V ring (unused until the first tile
@@ -117,8 +123,9 @@ __device__ __forceinline__ int lanes_below(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
 }
 
-// Whether x is among the n ascending values arr[0..n) (LDS).
-__device__ __forceinline__ bool lds_contains(const int *arr, int n, int x) {
+// Whether x is among the n ascending values arr[0..n) (LDS); *pos gets the
+// number of values below x.
+__device__ __forceinline__ bool lds_contains(const int *arr, int n, int x, int *pos) {
   const int len = n;
   int lo = 0;
   while (n > 0) {
@@ -130,6 +137,7 @@ __device__ __forceinline__ bool lds_contains(const int *arr, int n, int x) {
       n = half;
     }
   }
+  *pos = lo;
   return lo < len && arr[lo] == x;
 }
 
@@ -137,7 +145,7 @@ __device__ __forceinline__ bool lds_contains(const int *arr, int n, int x) {
 // barriers (the caller's): compact (waves 0 and 1, one list each), classify
 // (waves 0 and 1) and emit (wave 0).  Scalars: cnt[0..2] = nU, nBi, nE;
 // cnt[3..7] = valid entries of A and B, private entries of A and B, shared
-// entries.
+// entries; cnt[8] = 1 when a list is not strictly ascending.
 
 // Pass 1: the valid entries of one list (lst, global or LDS), in order, to
 // dst.  `first` holds entry `lane` of the list (read before anything else),
@@ -157,19 +165,43 @@ __device__ __forceinline__ void pair_compact(const PairParams &p, const int32_t 
 }
 
 // Pass 2: entries of `own` also in `other` go to sh (when given), the rest
-// to priv.
+// to priv.  Each entry's rank in the merged order goes beside it:
+//
+// The schedule walks the entries in ascending order of their larger key
+// block (a shared entry x counts as (x, x)), so that the workgroups that run
+// together on an XCD sweep the key range of a head together and a K/V tile
+// is still in L2 when the next workgroup asks for it.  Private entries are
+// paired in list order (i-th of A with i-th of B), so with both lists
+// ascending the merged rank is the larger of the two list positions for a
+// pair and the smaller of the two for a shared entry: a private pair i
+// comes after the shared entries below its larger block (its list position
+// in that list minus i) and after the i pairs before it, and a shared entry
+// at position j of the shared list comes after the pairs whose both blocks
+// lie below it (the smaller of its two list positions minus j).  privrk gets
+// the own-list position of each private entry, shrk the merged rank of each
+// shared entry.  A list that is not strictly ascending (outside the
+// contract) sets *unsorted, and the entries then keep the unmerged order.
 __device__ __forceinline__ void pair_classify(const int *own, int n_own, const int *other, int n_other,
-                                              int *priv, int *n_priv_out, int *sh, int *n_sh_out,
-                                              int lane) {
+                                              int *priv, int *privrk, int *n_priv_out, int *sh,
+                                              int *shrk, int *n_sh_out, int *unsorted, int lane) {
   int np = 0, ns = 0;
   for (int cb = 0; cb < n_own; cb += 64) {
     const int i = cb + lane;
     const bool in = i < n_own;
     const int x = in ? own[i] : -1;
-    const bool shared = in && lds_contains(other, n_other, x);
+    // the merge ranks need strictly ascending lists; others keep list order
+    if (__any(i + 1 < n_own && own[i + 1] <= x) && lane == 0) *unsorted = 1;
+    int pos = 0;
+    const bool shared = in && lds_contains(other, n_other, x, &pos);
     const uint64_t mp = __ballot(in && !shared), ms = __ballot(shared);
-    if (in && !shared) priv[np + lanes_below(mp)] = x;
-    if (shared && sh != nullptr) sh[ns + lanes_below(ms)] = x;
+    if (in && !shared) {
+      priv[np + lanes_below(mp)] = x;
+      privrk[np + lanes_below(mp)] = i;
+    }
+    if (shared && sh != nullptr) {
+      sh[ns + lanes_below(ms)] = x;
+      shrk[ns + lanes_below(ms)] = i < pos ? i : pos;
+    }
     np += __popcll(mp);
     ns += __popcll(ms);
   }
@@ -179,12 +211,18 @@ __device__ __forceinline__ void pair_classify(const int *own, int n_own, const i
   }
 }
 
-// Pass 3: private pairs (and leftovers), then shared entries, sorted into
-// the three phases.
+// Pass 3: the entries (private pairs, leftovers, shared entries) in merged
+// order (pass 2), then sorted into the three phases, stable in that order.
+// Leftover private entries (one list longer than the other) follow all
+// others; they are general-phase entries anyway.
 __device__ __forceinline__ void pair_emit(const PairParams &p, unsigned char *smem, int lane) {
   const int *PA = reinterpret_cast<const int *>(smem + kPAOff);
   const int *PB = reinterpret_cast<const int *>(smem + kPBlOff);
   const int *SH = reinterpret_cast<const int *>(smem + kSHOff);
+  const int *PArk = reinterpret_cast<const int *>(smem + kPARkOff);
+  const int *PBrk = reinterpret_cast<const int *>(smem + kPBRkOff);
+  const int *SHrk = reinterpret_cast<const int *>(smem + kSHRkOff);
+  int2 *mrg = reinterpret_cast<int2 *>(smem + kMrgOff);
   int2 *sch = reinterpret_cast<int2 *>(smem + kPSchOff);
   int *cnt = reinterpret_cast<int *>(smem + kPCntOff);
   const int nPA = __builtin_amdgcn_readfirstlane(cnt[5]);
@@ -193,14 +231,29 @@ __device__ __forceinline__ void pair_emit(const PairParams &p, unsigned char *sm
   const int partial = (p.T % kBlock) != 0 ? p.nb - 1 : -1;
   const bool biased = p.key_bias != nullptr;
   const int nX = nPA > nPB ? nPA : nPB;
+  const int nMin = nPA < nPB ? nPA : nPB;
   const int nC = nX + nS;
-  auto entry = [&](int c, int &a, int &b) {
-    if (c < nX) {
-      a = c < nPA ? PA[c] : -1;
-      b = c < nPB ? PB[c] : -1;
-    } else {
-      a = b = SH[c - nX];
+  const bool unsorted = __builtin_amdgcn_readfirstlane(cnt[8]) != 0;
+  for (int cb = 0; cb < nC; cb += 64) {
+    const int c = cb + lane;
+    if (c < nC) {
+      int a, b, r;
+      if (c < nX) {
+        a = c < nPA ? PA[c] : -1;
+        b = c < nPB ? PB[c] : -1;
+        r = c < nMin ? (PArk[c] > PBrk[c] ? PArk[c] : PBrk[c]) : nS + c;
+      } else {
+        a = b = SH[c - nX];
+        r = SHrk[c - nX];
+      }
+      mrg[unsorted ? c : r] = make_int2(a, b);
     }
+  }
+  wave_lds_sync();   // the merged entries were written by other lanes of this wave
+  auto entry = [&](int c, int &a, int &b) {
+    const int2 v = mrg[c];
+    a = v.x;
+    b = v.y;
   };
   auto phase = [&](int a, int b) -> int {
     if (a < 0 || b < 0 || a == partial || b == partial) return 2;
@@ -409,21 +462,26 @@ void attn_pair_kernel(PairParams p) {
     if (wave == 0 || (wave == 1 && hasB))
       pair_compact(p, lst, __builtin_amdgcn_readfirstlane(lcnt), lfirst, wave ? LB : LA, cnt + 3 + wave,
                    lane);
+    if (wave == 2 && lane == 0) cnt[8] = 0;
     __syncthreads();
     if (wave < 2) {
       const int nA = __builtin_amdgcn_readfirstlane(cnt[3]);
       if (!hasB) {   // a missing block B: every entry of A is shared
-        if (wave == 0) pair_classify(LA, nA, LA, 0, reinterpret_cast<int *>(smem + kSHOff), cnt + 7,
-                                     nullptr, nullptr, lane);
+        if (wave == 0) pair_classify(LA, nA, LA, 0, reinterpret_cast<int *>(smem + kSHOff),
+                                     reinterpret_cast<int *>(smem + kSHRkOff), cnt + 7, nullptr,
+                                     nullptr, nullptr, cnt + 8, lane);
         if (wave == 0 && lane == 0) cnt[5] = cnt[6] = 0;
       } else {
         const int nB = __builtin_amdgcn_readfirstlane(cnt[4]);
         if (wave == 0)
-          pair_classify(LA, nA, LB, nB, reinterpret_cast<int *>(smem + kPAOff), cnt + 5,
-                        reinterpret_cast<int *>(smem + kSHOff), cnt + 7, lane);
+          pair_classify(LA, nA, LB, nB, reinterpret_cast<int *>(smem + kPAOff),
+                        reinterpret_cast<int *>(smem + kPARkOff), cnt + 5,
+                        reinterpret_cast<int *>(smem + kSHOff), reinterpret_cast<int *>(smem + kSHRkOff),
+                        cnt + 7, cnt + 8, lane);
         else
-          pair_classify(LB, nB, LA, nA, reinterpret_cast<int *>(smem + kPBlOff), cnt + 6, nullptr,
-                        nullptr, lane);
+          pair_classify(LB, nB, LA, nA, reinterpret_cast<int *>(smem + kPBlOff),
+                        reinterpret_cast<int *>(smem + kPBRkOff), cnt + 6, nullptr, nullptr, nullptr,
+                        cnt + 8, lane);
       }
     }
     __syncthreads();

@@ -435,3 +435,68 @@ def test_pad_batch2_radius2_with_bias():
     wl = workloads.Workload("pad_B2_H3_r2", q, k, v, sink_start=1000, topk_ratio=0.3, local_radius=2,
                             key_bias=bias, tail_mode="pad")
     _full_parity(wl)
+
+
+def _mid_lists():
+    import block_sparse_attention_05_amd as sa
+    wl = workloads.mid()
+    q, k, v = (x.cuda() for x in (wl.q, wl.k, wl.v))
+    idx, cnt = sa.sparse_attn_route(q, k, wl.sink_start, wl.topk_ratio, wl.local_radius)
+    return sa, wl, q, k, v, idx, cnt
+
+
+def test_invalid_entries_are_skipped():
+    """Entries outside [0, NB) are skipped and counts above max_sel are
+    clamped: lists padded with -7, -1 in front and NB, NB + 3 and 1 << 30
+    behind give the same bits as the plain lists."""
+    sa, wl, q, k, v, idx, cnt = _mid_lists()
+    B, T, H, _ = q.shape
+    nb = -(-T // 64)
+    ss = wl.sink_start
+    ref = sa.sparse_attn_fwd(q, k, v, ss, idx, cnt)
+    ms = idx.shape[-1]
+    wide = torch.full(idx.shape[:-1] + (ms + 5,), -1, dtype=torch.int32, device=idx.device)
+    wide[..., 0] = -7
+    wide[..., 1] = -1
+    ar = torch.arange(ms, device=idx.device)
+    for j in range(ms):   # entry j of a list of length c lands at 2 + j; the tail after it
+        wide[..., 2 + j] = torch.where(j < cnt, idx[..., j], torch.full_like(cnt, nb))
+    pos = (cnt + 2).long().unsqueeze(-1)
+    wide.scatter_(-1, pos, torch.full_like(pos, nb, dtype=torch.int32))
+    wide.scatter_(-1, pos + 1, torch.full_like(pos, nb + 3, dtype=torch.int32))
+    wide.scatter_(-1, pos + 2, torch.full_like(pos, 1 << 30, dtype=torch.int32))
+    wcnt = cnt + 5
+    assert ar.numel() == ms
+    got = sa.sparse_attn_fwd(q, k, v, ss, wide, wcnt)
+    # counts past max_sel: the clamped list is the whole padded row
+    got2 = sa.sparse_attn_fwd(q, k, v, ss, wide, torch.full_like(wcnt, 1 << 20))
+    torch.cuda.synchronize()
+    rows = slice(0, ss)
+    assert torch.equal(got[:, rows], ref[:, rows])
+    assert torch.equal(got2[:, rows], ref[:, rows])
+
+
+def test_unsorted_lists_stay_in_bounds():
+    """Lists outside the contract (not ascending, repeated entries) give
+    unspecified values but must not disturb anything else: the workgroups
+    whose two lists are ascending give the same bits, the others finite
+    values."""
+    sa, wl, q, k, v, idx, cnt = _mid_lists()
+    ss = wl.sink_start
+    ref = sa.sparse_attn_fwd(q, k, v, ss, idx, cnt)
+    bad = idx.clone()
+    # head 0: query block 4 reversed, block 9 with a repeated first entry
+    c4, c9 = int(cnt[0, 0, 4]), int(cnt[0, 0, 9])
+    bad[0, 0, 4, :c4] = idx[0, 0, 4, :c4].flip(0)
+    bad[0, 0, 9, 1] = idx[0, 0, 9, 0]
+    got = sa.sparse_attn_fwd(q, k, v, ss, bad, cnt)
+    torch.cuda.synchronize()
+    assert torch.isfinite(got.float()).all()
+    same = torch.ones(q.shape[2], ss // 64, dtype=torch.bool)
+    same[0, 4:6] = False   # the pair of block 4
+    same[0, 8:10] = False  # the pair of block 9
+    for h in range(q.shape[2]):
+        for i in range(ss // 64):
+            if same[h, i]:
+                r = slice(64 * i, 64 * i + 64)
+                assert torch.equal(got[0, r, h], ref[0, r, h]), (h, i)
