@@ -356,10 +356,20 @@ void attn_pair_kernel(PairParams p) {
     if (lane < p.max_sel) lfirst = p.block_idx[li * p.max_sel + lane];
   }
 
-  // Q^T fragments of this lane's row (d = 16*dc + 8*g + [0, 8)), read
-  // straight from memory; rows past T read as zero.
+  // Q^T fragments of this lane's row (d = 16*dc + 8*g + [0, 8)).  Without
+  // the fused route the wave's 32 rows are copied into its 8 KiB of the V
+  // ring (free until the first tiles load) in whole 256-byte rows, four
+  // rows per instruction (lane l: row 4i + l/16, 16-byte chunk
+  // (l%16) ^ (row%16), so chunk c of row r lands at slot c ^ (r%16) and the
+  // fragment reads below are free of bank conflicts), and read after the
+  // schedule is built.  A lane that loads its own row instead would touch
+  // 32 rows per instruction, four times the cache-line requests.  The fused
+  // route keeps its scratch in the V ring and reads straight from memory.
+  // Rows past T and a missing block B read as zero.
+  const uint32_t slab = (uint32_t)T * (uint32_t)row_bytes;
+  const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>(LDS_PTR(unsigned char, smem));
   bf16x8 qf[8];
-  {
+  if (kFused) {
     const bool ok = active && tq < T;
     const uint16_t *qrow = p.q + bbase + (int64_t)(ok ? tq : 0) * rs + h * kHeadDim + 8 * g;
 #pragma unroll
@@ -368,7 +378,34 @@ void attn_pair_kernel(PairParams p) {
       if (ok) v = *reinterpret_cast<const bf16x8 *>(qrow + 16 * dc);
       qf[dc] = v;
     }
+  } else {
+    const i32x4s rq = buffer_rsrc(p.q + bbase, slab);
+    const uint32_t r4 = (uint32_t)(lane >> 4);
+    const uint32_t row0 = (uint32_t)(qb * kBlock + rw * 32);
+    const uint32_t l = lds0 + kPVOff + 8192u * (uint32_t)wave;
+    auto q_off = [&](uint32_t i) -> uint32_t {
+      const uint32_t r = 4 * i + r4;
+      const uint32_t ch = (uint32_t)(lane & 15) ^ (r & 15);
+      return active ? (row0 + r) * (uint32_t)row_bytes + (uint32_t)h * 256u + 16u * ch : slab;
+    };
+    lds_dma_b128<0>(rq, q_off(0), l);
+    lds_dma_b128<1024>(rq, q_off(1), l);
+    lds_dma_b128<2048>(rq, q_off(2), l);
+    lds_dma_b128<3072>(rq, q_off(3), l);
+    lds_dma_b128<4096>(rq, q_off(4), l);
+    lds_dma_b128<5120>(rq, q_off(5), l);
+    lds_dma_b128<6144>(rq, q_off(6), l);
+    lds_dma_b128<7168>(rq, q_off(7), l);
   }
+  // the wave's Q fragments from its copy (each wave reads what it copied)
+  auto read_q = [&]() {
+    if (kFused) return;
+    __builtin_amdgcn_s_waitcnt(kVmcntZero);
+    const unsigned char *qs = smem + kPVOff + 8192 * wave + 256 * c32;
+#pragma unroll
+    for (int dc = 0; dc < 8; ++dc)
+      qf[dc] = *reinterpret_cast<const bf16x8 *>(qs + 16 * ((2 * dc + g) ^ (c32 & 15)));
+  };
 
   // ---- schedule ------------------------------------------------------------
   const bool has_bias = p.key_bias != nullptr;
@@ -392,6 +429,8 @@ void attn_pair_kernel(PairParams p) {
     nE = nub + ((nbfull < p.nb && p.nb - 1 >= t_begin && p.nb - 1 < t_end) ? 1 : 0);
     d_t0 = t_begin;
     d_nub = nub;
+    read_q();
+    __syncthreads();
   } else {
     int *cnt = reinterpret_cast<int *>(smem + kPCntOff);
     int *LA = reinterpret_cast<int *>(smem + kLAOff);
@@ -486,6 +525,8 @@ void attn_pair_kernel(PairParams p) {
     }
     __syncthreads();
     if (wave == 0) pair_emit(p, smem, lane);
+    read_q();
+    // all waves have their Q before the first tile copies refill the V ring
     __syncthreads();
     nU = __builtin_amdgcn_readfirstlane(cnt[0]);
     nBi = __builtin_amdgcn_readfirstlane(cnt[1]);
@@ -523,13 +564,11 @@ void attn_pair_kernel(PairParams p) {
   };
 
   // ---- loads --------------------------------------------------------------
-  const uint32_t slab = (uint32_t)T * (uint32_t)row_bytes;
   const i32x4s rk = buffer_rsrc(p.k + bbase, slab);
   const i32x4s rv = buffer_rsrc(p.v + bbase, slab);
   const float *kbias = has_bias ? p.key_bias + (int64_t)b * T : nullptr;
   const i32x4s rb = buffer_rsrc(kbias ? (const void *)kbias : (const void *)p.k, kbias ? T * 4u : 0u);
   const int sink0 = p.nvb * kBlock;
-  const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>(LDS_PTR(unsigned char, smem));
   const uint32_t rows8 = (uint32_t)(8 * row_bytes);
   // LDS tile layout: the one-block kernel's.  A 64-key slot is 16 blocks of
   // 1 KiB; block 2*kg + hf holds keys 8*kg .. +7 (kg = 0..7) and bytes
