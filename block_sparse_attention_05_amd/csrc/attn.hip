@@ -216,13 +216,25 @@ void attn_fwd_kernel(Params p) {
       first = lane < p.max_sel ? list[lane] : 0;
       n = p.block_cnt[li];
     }
-    t_end = n < 0 ? 0 : (n > p.max_sel ? p.max_sel : n);
-    list_v = lane < t_end ? first : 0;
-    // entries below nvb come first; count them over all 64-entry chunks
-    n_plain = __popcll(__ballot(lane < t_end && list_v < p.nvb));
-    for (int cb = 64; cb < t_end; cb += 64) {
-      const int e = cb + lane < t_end ? list[cb + lane] : p.nb;
-      n_plain += __popcll(__ballot(e < p.nvb));
+    const int t_cnt = n < 0 ? 0 : (n > p.max_sel ? p.max_sel : n);
+    list_v = lane < t_cnt ? first : 0;
+    // An ascending list holds its entries outside [0, NB) as a prefix (< 0)
+    // and a suffix (>= NB); the tiles are the entries between them, video
+    // blocks (< NVB) first.  Count the groups over all 64-entry chunks.
+    int n_neg = 0, n_valid = 0;
+    n_plain = 0;
+    for (int cb = 0; cb < t_cnt; cb += 64) {
+      const bool in = cb + lane < t_cnt;
+      const int e = cb == 0 ? list_v : (in ? list[cb + lane] : 0);
+      n_neg += __popcll(__ballot(in && e < 0));
+      n_valid += __popcll(__ballot(in && e >= 0 && e < p.nb));
+      n_plain += __popcll(__ballot(in && e >= 0 && e < p.nvb));
+    }
+    t_begin = n_neg;
+    t_end = n_neg + n_valid;
+    if (t_begin >= 64) {   // the first tile lies past the first chunk
+      list_cb = t_begin & ~63;
+      list_v = list_cb + lane < t_end ? list[list_cb + lane] : 0;
     }
   }
   const int n = t_end - t_begin;  // exact tiles
@@ -254,7 +266,9 @@ void attn_fwd_kernel(Params p) {
   bf16x8 qf[8];
 
   // First token of tile t_begin + j; calls come with j = 0, 1, 2, ... in
-  // order.  An invalid list entry maps to T (reads as zero, fully masked).
+  // order.  An entry outside [0, NB) between valid ones (only in a list that
+  // is not ascending, whose results are unspecified) maps to T: its tile
+  // reads as zero and every access stays in bounds.
   // The next 64-entry chunk is loaded one call before it is needed, so that
   // the end-of-step wait already covers it: a wait placed by the compiler at
   // the use would also drain the K/V tile loads in flight.
@@ -562,7 +576,8 @@ void attn_fwd_kernel(Params p) {
     for (int x = tid; 4 * x < p.nvb; x += kThreads) reinterpret_cast<uint32_t *>(fl)[x] = 0u;
     __syncthreads();
     for (int cb = 64 * wave; cb < t_end; cb += kThreads) {
-      const int e = cb == 0 ? list_v : (cb + lane < t_end ? list[cb + lane] : -1);
+      // list_v still holds the first chunk unless the walk started past it
+      const int e = (cb == 0 && list_cb == 0) ? list_v : (cb + lane < t_end ? list[cb + lane] : -1);
       if (cb + lane < t_end && e >= 0 && e < p.nvb) fl[e] = 1;
     }
     __syncthreads();

@@ -88,3 +88,24 @@ def adopt_lists(idx, cnt, rt):
 def err_stats(got, want):
     d = np.abs(np.asarray(got, np.float64) - np.asarray(want, np.float64))
     return float(d.max()), float(d.mean())
+
+
+def pad_lists(idx, cnt, front, back, width):
+    """Lists with the entries `front` before and `back` after every list's
+    own entries (all ascending), -1 beyond, `width` entries per list."""
+    B, H, nq, ms = idx.shape
+    wide = torch.full((B, H, nq, width), -1, dtype=torch.int32, device=idx.device)
+    c = cnt.long()
+    nf = len(front)
+    for j, x in enumerate(front):
+        wide[..., j] = x
+    pos = torch.arange(ms, device=idx.device).view(1, 1, 1, ms)
+    ok = pos < c.unsqueeze(-1)
+    tgt = torch.where(ok, pos + nf, torch.full_like(pos, width - 1)).expand(B, H, nq, ms)
+    vals = torch.where(ok, idx, torch.full_like(idx, -1))
+    wide.scatter_(-1, tgt, vals)
+    for j, x in enumerate(back):
+        wide.scatter_(-1, (c + nf + j).unsqueeze(-1), torch.full_like(c.unsqueeze(-1), x, dtype=torch.int32))
+    wide[..., width - 1] = torch.where(c + nf + len(back) > width - 1, wide[..., width - 1],
+                                       torch.full_like(cnt, -1))
+    return wide, (cnt + nf + len(back)).to(torch.int32)

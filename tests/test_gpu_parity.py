@@ -14,7 +14,8 @@ import torch
 
 import oracle.sparse_attention as ora
 import workloads
-from gpu_helpers import MAX_ABS, MEAN_ABS, adopt_lists, compare_lists, err_stats, log, run_gpu, to_np
+from gpu_helpers import (MAX_ABS, MEAN_ABS, adopt_lists, compare_lists, err_stats, log, pad_lists,
+                         run_gpu, to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -448,25 +449,13 @@ def _mid_lists():
 def test_invalid_entries_are_skipped():
     """Entries outside [0, NB) are skipped and counts above max_sel are
     clamped: lists padded with -7, -1 in front and NB, NB + 3 and 1 << 30
-    behind give the same bits as the plain lists."""
+    behind give the same bits as the plain lists (paired kernel)."""
     sa, wl, q, k, v, idx, cnt = _mid_lists()
-    B, T, H, _ = q.shape
+    T = q.shape[1]
     nb = -(-T // 64)
     ss = wl.sink_start
     ref = sa.sparse_attn_fwd(q, k, v, ss, idx, cnt)
-    ms = idx.shape[-1]
-    wide = torch.full(idx.shape[:-1] + (ms + 5,), -1, dtype=torch.int32, device=idx.device)
-    wide[..., 0] = -7
-    wide[..., 1] = -1
-    ar = torch.arange(ms, device=idx.device)
-    for j in range(ms):   # entry j of a list of length c lands at 2 + j; the tail after it
-        wide[..., 2 + j] = torch.where(j < cnt, idx[..., j], torch.full_like(cnt, nb))
-    pos = (cnt + 2).long().unsqueeze(-1)
-    wide.scatter_(-1, pos, torch.full_like(pos, nb, dtype=torch.int32))
-    wide.scatter_(-1, pos + 1, torch.full_like(pos, nb + 3, dtype=torch.int32))
-    wide.scatter_(-1, pos + 2, torch.full_like(pos, 1 << 30, dtype=torch.int32))
-    wcnt = cnt + 5
-    assert ar.numel() == ms
+    wide, wcnt = pad_lists(idx, cnt, [-7, -1], [nb, nb + 3, 1 << 30], idx.shape[-1] + 5)
     got = sa.sparse_attn_fwd(q, k, v, ss, wide, wcnt)
     # counts past max_sel: the clamped list is the whole padded row
     got2 = sa.sparse_attn_fwd(q, k, v, ss, wide, torch.full_like(wcnt, 1 << 20))
@@ -474,6 +463,31 @@ def test_invalid_entries_are_skipped():
     rows = slice(0, ss)
     assert torch.equal(got[:, rows], ref[:, rows])
     assert torch.equal(got2[:, rows], ref[:, rows])
+
+
+def test_invalid_entries_are_skipped_long_lists():
+    """Lists wider than the paired kernel's 512 entries take the one-block
+    kernel: 300 negative entries in front (the first tile past the first
+    64-entry chunk) and NB, NB + 1 behind give the same bits as the same
+    width without them."""
+    sa, wl, q, k, v, idx, cnt = _mid_lists()
+    T = q.shape[1]
+    nb = -(-T // 64)
+    ss = wl.sink_start
+    width = 520
+    plain, pcnt = pad_lists(idx, cnt, [], [], width)
+    ref = sa.sparse_attn_fwd(q, k, v, ss, plain, pcnt)
+    front = list(range(-300, 0))
+    wide, wcnt = pad_lists(idx, cnt, front, [nb, nb + 1], width)
+    got = sa.sparse_attn_fwd(q, k, v, ss, wide, wcnt)
+    torch.cuda.synchronize()
+    rows = slice(0, ss)
+    assert torch.equal(got[:, rows], ref[:, rows])
+    # and the one-block kernel agrees with the paired one within rounding
+    pair = sa.sparse_attn_fwd(q, k, v, ss, idx, cnt)
+    torch.cuda.synchronize()
+    err = (got[:, rows].float() - pair[:, rows].float()).abs().max().item()
+    assert err <= 2e-2, err
 
 
 def test_unsorted_lists_stay_in_bounds():

@@ -208,3 +208,27 @@ def test_spark_batch2_radius2_pad_with_bias():
     q, k, v = workloads.random_qkv(2, 1100, 3, seed=19)
     bias = workloads.sink_key_bias(2, 1100, 1000, seed=20)
     _spark_parity(q, k, v, 1000, 0.3, 2, "spark_B2_pad", key_bias=bias, tail_mode="pad")
+
+
+def test_spark_invalid_entries_are_skipped():
+    """The approximate branch with lists padded by entries outside [0, NB)
+    (-7, -1 in front; NB, NB + 3 behind) gives the same bits as the plain
+    lists, with and without key_bias: the virtual keys are the video blocks
+    the valid entries skip."""
+    import block_sparse_attention_05_amd as sa
+    from gpu_helpers import pad_lists
+    wl = workloads.mid()
+    q, k, v = (x.cuda() for x in (wl.q, wl.k, wl.v))
+    T = q.shape[1]
+    nb = -(-T // 64)
+    ss = wl.sink_start
+    bias = workloads.sink_key_bias(1, T, ss, seed=12).cuda()
+    out, parts = sa.routed_attention_spark(q, k, v, ss, wl.topk_ratio, wl.local_radius, return_parts=True)
+    idx, cnt = parts["block_idx"], parts["block_cnt"]
+    summ = parts["summaries"]
+    wide, wcnt = pad_lists(idx, cnt, [-7, -1], [nb, nb + 3], idx.shape[-1] + 4)
+    for kb in (None, bias):
+        ref = sa.sparse_attn_fwd_spark(q, k, v, ss, idx, cnt, summ, key_bias=kb)
+        got = sa.sparse_attn_fwd_spark(q, k, v, ss, wide, wcnt, summ, key_bias=kb)
+        torch.cuda.synchronize()
+        assert torch.equal(got[:, :ss], ref[:, :ss]), kb is None
