@@ -56,6 +56,8 @@
 // ds_read_b64_tr_b16; the S(j+1) MFMAs of the next step overlap the softmax
 // of this one.  The same arithmetic as the one-block kernel, with the keys of
 // a 64-key tile accumulated in two sequential steps instead of two waves.
+#include <atomic>
+
 #include "attn_common.h"
 #include "device_util.h"
 #include "kernels.h"
@@ -109,6 +111,9 @@ struct PairParams {
   int qb0, nqb, npair;
   int row_lo, row_hi;  // rows written: [row_lo, row_hi)
   int nsplit, tiles_per_split;
+  // Workgroups resident on one XCD at a time (two per CU), for the order of
+  // the sparse items below; 0 keeps the plain order.
+  int slots;
   float scale_log2;
   // fused route: pooled means in the route workspace layout, budget, forced
   // radius, optional copies of the selected lists
@@ -139,6 +144,31 @@ __device__ __forceinline__ bool lds_contains(const int *arr, int n, int x, int *
   }
   *pos = lo;
   return lo < len && arr[lo] == x;
+}
+
+// Item (pair of query blocks, head-major) of workgroup blk among total.
+// Every XCD owns a contiguous, head-aligned range of items (the XCD remap).
+// Its `slots` resident workgroups run consecutive items side by side and
+// sweep one head's keys together, which fits the head's K and V in that
+// XCD's L2 once; a head with more pairs than a multiple of `slots` would
+// spill its last pairs into the next head's round and sweep its keys a
+// second time.  So within the range every head's first multiple of `slots`
+// pairs come first, head after head, and the spilled pairs of all heads
+// follow.  Ranges that do not start and end on a head keep the plain order.
+__device__ __forceinline__ int pair_order(int blk, int total, int npair, int slots) {
+  const int w = xcd_remap(blk, total);
+  if (slots <= 0 || npair <= slots) return w;
+  constexpr int kXcd = 8;
+  const int x = blk % kXcd;
+  const int per = total / kXcd, rem = total % kXcd;
+  const int lo = x * per + (x < rem ? x : rem), n = per + (x < rem ? 1 : 0);
+  const int full = npair - npair % slots;      // pairs per head in whole rounds
+  const int left = npair - full;
+  if (left == 0 || lo % npair != 0 || n % npair != 0) return w;
+  const int k = w - lo, nh = n / npair;
+  if (k < nh * full) return lo + (k / full) * npair + k % full;
+  const int k2 = k - nh * full;
+  return lo + (k2 / left) * npair + full + k2 % left;
 }
 
 // Entry list of one workgroup, in three passes separated by workgroup
@@ -320,7 +350,7 @@ void attn_pair_kernel(PairParams p) {
   __shared__ __align__(16) unsigned char smem[kPLdsBytes];
 
   const int total = p.B * p.H * p.npair * p.nsplit;
-  const int w = xcd_remap(blockIdx.x, total);
+  const int w = kDense ? xcd_remap(blockIdx.x, total) : pair_order(blockIdx.x, total, p.npair, p.slots);
   const int split = w % p.nsplit;
   const int wp = w / p.nsplit;
   const int pi = wp % p.npair;
@@ -1028,7 +1058,24 @@ PairParams make_pair_params(const AttnArgs &a, int qb0, int nqb) {
   p.radius = a.radius;
   p.list_out = a.list_out;
   p.cnt_out = a.cnt_out;
+  p.slots = 0;
   return p;
+}
+
+// Resident paired-kernel workgroups per XCD on the current device (two per
+// CU, eight XCDs), looked up once per device.
+int pair_slots_per_xcd() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 8)
+    return 0;
+  v = 2 * (cus / 8);
+  cache[dev].store(v, std::memory_order_relaxed);
+  return v;
 }
 
 }  // namespace
@@ -1066,6 +1113,7 @@ hipError_t launch_attn_pair_sparse(const AttnArgs &a, hipStream_t stream) {
   if (a.max_sel > kMaxPairList) return hipErrorInvalidValue;
   PairParams p = make_pair_params(a, 0, a.nvq);
   p.row_hi = a.rows_end;
+  p.slots = pair_slots_per_xcd();
   const int total = a.B * a.H * p.npair;
   hipLaunchKernelGGL((attn_pair_kernel<false, false, kPairDmaAt, kPairPlan>), dim3(total), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
