@@ -71,7 +71,7 @@ using namespace attn;
 constexpr int kPKOff = 0;                       // K ring: 2 slots x 16 KiB (A half | B half)
 constexpr int kPVOff = 32768;                   // V ring: 2 slots x 16 KiB
 constexpr int kPBOff = 65536;                   // bias ring: 2 slots x 64 floats (A | B)
-constexpr int kPSchOff = 65536 + 512;           // entries: kMaxPairEntries x (block A, block B)
+constexpr int kPSchOff = 65536 + 512;           // entries: kMaxPairEntries x (first key of A's tile, of B's)
 constexpr int kMaxPairEntries = 2 * kMaxPairList;
 constexpr int kPCntOff = kPSchOff + kMaxPairEntries * 8;   // schedule counts and flags
 constexpr int kPCntInts = 12;
@@ -285,6 +285,8 @@ __device__ __forceinline__ void pair_emit(const PairParams &p, unsigned char *sm
     a = v.x;
     b = v.y;
   };
+  // entries are stored as the first key of each block's tile (T: no tile)
+  auto first_key = [&](int x) -> int { return x < 0 ? p.T : x * kBlock; };
   auto phase = [&](int a, int b) -> int {
     if (a < 0 || b < 0 || a == partial || b == partial) return 2;
     if (biased && (a >= p.nvb || b >= p.nvb)) return 1;
@@ -298,7 +300,7 @@ __device__ __forceinline__ void pair_emit(const PairParams &p, unsigned char *sm
     const int n0 = __popcll(m0), n1 = __popcll(m1);
     if (ph < 3) {
       const int pos = ph == 0 ? lanes_below(m0) : ph == 1 ? n0 + lanes_below(m1) : n0 + n1 + lanes_below(m2);
-      sch[pos] = make_int2(a, b);
+      sch[pos] = make_int2(first_key(a), first_key(b));
     }
     if (lane == 0) {
       cnt[0] = n0;
@@ -325,7 +327,7 @@ __device__ __forceinline__ void pair_emit(const PairParams &p, unsigned char *sm
     const uint64_t m0 = __ballot(ph == 0), m1 = __ballot(ph == 1), m2 = __ballot(ph == 2);
     if (ph < 3) {
       const int pos = ph == 0 ? r0 + lanes_below(m0) : ph == 1 ? r1 + lanes_below(m1) : r2 + lanes_below(m2);
-      sch[pos] = make_int2(a, b);
+      sch[pos] = make_int2(first_key(a), first_key(b));
     }
     r0 += __popcll(m0);
     r1 += __popcll(m1);
@@ -572,7 +574,7 @@ void attn_pair_kernel(PairParams p) {
   }
   auto entry = [&](int e, int &a, int &bb) {
     if (kDense) {
-      a = bb = e < d_nub ? d_t0 + e : p.nb - 1;
+      a = bb = (e < d_nub ? d_t0 + e : p.nb - 1) * kBlock;
       return;
     }
     if (e - ch_cb >= 64) {
@@ -586,11 +588,12 @@ void attn_pair_kernel(PairParams p) {
     a = __builtin_amdgcn_readlane(ch_a, e - ch_cb);
     bb = __builtin_amdgcn_readlane(ch_b, e - ch_cb);
   };
-  // First key of half tile `half` of block bl; T (no tile) for a missing
-  // block or a half that lies past T.
-  auto hkey = [&](int bl, int half) -> int {
-    const int k0 = bl * kBlock + 32 * half;
-    return (bl < 0 || k0 >= T) ? T : k0;
+  // First key of half tile `half` of the tile whose first key is k0; T (no
+  // tile) for a missing block (k0 = T) or a half that lies past T.
+  auto hkey = [&](int k0, int half) -> int {
+    if (half == 0) return k0;
+    const int k1 = k0 + 32;
+    return k1 < T ? k1 : T;
   };
 
   // ---- loads --------------------------------------------------------------
@@ -767,11 +770,15 @@ void attn_pair_kernel(PairParams p) {
 #pragma unroll
         for (int u = 0; u < 4; u += 2) {
           const int r = 4 * q4 + u;
-          const bf16x2 pk = {(__bf16)__builtin_amdgcn_exp2f(e[u]), (__bf16)__builtin_amdgcn_exp2f(e[u + 1])};
-          l_run = __builtin_amdgcn_fdot2_f32_bf16(pk, ones, l_run, false);
-          pf[r >> 3][r & 7] = pk[0];
-          pf[r >> 3][(r & 7) + 1] = pk[1];
+          pf[r >> 3][r & 7] = (__bf16)__builtin_amdgcn_exp2f(e[u]);
+          pf[r >> 3][(r & 7) + 1] = (__bf16)__builtin_amdgcn_exp2f(e[u + 1]);
         }
+      }
+      // row sums of the bf16-rounded P, from the packed fragment itself
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bf16x2 two = {pf[H0 >> 1][2 * i], pf[H0 >> 1][2 * i + 1]};
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(two, ones, l_run, false);
       }
     };
     auto exps = [&](float m_sub) {
@@ -904,7 +911,7 @@ void attn_pair_kernel(PairParams p) {
   // j%2 and V(j) in V slot j%2; K is fetched two steps ahead, V one ahead.
   // Step j issues V(j+1) and K(j+2) into the slots step j-1 finished
   // reading, and ends with the barrier that publishes them.
-  int ea = -1, eb = -1, na = -1, nb2 = -1;
+  int ea = T, eb = T, na = T, nb2 = T;   // first keys (T: no tile)
   if (nE > 0) entry(0, ea, eb);
   if (nE > 1) entry(1, na, nb2);
   if (nE > 0) {
