@@ -1,5 +1,9 @@
-// Block-sparse flash attention on gfx950 bf16 MFMA, shared by the sparse
-// (block lists) and dense (all key blocks) paths.
+// Block-sparse flash attention on gfx950 bf16 MFMA, one query block per
+// workgroup.  It serves the approximate branch (virtual summary keys) and
+// block lists longer than the paired kernel (attn_pair.hip) takes; the plain
+// sparse rows, the dense rows and the fused route run on the paired kernel.
+// This file also holds the combine kernel of the split-KV dense rows and the
+// launch dispatch between the two kernels.
 //
 // Page "Sol-Attn and Spark for MiniMax-H3", Spark inference integration:
 // selected K/V tiles stream through a single FP32 online-softmax/output
@@ -7,8 +11,7 @@
 // Contract: the natural-log key bias is converted to log2 units and consumed
 // only by the exact branch (sink keys).
 //
-// Workgroup = one 64-row query block of one (b, h) (or, on the dense path,
-// one key range of such a block: split-KV), four wavefronts: wave w owns query
+// Workgroup = one 64-row query block of one (b, h), four wavefronts: wave w owns query
 // rows 32*(w&1)..+31 and keys 32*(w>>1)..+31 of every 64-key tile, with its
 // own online-softmax state; the two key halves of each row are merged at the
 // end, each of the two waves of a row finishing and storing half of its
@@ -108,7 +111,7 @@ struct Params {
   int32_t *list_out, *cnt_out;
 };
 
-template <bool kDense, bool kSpark = false, bool kFused = false>
+template <bool kSpark = false, bool kFused = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_kernel(Params p) {
   // K ring (2 tiles) | V ring (2 tiles) | natural-log key bias ring (2 tiles)
@@ -116,10 +119,8 @@ void attn_fwd_kernel(Params p) {
   __shared__ __align__(16) unsigned char smem[kLdsBytes + (kSpark ? kVbBytes : 0) +
                                               (kFused ? kFusedBytes : 0)];
 
-  const int total = p.B * p.H * p.nqb * p.nsplit;
-  const int w = xcd_remap(blockIdx.x, total);
-  const int split = w % p.nsplit;
-  const int wq = w / p.nsplit;
+  const int total = p.B * p.H * p.nqb;
+  const int wq = xcd_remap(blockIdx.x, total);
   const int qbi = wq % p.nqb;
   const int bh = wq / p.nqb;
   const int h = bh % p.H;
@@ -150,13 +151,7 @@ void attn_fwd_kernel(Params p) {
   int list_cb = 0;
   int list_v = 0;   // entries list_cb .. +63
   int list_nv = 0;  // entries list_cb + 64 .. +63, loaded one tile early
-  if (kDense) {
-    t_begin = split * p.tiles_per_split;
-    t_end = t_begin + p.tiles_per_split;
-    t_end = t_end < p.nb ? t_end : p.nb;
-    const int pe = p.nvb < t_end ? p.nvb : t_end;
-    n_plain = pe > t_begin ? pe - t_begin : 0;
-  } else {
+  {
     const int64_t li = (int64_t)bh * p.nqb + qbi;
     int first, n;
     if (kFused) {
@@ -279,7 +274,6 @@ void attn_fwd_kernel(Params p) {
       j -= nv;
     }
     const int it = t_begin + j;
-    if (kDense) return it * kBlock;
     if (it - list_cb >= 64) {
       list_cb += 64;
       list_v = list_nv;
@@ -758,22 +752,6 @@ void attn_fwd_kernel(Params p) {
     l_tot = __builtin_fmaf(l0, a0, l1 * a1);
     m_used = m;
 
-    if (kDense && p.nsplit > 1) {
-      if (tq >= T) return;
-      // partial (unnormalised O, max, sum) of this key range
-      const int64_t prow = ((int64_t)wq * p.nsplit + split) * kBlock + (rw * 32 + c32);
-      float *po = p.part_o + prow * kHeadDim;
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int rq = 0; rq < 4; ++rq) {
-          const int d0 = 32 * (DT0 + u) + 8 * rq + 4 * g;
-          *reinterpret_cast<float4 *>(po + d0) = make_float4(o[DT0 + u][4 * rq + 0], o[DT0 + u][4 * rq + 1],
-                                                             o[DT0 + u][4 * rq + 2], o[DT0 + u][4 * rq + 3]);
-        }
-      if (MINE_FIRST && g == 0) *reinterpret_cast<float2 *>(p.part_ml + 2 * prow) = make_float2(m_used, l_tot);
-      return;
-    }
     // The wave's 32 half rows (128 B) go through LDS (a free part of the V
     // ring, 16-byte chunks XOR-swizzled by row) and out as whole half rows:
     // each store instruction writes eight 128-byte half rows.
@@ -903,7 +881,7 @@ hipError_t launch_attn_sparse(const AttnArgs &a, hipStream_t stream) {
   Params p = make_params(a, 0, a.nvq);
   p.row_hi = a.rows_end;
   const int total = a.B * a.H * a.nvq;
-  hipLaunchKernelGGL(attn_fwd_kernel<false>, dim3(total), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL(attn_fwd_kernel<>, dim3(total), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -914,7 +892,7 @@ hipError_t launch_attn_sparse_spark(const AttnArgs &a, hipStream_t stream) {
   Params p = make_params(a, 0, a.nvq);
   p.row_hi = a.rows_end;
   const int total = a.B * a.H * a.nvq;
-  hipLaunchKernelGGL((attn_fwd_kernel<false, true>), dim3(total), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((attn_fwd_kernel<true>), dim3(total), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -927,7 +905,7 @@ hipError_t launch_attn_sparse_fused(const AttnArgs &a, hipStream_t stream) {
   Params p = make_params(a, 0, a.nvq);
   p.row_hi = a.rows_end;
   const int total = a.B * a.H * a.nvq;
-  hipLaunchKernelGGL((attn_fwd_kernel<false, false, true>), dim3(total), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((attn_fwd_kernel<false, true>), dim3(total), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

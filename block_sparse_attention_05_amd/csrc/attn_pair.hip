@@ -10,12 +10,14 @@
 //
 // Why pairs.  A 64-row query block does 2.1 MFLOP per 64-key tile against
 // 32 KiB of K/V copied from L2 into LDS, 64 FLOP per byte: at the MFMA rate
-// of a CU that needs the whole global-to-LDS copy bandwidth of the CU, which
-// makes the copies the binding resource of a one-block workgroup.  Adjacent
-// query blocks of a video (two 2-row strips of the same frame) select mostly
-// the same key blocks: at the H3 shape two adjacent lists share about 65% of
-// their entries (all sink blocks and most routed ones), so serving both from
-// one tile stream cuts the copied bytes by about a third.
+// of a CU that is the whole global-to-LDS copy bandwidth of the CU.
+// Adjacent query blocks of a video (two 2-row strips of the same frame)
+// select mostly the same key blocks: at the H3 shape two adjacent lists
+// share about 65% of their entries (all sink blocks and most routed ones),
+// so serving both from one tile stream cuts the copied bytes by about a
+// third, and it halves the number of workgroups and their fixed costs.  (On
+// the measured workloads the time per FLOP comes out close to the one-block
+// kernel's: the copies turned out not to be what bounds a step.)
 //
 // Workgroup: four wavefronts; wave w serves rows 32*(w&1) .. +31 of block
 // A (w < 2) or B (w >= 2), over all 32 keys of a half tile per step, so every
@@ -26,10 +28,12 @@
 // one only B holds, 32 KiB copied).  Every list entry is two steps (the two
 // 32-key halves of its 64-key block).
 //
-// Schedule.  Wave 0 builds the entry list in LDS before the first tile load:
-// it compacts both lists (entries outside [0, NB) are skipped), splits them
-// into shared and private entries (binary search in the other list), pairs
-// the i-th private entry of A with the i-th of B, and orders the entries in
+// Schedule.  Waves 0 and 1 build the entry list in LDS before the first
+// tile load: they compact both lists (entries outside [0, NB) are skipped)
+// and split them into shared and private entries (binary search in the
+// other list); wave 0 pairs the i-th private entry of A with the i-th of B,
+// sorts the entries by their larger key block (so that the workgroups that
+// share an XCD sweep a head's keys together) and splits them, stably, into
 // three phases:
 //   U  - both tiles complete and unbiased (every entry when key_bias is NULL
 //        apart from the partial block);
@@ -46,8 +50,9 @@
 // buffer_load ... lds in the one-block kernel's tile layout (a slot is the
 // 64-key layout whose key halves hold A's and B's half tiles; a shared entry
 // fills the first half only).  Keys past T fall outside the buffer range and
-// read as zero.  K runs two steps ahead and V one, two slots each.  Q rows
-// are read straight into the MFMA operand registers (each wave reads only
+// read as zero.  K runs two steps ahead and V one, two slots each.  Each
+// wave copies its Q rows into the V ring in whole rows before the schedule
+// is built and reads its MFMA operand fragments from there (each wave reads only
 // its own rows).
 //
 // Math per step and wave (32 rows x 32 keys): S^T = K Q^T on
@@ -1133,6 +1138,7 @@ hipError_t launch_attn_pair_fused(const AttnArgs &a, hipStream_t stream) {
     return hipErrorInvalidValue;
   PairParams p = make_pair_params(a, 0, a.nvq);
   p.row_hi = a.rows_end;
+  p.slots = pair_slots_per_xcd();
   const int total = a.B * a.H * p.npair;
   hipLaunchKernelGGL((attn_pair_kernel<false, true, kPairDmaAt, kPairPlan>), dim3(total), dim3(kThreads), 0,
                      stream, p);
