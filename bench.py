@@ -179,16 +179,16 @@ def spark_measure(sa, wl, q, k, v, kb, idx, cnt, ws, out, dws, steps, sparse_flo
     }
 
 
-def traffic_for_current_kernel():
+def traffic_for_current_kernel(workload_name):
     """HBM bytes per sparse-attention launch measured with rocprofv3 counters
     (FETCH_SIZE + WRITE_SIZE, scaled by a copy-kernel calibration), if they
-    were taken on the current kernel source; else None."""
+    were taken on the current kernel source and this workload; else None."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     with open(TRAFFIC_FILE) as f:
         t = json.load(f)
     src_hash = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
-    if t.get("attn_src_sha256") != src_hash:
+    if t.get("attn_src_sha256") != src_hash or not t.get("workload", "").startswith(workload_name + " "):
         return None
     return t.get("bytes_per_launch")
 
@@ -204,6 +204,7 @@ def cpu_baseline(wl, heads):
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     except Exception:  # pragma: no cover
         threads = 1
+    heads = min(heads, wl.q.shape[2])
     f = lambda t: t[:, :, :heads].float().contiguous().numpy()
     q, k, v = f(wl.q), f(wl.k), f(wl.v)
     t0 = time.perf_counter()
@@ -225,7 +226,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="h3", choices=["h3", "h3_bias", "mid", "long", "tiny"])
+    ap.add_argument("--workload", default="h3", choices=["h3", "h3_bias", "mid", "long", "tiny", "h3_share"])
     ap.add_argument("--cpu-heads", type=int, default=56)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-spark", action="store_true",
@@ -409,7 +410,7 @@ def main():
                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
                      "algorithmic_gflop_per_launch": round(sparse_flops / 1e9, 3),
                      "launch_ms_mean": round(sparse_ms, 4),
-                     "traffic": traffic_for_current_kernel()},
+                     "traffic": traffic_for_current_kernel(wl.name)},
     }
     if not args.no_fused:
         res["fused_route"] = fused_measure(sa, wl, q, k, v, kb, idx, cnt, out, dws, args.steps,

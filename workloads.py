@@ -157,5 +157,14 @@ def h3_heads(H, seed=2, with_bias=False):
                     local_radius=0, key_bias=bias)
 
 
+def h3_share():
+    """One GPU's share of the H3 call split by head over eight GPUs: the H3
+    sequence shape and recipe with 7 heads (56 / 8)."""
+    w = h3_heads(7)
+    return Workload("h3_share_B1_H7_T9505", w.q, w.k, w.v, sink_start=w.sink_start,
+                    topk_ratio=w.topk_ratio, local_radius=w.local_radius)
+
+
 NAMED = {"tiny": tiny, "mid": mid, "h3": h3,
-         "h3_bias": lambda: h3(with_bias=True), "long": long, "max_blocks": max_blocks}
+         "h3_bias": lambda: h3(with_bias=True), "long": long, "max_blocks": max_blocks,
+         "h3_share": h3_share}
