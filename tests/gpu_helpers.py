@@ -1,6 +1,7 @@
 """Helpers for the GPU parity tests: run the HIP path through the C-ABI
 binding, run the oracle on the same bf16 inputs, compare."""
 import sys
+import time
 
 import numpy as np
 import torch
@@ -109,3 +110,58 @@ def pad_lists(idx, cnt, front, back, width):
     wide[..., width - 1] = torch.where(c + nf + len(back) > width - 1, wide[..., width - 1],
                                        torch.full_like(cnt, -1))
     return wide, (cnt + nf + len(back)).to(torch.int32)
+
+
+def check_route(res, rt, wl):
+    B, T, H, _ = wl.q.shape
+    nvb, nvq = rt.nvb, rt.nvq
+    if nvq == 0:
+        return
+    rows, mism, ties, unexp = compare_lists(res["idx"], res["cnt"], rt)
+    log(f"[{wl.name}] lists: rows={rows} mismatched={mism} near_ties={ties} unexplained={unexp}")
+    assert unexp == 0
+    if res["scores"] is not None and nvb > 0:
+        g = res["scores"].numpy()
+        # fp32 of an fp64 dot product on both sides: equal except where the two
+        # fp64 sums straddle an fp32 rounding boundary (1 ulp)
+        gi = g.view(np.int32).astype(np.int64)
+        oi = rt.scores.view(np.int32).astype(np.int64)
+        ulps = np.abs(gi - oi)
+        log(f"[{wl.name}] scores: bit-equal={np.mean(ulps == 0):.6f} max_ulp={ulps.max()}")
+        assert ulps.max() <= 1
+    # forced and sink blocks always present
+    idx, cnt = res["idx"].numpy(), res["cnt"].numpy()
+    nb = rt.nb
+    for b in range(B):
+        for h in range(H):
+            for i in range(nvq):
+                s = set(idx[b, h, i, :cnt[b, h, i]].tolist())
+                assert set(ora.forced_blocks(i, nvb, wl.local_radius)) <= s
+                assert set(range(nvb, nb)) <= s
+
+
+def full_parity(wl, key_bias=None):
+    q, k, v = (to_np(x) for x in (wl.q, wl.k, wl.v))
+    kb = key_bias if key_bias is not None else wl.key_bias
+    kbn = None if kb is None else kb.numpy()
+    log(f"[{wl.name}] GPU run")
+    res = run_gpu(wl, key_bias=kb)
+    t0 = time.perf_counter()
+    log(f"[{wl.name}] oracle route")
+    rt = ora.route(q, k, wl.sink_start, wl.topk_ratio, wl.local_radius, tail_mode=wl.tail_mode)
+    check_route(res, rt, wl)
+    adopt_lists(res["idx"], res["cnt"], rt)
+    log(f"[{wl.name}] oracle attention ({time.perf_counter() - t0:.1f} s so far)")
+    want, want_lse, _ = ora.routed_attention(q, k, v, wl.sink_start, wl.topk_ratio,
+                                             wl.local_radius, key_bias=kbn, rt=rt)
+    got = to_np(res["out"])
+    assert np.isfinite(got).all()
+    mx, mean = err_stats(got, want)
+    lmx, _ = err_stats(res["lse"].numpy(), want_lse)
+    worst = np.unravel_index(np.argmax(np.abs(got - want)), got.shape)
+    log(f"[{wl.name}] every element: out max_abs={mx:.3e} (oracle value there {want[worst]:.4f}) "
+        f"mean_abs={mean:.3e} |out|max={np.abs(want).max():.3f} lse max_abs={lmx:.3e} "
+        f"(oracle {time.perf_counter() - t0:.1f} s)")
+    assert mx <= MAX_ABS and mean <= MEAN_ABS
+    assert lmx <= 1e-2
+    return res, rt

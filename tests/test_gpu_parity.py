@@ -14,78 +14,24 @@ import torch
 
 import oracle.sparse_attention as ora
 import workloads
-from gpu_helpers import (MAX_ABS, MEAN_ABS, adopt_lists, compare_lists, err_stats, log, pad_lists,
-                         run_gpu, to_np)
+from gpu_helpers import (MAX_ABS, MEAN_ABS, adopt_lists, check_route, compare_lists, err_stats,
+                         full_parity, log, pad_lists, run_gpu, to_np)
 
 pytestmark = pytest.mark.gpu
 
 
-def _check_route(res, rt, wl):
-    B, T, H, _ = wl.q.shape
-    nvb, nvq = rt.nvb, rt.nvq
-    if nvq == 0:
-        return
-    rows, mism, ties, unexp = compare_lists(res["idx"], res["cnt"], rt)
-    log(f"[{wl.name}] lists: rows={rows} mismatched={mism} near_ties={ties} unexplained={unexp}")
-    assert unexp == 0
-    if res["scores"] is not None and nvb > 0:
-        g = res["scores"].numpy()
-        # fp32 of an fp64 dot product on both sides: equal except where the two
-        # fp64 sums straddle an fp32 rounding boundary (1 ulp)
-        gi = g.view(np.int32).astype(np.int64)
-        oi = rt.scores.view(np.int32).astype(np.int64)
-        ulps = np.abs(gi - oi)
-        log(f"[{wl.name}] scores: bit-equal={np.mean(ulps == 0):.6f} max_ulp={ulps.max()}")
-        assert ulps.max() <= 1
-    # forced and sink blocks always present
-    idx, cnt = res["idx"].numpy(), res["cnt"].numpy()
-    nb = rt.nb
-    for b in range(B):
-        for h in range(H):
-            for i in range(nvq):
-                s = set(idx[b, h, i, :cnt[b, h, i]].tolist())
-                assert set(ora.forced_blocks(i, nvb, wl.local_radius)) <= s
-                assert set(range(nvb, nb)) <= s
-
-
-def _full_parity(wl, key_bias=None):
-    q, k, v = (to_np(x) for x in (wl.q, wl.k, wl.v))
-    kb = key_bias if key_bias is not None else wl.key_bias
-    kbn = None if kb is None else kb.numpy()
-    log(f"[{wl.name}] GPU run")
-    res = run_gpu(wl, key_bias=kb)
-    t0 = time.perf_counter()
-    log(f"[{wl.name}] oracle route")
-    rt = ora.route(q, k, wl.sink_start, wl.topk_ratio, wl.local_radius, tail_mode=wl.tail_mode)
-    _check_route(res, rt, wl)
-    adopt_lists(res["idx"], res["cnt"], rt)
-    log(f"[{wl.name}] oracle attention ({time.perf_counter() - t0:.1f} s so far)")
-    want, want_lse, _ = ora.routed_attention(q, k, v, wl.sink_start, wl.topk_ratio,
-                                             wl.local_radius, key_bias=kbn, rt=rt)
-    got = to_np(res["out"])
-    assert np.isfinite(got).all()
-    mx, mean = err_stats(got, want)
-    lmx, _ = err_stats(res["lse"].numpy(), want_lse)
-    log(f"[{wl.name}] every element: out max_abs={mx:.3e} mean_abs={mean:.3e} "
-        f"|out|max={np.abs(want).max():.3f} lse max_abs={lmx:.3e} "
-        f"(oracle {time.perf_counter() - t0:.1f} s)")
-    assert mx <= MAX_ABS and mean <= MEAN_ABS
-    assert lmx <= 1e-2
-    return res, rt
-
-
 def test_tiny_full():
-    _full_parity(workloads.tiny())
+    full_parity(workloads.tiny())
 
 
 def test_tiny_batch2_radius2():
     q, k, v = workloads.tiny_qkv(B=2, H=3, T=1024, seed=5)
     wl = workloads.Workload("tiny_B2_H3_r2", q, k, v, sink_start=1024, topk_ratio=0.3, local_radius=2)
-    _full_parity(wl)
+    full_parity(wl)
 
 
 def test_mid_full():
-    _full_parity(workloads.mid())
+    full_parity(workloads.mid())
 
 
 def test_split_video_block_and_bias():
@@ -96,7 +42,7 @@ def test_split_video_block_and_bias():
     bias = workloads.sink_key_bias(1, q.shape[1], tv2, seed=8)
     wl = workloads.Workload("split_block", q, k, v, sink_start=tv2, topk_ratio=0.2, local_radius=1,
                             key_bias=bias)
-    _full_parity(wl)
+    full_parity(wl)
 
 
 # ---- pad video tail mode ---------------------------------------------------
@@ -111,7 +57,7 @@ def _split_workload(mode, name="split_block"):
 
 def test_pad_split_video_block_and_bias():
     # block 15 (47 real video rows) is routed and sparse, context rows dense
-    res, rt = _full_parity(_split_workload("pad"))
+    res, rt = full_parity(_split_workload("pad"))
     assert rt.nvq == rt.nvb + 1 and res["cnt"].shape[2] == rt.nvq
 
 
@@ -121,7 +67,7 @@ def test_pad_h3_shape_split_tail():
     bias = workloads.sink_key_bias(1, q.shape[1], tv - 17, seed=14)
     wl = workloads.Workload("h3_H4_pad", q, k, v, sink_start=tv - 17, topk_ratio=0.1,
                             local_radius=1, key_bias=bias, tail_mode="pad")
-    _full_parity(wl)
+    full_parity(wl)
 
 
 def test_pad_without_complete_video_block():
@@ -129,7 +75,7 @@ def test_pad_without_complete_video_block():
     q, k, v = workloads.random_qkv(1, 700, 2, seed=15)
     wl = workloads.Workload("pad_nvb0", q, k, v, sink_start=40, topk_ratio=0.1, local_radius=1,
                             tail_mode="pad")
-    res, rt = _full_parity(wl)
+    res, rt = full_parity(wl)
     assert res["cnt"].flatten().tolist() == [11, 11]
 
 
@@ -217,19 +163,19 @@ def test_exact_ties_break_to_lower_index(nvb, ratio, radius, copies):
 def test_no_video_blocks_all_dense():
     q, k, v = workloads.random_qkv(1, 700, 2, seed=9)
     wl = workloads.Workload("all_dense", q, k, v, sink_start=40, topk_ratio=0.1, local_radius=1)
-    _full_parity(wl)
+    full_parity(wl)
 
 
 def test_single_video_block():
     q, k, v = workloads.random_qkv(1, 200, 2, seed=10)
     wl = workloads.Workload("one_block", q, k, v, sink_start=100, topk_ratio=0.1, local_radius=0)
-    _full_parity(wl)
+    full_parity(wl)
 
 
 def test_ratio_one_is_dense_and_matches_oracle():
     q, k, v = workloads.random_qkv(1, 1000, 2, seed=11)
     wl = workloads.Workload("ratio_one", q, k, v, sink_start=900, topk_ratio=1.0, local_radius=0)
-    _full_parity(wl)
+    full_parity(wl)
 
 
 def test_ratio_one_sparse_bit_identical_to_dense_kernel():
@@ -336,21 +282,21 @@ def test_pooled_means_bit_exact():
 # ---- full-size workloads: every list, every output and LSE element --------
 
 def test_h3_full():
-    _full_parity(workloads.h3())
+    full_parity(workloads.h3())
 
 
 def test_h3_keybias_full():
-    _full_parity(workloads.h3(with_bias=True))
+    full_parity(workloads.h3(with_bias=True))
 
 
 def test_long_full():
-    _full_parity(workloads.long())
+    full_parity(workloads.long())
 
 
 def test_max_route_blocks_full():
     """NVB = 1024 (the widest route row): lists of 110 entries, walked in two
     chunks."""
-    _full_parity(workloads.max_blocks())
+    full_parity(workloads.max_blocks())
 
 
 def test_h3_deterministic_repeat():
@@ -435,7 +381,7 @@ def test_pad_batch2_radius2_with_bias():
     bias = workloads.sink_key_bias(2, 1100, 1000, seed=18)
     wl = workloads.Workload("pad_B2_H3_r2", q, k, v, sink_start=1000, topk_ratio=0.3, local_radius=2,
                             key_bias=bias, tail_mode="pad")
-    _full_parity(wl)
+    full_parity(wl)
 
 
 def _mid_lists():
