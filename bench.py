@@ -69,6 +69,11 @@ def effective_flops_from_lists(cnt, idx, T, nvb, H, B):
     return 4 * 128 * sparse_pairs, 4 * 128 * dense_pairs
 
 
+# GPU time of untimed back-to-back steps before each measured loop, enough
+# for the clock to reach its steady state under this load.
+SETTLE_MS = 100.0
+
+
 def fused_measure(sa, wl, q, k, v, kb, idx, cnt, out, dws, steps, sparse_flops):
     """Per-stage and whole-call times with the route inside the attention
     kernel (pool, fused sparse rows, dense rows; one stream), and whether its
@@ -289,48 +294,49 @@ def main():
     def dense():
         sa.dense_sink_fwd(q, k, v, ss, key_bias=kb, out=out, workspace=dws, check_bias=False)
 
-    def step():
-        if side is stream:
-            route()
-            sparse()
-            dense()
-            return
-        side.wait_stream(stream)
+    def step(sparse_ev=None):
+        # sparse_ev: optional pair of events recorded on the main stream right
+        # before and after the sparse launch
+        if side is not stream:
+            side.wait_stream(stream)
         route()
-        with torch.cuda.stream(side):   # queued behind the pool/route launches
-            dense()
+        if side is not stream:
+            with torch.cuda.stream(side):   # queued behind the pool/route launches
+                dense()
+        if sparse_ev:
+            sparse_ev[0].record(stream)
         sparse()
-        stream.wait_stream(side)
+        if sparse_ev:
+            sparse_ev[1].record(stream)
+        if side is stream:
+            dense()
+        else:
+            stream.wait_stream(side)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    # From a cold start, or after about a second without work, the first
+    # 20-40 ms of back-to-back steps run up to a fifth slower than the steady
+    # state while the GPU's clock comes up.  Every measured loop below
+    # (diagnostics and headline alike) is therefore preceded by untimed steps
+    # worth SETTLE_MS of GPU time; none of them is inside a timed region.
+    def settle():
+        done_ms, n = 0.0, 0
+        while done_ms < SETTLE_MS:
+            a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a0.record(stream)
+            for _ in range(20):
+                step()
+            a1.record(stream)
+            torch.cuda.synchronize()
+            done_ms += a0.elapsed_time(a1)
+            n += 20
+        return n
 
-    # whole-step timing: events only at the ends
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    step()
     torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
+    sparse_flops, dense_flops = effective_flops_from_lists(cnt, idx, T, nvb, H, B)
+    untimed = {"first_step": 1}
 
-    # the same back-to-back loop once more with an event between consecutive
-    # steps (GPU time of each step in order, gaps between steps included) and
-    # the host's enqueue time per step, to see where the back-to-back mean
-    # and the per-call times part
-    sev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    host_us = []
-    torch.cuda.synchronize()
-    sev[0].record(stream)
-    for i in range(args.steps):
-        h0 = time.perf_counter()
-        step()
-        sev[i + 1].record(stream)
-        host_us.append((time.perf_counter() - h0) * 1e6)
-    torch.cuda.synchronize()
-    seq_ms = [sev[i].elapsed_time(sev[i + 1]) for i in range(args.steps)]
+    untimed["settle_steps_1"] = settle()
 
     # per-call distribution of the same schedule: an event pair around every
     # call (the events sit on the main stream, which joins the side stream)
@@ -343,6 +349,7 @@ def main():
         a1.record(stream)
     torch.cuda.synchronize()
     calls = np.array([a0.elapsed_time(a1) for a0, a1 in cev])
+    untimed["per_call_steps"] = args.steps
 
     # per-stage timing: the three calls back to back on the main stream, with
     # events between them, so that each kernel is timed alone
@@ -359,16 +366,67 @@ def main():
     torch.cuda.synchronize()
     st = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(3)] for e in evs])
     med = np.median(st, axis=0)
+    untimed["per_stage_steps"] = args.steps
+
+    extra = {}
+    if not args.no_fused:
+        untimed["settle_steps_2"] = settle()
+        extra["fused_route"] = fused_measure(sa, wl, q, k, v, kb, idx, cnt, out, dws, args.steps,
+                                             sparse_flops)
+        untimed["fused_route_passes"] = args.steps + 4
+    if not args.no_spark:
+        untimed["settle_steps_3"] = settle()
+        extra["spark"] = spark_measure(sa, wl, q, k, v, kb, idx, cnt, ws, out, dws, args.steps,
+                                       sparse_flops, dense_flops)
+        untimed["spark_passes"] = args.steps + 3
+    torch.cuda.synchronize()
+
+    untimed["settle_steps_4"] = settle()
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # whole-step timing: events only at the ends
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+
+    # the same back-to-back loop once more with an event between consecutive
+    # steps (GPU time of each step in order, gaps between steps included),
+    # events around every sparse launch (its duration as the timed steps run
+    # it, the dense rows on the side stream overlapping part of it) and the
+    # host's enqueue time per step
+    sev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    spev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(args.steps)]
+    host_us = []
+    torch.cuda.synchronize()
+    sev[0].record(stream)
+    for i in range(args.steps):
+        h0 = time.perf_counter()
+        step(spev[i])
+        sev[i + 1].record(stream)
+        host_us.append((time.perf_counter() - h0) * 1e6)
+    torch.cuda.synchronize()
+    seq_ms = [sev[i].elapsed_time(sev[i + 1]) for i in range(args.steps)]
+    sparse_in_step = np.array([a0.elapsed_time(a1) for a0, a1 in spev])
 
     # bf16 MFMA peak from this device's CU count and peak clock:
     # 4 SIMDs x 1024 FLOP per clock per CU (one 32x32x16 MFMA per 32 clocks)
     cu, clk_khz = sa.sa_device_info(0)
     peak_dev = {"tflops": round(cu * clk_khz * 1e3 * 4096 / 1e12, 1), "cu": cu, "clock_mhz": clk_khz / 1e3}
 
-    sparse_flops, dense_flops = effective_flops_from_lists(cnt, idx, T, nvb, H, B)
     total_flops = sparse_flops + dense_flops
     tflops = total_flops / (ms * 1e-3) / 1e12
-    sparse_ms = float(st[:, 1].mean())
+    # the sparse kernel's mean launch duration as the timed steps run it
+    # (prices the roofline), and alone on one stream (the per-stage loop)
+    sparse_ms = float(sparse_in_step.mean())
+    sparse_alone_ms = float(st[:, 1].mean())
     achieved = sparse_flops / (sparse_ms * 1e-3) / 1e12
 
     res = {
@@ -388,6 +446,12 @@ def main():
                    "sink_tokens": T - ss, "topk_ratio": wl.topk_ratio, "local_radius": wl.local_radius,
                    "key_bias": kb is not None, "inputs": "smooth-field+noise Q/K, N(0,1) V, seed 2"},
         "ms_per_call": round(ms, 4),
+        "timed_after": {"loops": untimed, "settle_gpu_ms_each": SETTLE_MS, "warmup_steps": args.warmup,
+                        "note": "untimed loops in run order: a first step, clock-settling steps, "
+                                "per-call and per-stage timing, settling, the fused-route loop, "
+                                "settling, the Spark loop, settling, then the warm-up steps and "
+                                "the timed steps; the back-to-back list below is one more pass "
+                                "right after them"},
         "back_to_back_steps_ms_in_order": [round(x, 4) for x in seq_ms],
         "host_enqueue_us_per_step_median_max": [round(float(np.median(host_us)), 1),
                                                 round(float(np.max(host_us)), 1)],
@@ -410,14 +474,12 @@ def main():
                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
                      "algorithmic_gflop_per_launch": round(sparse_flops / 1e9, 3),
                      "launch_ms_mean": round(sparse_ms, 4),
+                     "launch_ms_from": "events around each sparse launch in the back-to-back pass "
+                                       "(same streams as the timed steps)",
+                     "launch_ms_mean_alone_one_stream": round(sparse_alone_ms, 4),
                      "traffic": traffic_for_current_kernel(wl.name)},
     }
-    if not args.no_fused:
-        res["fused_route"] = fused_measure(sa, wl, q, k, v, kb, idx, cnt, out, dws, args.steps,
-                                           sparse_flops)
-    if not args.no_spark:
-        res["spark"] = spark_measure(sa, wl, q, k, v, kb, idx, cnt, ws, out, dws, args.steps,
-                                     sparse_flops, dense_flops)
+    res.update(extra)
     if not args.no_cpu_baseline:
         cb = cpu_baseline(wl, args.cpu_heads)
         cb.pop("seconds")
