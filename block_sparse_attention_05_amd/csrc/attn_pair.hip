@@ -15,9 +15,10 @@
 // select mostly the same key blocks: at the H3 shape two adjacent lists
 // share about 65% of their entries (all sink blocks and most routed ones),
 // so serving both from one tile stream cuts the copied bytes by about a
-// third, and it halves the number of workgroups and their fixed costs.  (On
-// the measured workloads the time per FLOP comes out close to the one-block
-// kernel's: the copies turned out not to be what bounds a step.)
+// third, and it halves the number of workgroups and their fixed costs.
+// The copies still cost a step a good share of its time: on the H3 shape a
+// paired step copies 32 KiB per workgroup, about what a CU moves from L2 to
+// LDS in the time of the step's MFMAs.
 //
 // Workgroup: four wavefronts; wave w serves rows 32*(w&1) .. +31 of block
 // A (w < 2) or B (w >= 2), over all 32 keys of a half tile per step, so every
@@ -50,7 +51,9 @@
 // buffer_load ... lds in the one-block kernel's tile layout (a slot is the
 // 64-key layout whose key halves hold A's and B's half tiles; a shared entry
 // fills the first half only).  Keys past T fall outside the buffer range and
-// read as zero.  K runs two steps ahead and V one, two slots each.  Each
+// read as zero.  Step j issues, at its start, K of step j+2 and V of step
+// j+1 into the slots step j-1 finished reading (two slots each), and ends
+// with the wait and the barrier that publish them.  Each
 // wave copies its Q rows into the V ring in whole rows before the schedule
 // is built and reads its MFMA operand fragments from there (each wave reads only
 // its own rows).
@@ -58,9 +61,13 @@
 // Math per step and wave (32 rows x 32 keys): S^T = K Q^T on
 // v_mfma_f32_32x32x16_bf16, online softmax in base 2 with lazy rescaling
 // (slack 8), P rounded to bf16, O^T += V^T P^T with V^T from
-// ds_read_b64_tr_b16; the S(j+1) MFMAs of the next step overlap the softmax
-// of this one.  The same arithmetic as the one-block kernel, with the keys of
-// a 64-key tile accumulated in two sequential steps instead of two waves.
+// ds_read_b64_tr_b16.  A full-tile step issues its copies, takes the tile
+// max and the rare rescale, then runs one straight block in a fixed order:
+// each of the eight S(j+1) MFMAs is followed by the exponentials of two of
+// the lane's logits of tile j, so that the wave's matrix and vector work
+// overlap, and the eight PV MFMAs close the step.  The same arithmetic as
+// the one-block kernel, with the keys of a 64-key tile accumulated in two
+// sequential steps instead of two waves.
 #include <atomic>
 
 #include "attn_common.h"
@@ -345,13 +352,7 @@ __device__ __forceinline__ void pair_emit(const PairParams &p, unsigned char *sm
   }
 }
 
-// kPlan: 0 the step's PV MFMAs run after all its exponentials; 1 the
-// exponentials of the second 16 keys run beside the PV MFMAs of the first.
-// kDmaAt: where a steady-state step issues its copies (V of the next step, K
-// of the step after): 0 both before the step's math, 1 both after the max
-// block, 2 K before and V after the max block, 3 K after the max block and V
-// after the exponentials, 4 V before and K after the max block.
-template <bool kDense, bool kFused, int kDmaAt, int kPlan>
+template <bool kDense, bool kFused>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_pair_kernel(PairParams p) {
   __shared__ __align__(16) unsigned char smem[kPLdsBytes];
@@ -709,14 +710,22 @@ void attn_pair_kernel(PairParams p) {
     const unsigned char *kbuf = smem + kPKOff + (VS ^ 1) * 16384 + rh_n;
     const float *bs = reinterpret_cast<const float *>(smem + kPBOff + VS * 256 + (rh >> 6));
 
-    auto qk_part = [&](auto lo_c, auto hi_c) {
-      constexpr int LO = decltype(lo_c)::value;
-      constexpr int HI = decltype(hi_c)::value;
+    // K fragment dc of S(j+1) (dims 16*dc .. +15) and V fragment dt of keys
+    // 16*kc .. +15 (dims 32*dt .. +31, transposed on the read)
+    auto k_frag = [&](int dc) -> bf16x8 {
+      return *reinterpret_cast<const bf16x8 *>(kbuf + (k_rd0 ^ (32u * (dc & 3))) + 1024 * (dc >> 2));
+    };
+    auto v_frag = [&](int kc, int dt) -> bf16x8 {
+      const unsigned char *src = vbuf + ((dt & 1) ? (v_rd0 ^ 64u) : v_rd0) + 4096 * kc + 1024 * (dt >> 1);
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, src));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, src + 2048));
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    auto qk = [&]() {
 #pragma unroll
-      for (int dc = LO; dc < HI; ++dc) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(kbuf + (k_rd0 ^ (32u * (dc & 3))) + 1024 * (dc >> 2));
-        s_nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[dc], s_nxt, 0, 0, 0);
-      }
+      for (int r = 0; r < 16; ++r) s_nxt[r] = 0.f;
+#pragma unroll
+      for (int dc = 0; dc < 8; ++dc) s_nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag(dc), qf[dc], s_nxt, 0, 0, 0);
     };
     auto bias4 = [&](int q4) {
       const float4 b4 = *reinterpret_cast<const float4 *>(bs + 8 * q4 + 4 * g);
@@ -790,21 +799,12 @@ void attn_pair_kernel(PairParams p) {
       exps_half(m_sub, Int<0>{});
       exps_half(m_sub, Int<1>{});
     };
-    // O^T += V^T P^T over keys 16*kc .. +15 of the half tile
-    auto pv_half = [&](auto kc_c) {
-      constexpr int KC = decltype(kc_c)::value;
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        const unsigned char *src = vbuf + ((dt & 1) ? (v_rd0 ^ 64u) : v_rd0) + 4096 * KC + 1024 * (dt >> 1);
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, src));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, src + 2048));
-        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[KC], o[dt], 0, 0, 0);
-      }
-    };
+    // O^T += V^T P^T over the half tile's 32 keys
     auto pv = [&]() {
-      pv_half(Int<0>{});
-      pv_half(Int<1>{});
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_frag(kc, dt), pf[kc], o[dt], 0, 0, 0);
     };
 
     if (MASKED) {
@@ -812,11 +812,7 @@ void attn_pair_kernel(PairParams p) {
       // has one
       dma_k();
       dma_v();
-      if (DO_QK) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s_nxt[r] = 0.f;
-        qk_part(Int<0>{}, Int<8>{});
-      }
+      if (DO_QK) qk();
       if (my_key >= T) return;     // this wave's block has no tile in this step
       const int kbase = my_key + 4 * g;   // key of s[r] = kbase + 8*(r/4) + r%4
 #pragma unroll
@@ -828,86 +824,67 @@ void attn_pair_kernel(PairParams p) {
       return;
     }
 
-    if (kDmaAt == 0 || kDmaAt == 2) dma_k();
-    if (kDmaAt == 0 || kDmaAt == 4) dma_v();
-    // -- block A: max of tile j (+ first S(j+1) MFMAs) --
-    if (DO_QK) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s_nxt[r] = 0.f;
-      qk_part(Int<0>{}, Int<3>{});
-    }
-    const float mt = tile_max();
-    if (DO_QK) {
-      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 3, 0);
-#pragma unroll
-      for (int i = 0; i < 3; ++i) {
-        __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedVALU, 4, 0);
-      }
-    }
-    if (kDmaAt == 1 || kDmaAt == 3 || kDmaAt == 4) dma_k();
-    if (kDmaAt == 1 || kDmaAt == 2) dma_v();
-    rescale(mt);
+    // Full tiles.  Copies, the max of tile j and the rare rescale come
+    // first; all of them may branch.  Then one straight block in a fixed
+    // order (sched_barrier fences keep the scheduler from regrouping it):
+    // the K fragments of S(j+1) are read at once, every S(j+1) MFMA is
+    // followed by the exponentials of two of this lane's logits (so that
+    // the matrix and vector units of the wave work side by side), the V
+    // fragments are read half way, and the PV MFMAs end the step.  Every
+    // sum runs in the same order as in the general step above.
+    dma_k();
+    dma_v();
+    rescale(tile_max());
     const float m_sub = (m_used == -INFINITY) ? 0.f : m_used;
-
-    if (kPlan == 0) {
-      // -- block B: P of tile j (+ remaining S(j+1) MFMAs), raised priority --
-      __builtin_amdgcn_s_setprio(1);
-      if (DO_QK) qk_part(Int<3>{}, Int<8>{});
-      exps(m_sub);
-      if (DO_QK) {
-        __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 2, 0);
-#pragma unroll
-        for (int i = 0; i < 3; ++i) {
-          __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(kSchedVALU, 8, 0);
-        }
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(kSchedVALU, 8, 0);
-        }
-      }
-      if (kDmaAt == 3) dma_v();
-      // -- block C: O^T += V^T P^T over the half tile's 32 keys --
-      pv();
-      __builtin_amdgcn_s_setprio(0);
-      return;
-    }
-    // kPlan 1: the exponentials of keys 16-31 run beside the PV MFMAs of
-    // keys 0-15, so that every block of the step pairs MFMAs with VALU work.
-    // -- block B: P of keys 0-15 (+ remaining S(j+1) MFMAs) --
     __builtin_amdgcn_s_setprio(1);
-    if (DO_QK) qk_part(Int<3>{}, Int<8>{});
-    exps_half(m_sub, Int<0>{});
+    bf16x8 kf[8];
     if (DO_QK) {
-      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 2, 0);
 #pragma unroll
-      for (int i = 0; i < 3; ++i) {
-        __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedVALU, 5, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedVALU, 5, 0);
-      }
+      for (int dc = 0; dc < 8; ++dc) kf[dc] = k_frag(dc);
     }
-    if (kDmaAt == 3) dma_v();
-    // -- block C: PV of keys 0-15 beside P of keys 16-31 --
-    pv_half(Int<0>{});
-    exps_half(m_sub, Int<1>{});
-    __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 4, 0);
+    bf16x8 vf[4], vg[4];
+    float4 bq = make_float4(0.f, 0.f, 0.f, 0.f);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedVALU, 6, 0);
+    for (int i = 0; i < 8; ++i) {
+      if (DO_QK) {
+        if (i == 0) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s_nxt[r] = 0.f;
+        }
+        s_nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[i], s_nxt, 0, 0, 0);
+      }
+      // logits r = 2i, 2i+1 (q4 = i/2)
+      const int r = 2 * i;
+      if (BIASED && (i & 1) == 0) bq = bias4(i >> 1);
+      float e0, e1;
+      if (BIASED) {
+        e0 = __builtin_fmaf(s_cur[r], c, ((i & 1) ? bq.z : bq.x) - m_sub);
+        e1 = __builtin_fmaf(s_cur[r + 1], c, ((i & 1) ? bq.w : bq.y) - m_sub);
+      } else {
+        e0 = __builtin_fmaf(s_cur[r], c, -m_sub);
+        e1 = __builtin_fmaf(s_cur[r + 1], c, -m_sub);
+      }
+      pf[r >> 3][r & 7] = (__bf16)__builtin_amdgcn_exp2f(e0);
+      pf[r >> 3][(r & 7) + 1] = (__bf16)__builtin_amdgcn_exp2f(e1);
+      const bf16x2 two = {pf[r >> 3][r & 7], pf[r >> 3][(r & 7) + 1]};
+      l_run = __builtin_amdgcn_fdot2_f32_bf16(two, ones, l_run, false);
+      // V fragments of keys 0-15 and 16-31, read while the S(j+1) MFMAs
+      // run (late enough that few K fragments are still held)
+      if (i == 3) {
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) vf[dt] = v_frag(0, dt);
+      }
+      if (i == 5) {
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) vg[dt] = v_frag(1, dt);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    // -- block D: PV of keys 16-31 --
-    pv_half(Int<1>{});
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[dt], pf[0], o[dt], 0, 0, 0);
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vg[dt], pf[1], o[dt], 0, 0, 0);
     __builtin_amdgcn_s_setprio(0);
   };
 
@@ -1037,9 +1014,6 @@ void attn_pair_kernel(PairParams p) {
     p.lse[((int64_t)b * p.H + h) * T + tq] = (m_used + __log2f(l_tot)) * kLn2;
 }
 
-constexpr int kPairDmaAt = 3;
-constexpr int kPairPlan = 0;
-
 PairParams make_pair_params(const AttnArgs &a, int qb0, int nqb) {
   PairParams p{};
   p.q = static_cast<const uint16_t *>(a.q);
@@ -1127,7 +1101,7 @@ hipError_t launch_attn_pair_sparse(const AttnArgs &a, hipStream_t stream) {
   p.row_hi = a.rows_end;
   p.slots = pair_slots_per_xcd();
   const int total = a.B * a.H * p.npair;
-  hipLaunchKernelGGL((attn_pair_kernel<false, false, kPairDmaAt, kPairPlan>), dim3(total), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((attn_pair_kernel<false, false>), dim3(total), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -1140,7 +1114,7 @@ hipError_t launch_attn_pair_fused(const AttnArgs &a, hipStream_t stream) {
   p.row_hi = a.rows_end;
   p.slots = pair_slots_per_xcd();
   const int total = a.B * a.H * p.npair;
-  hipLaunchKernelGGL((attn_pair_kernel<false, true, kPairDmaAt, kPairPlan>), dim3(total), dim3(kThreads), 0,
+  hipLaunchKernelGGL((attn_pair_kernel<false, true>), dim3(total), dim3(kThreads), 0,
                      stream, p);
   return hipGetLastError();
 }
@@ -1157,7 +1131,7 @@ hipError_t launch_attn_pair_dense(const AttnArgs &a, float *part_o, float *part_
     p.part_ml = part_ml;
   }
   const int total = a.B * a.H * p.npair * p.nsplit;
-  hipLaunchKernelGGL((attn_pair_kernel<true, false, kPairDmaAt, kPairPlan>), dim3(total), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((attn_pair_kernel<true, false>), dim3(total), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
