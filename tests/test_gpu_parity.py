@@ -213,6 +213,34 @@ def test_dense_split_and_unsplit_agree_with_oracle():
             assert mx <= MAX_ABS and mean <= MEAN_ABS
 
 
+def test_dense_rows_odd_block_count_batch2():
+    """Seven dense query blocks per head (odd: the last pair of every head
+    has no block B) and five heads, batch 2.  Every dense row of every head
+    and batch, out and LSE, with and without the split-KV workspace."""
+    import block_sparse_attention_05_amd as sa
+    B, T, H, ss = 2, 1000, 5, 576
+    assert (sa.sa_num_blocks(T) - ss // 64) % 2 == 1
+    q, k, v = (x.cuda() for x in workloads.random_qkv(B, T, H, seed=41))
+    bias = workloads.sink_key_bias(B, T, ss, seed=42)
+    assert sa.sa_dense_workspace_bytes(B, T, H, ss) > 0
+    lse_a = torch.full((B, H, T), float("nan"), device="cuda")
+    lse_b = torch.full((B, H, T), float("nan"), device="cuda")
+    a = sa.dense_sink_fwd(q, k, v, ss, key_bias=bias.cuda(), lse=lse_a)
+    b = sa.dense_sink_fwd(q, k, v, ss, key_bias=bias.cuda(), lse=lse_b, workspace=None)
+    torch.cuda.synchronize()
+    rows = np.arange(ss, T)
+    qn, kn, vn = (to_np(x) for x in (q, k, v))
+    for bb in range(B):
+        for h in range(H):
+            want, want_lse = ora.dense_rows_output(qn, kn, vn, bb, h, rows, bias.numpy(), ss // 64)
+            for got, gl in ((a, lse_a), (b, lse_b)):
+                mx, mean = err_stats(to_np(got[bb, ss:, h]), want)
+                lmx, _ = err_stats(to_np(gl[bb, h, ss:]), want_lse)
+                assert mx <= MAX_ABS and mean <= MEAN_ABS, (bb, h, mx, mean)
+                assert lmx <= 1e-2, (bb, h, lmx)
+    log(f"[dense odd blocks, B{B} H{H}] every row within tolerance, split and unsplit")
+
+
 def test_zero_bias_bit_identical_to_no_bias():
     wl = workloads.mid()
     a = run_gpu(wl, scores=False)
