@@ -45,7 +45,9 @@
 // U and Bi steps are straight-line code; G steps mask keys past T and skip
 // the softmax of a block without a tile.  The dense path (dense_sink_fwd)
 // takes the implicit list [t_begin, t_end) for both blocks (all shared), in
-// the same three phases.
+// the same three phases; with split key ranges, a block without a partner
+// (odd block count) has both wave pairs serve its rows over the two halves
+// of the range (paired entries) and merges their results at the end.
 //
 // Data movement.  K and V half tiles go from HBM/L2 straight to LDS with
 // buffer_load ... lds in the one-block kernel's tile layout (a slot is the
@@ -367,6 +369,12 @@ void attn_pair_kernel(PairParams p) {
   const int b = bh / p.H;
   const int qbiA = 2 * pi;
   const bool hasB = qbiA + 1 < p.nqb;
+  // Dense rows split over key ranges, a block without a partner (odd block
+  // count): both wave pairs serve its rows, over the two halves of the
+  // split's key range, and merge at the end, instead of waves 2-3 idling.
+  // (Unsplit, the dense rows keep the sparse path's tile order, and with it
+  // its bits at ratio 1.)
+  const bool self_wg = kDense && !hasB && p.nsplit > 1;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -379,9 +387,9 @@ void attn_pair_kernel(PairParams p) {
   const int64_t rs = (int64_t)p.H * kHeadDim;   // elements per token
   const int row_bytes = p.H * kHeadDim * 2;
   const int64_t bbase = (int64_t)b * T * rs;
-  const int qbi = qbiA + blk;
+  const int qbi = self_wg ? qbiA : qbiA + blk;
   const int qb = p.qb0 + qbi;
-  const bool active = blk == 0 || hasB;          // a missing block B computes nothing it keeps
+  const bool active = blk == 0 || hasB || self_wg;   // a missing block B computes nothing it keeps
   const int tq = qb * kBlock + rw * 32 + c32;    // this lane's query row
 
   // The lists go first: wave 0 reads A's count and first 64 entries, wave 1
@@ -449,24 +457,48 @@ void attn_pair_kernel(PairParams p) {
   const bool has_bias = p.key_bias != nullptr;
   const int nbfull = (T % kBlock) != 0 ? p.nb - 1 : p.nb;   // blocks of 64 keys
   int nU, nBi, nE;
-  int d_t0 = 0, d_nub = 0;
+  int d_t0 = 0, d_nub = 0, d_lenA = 0, d_lenB = 0;
   const int2 *sch = reinterpret_cast<const int2 *>(smem + kPSchOff);
   if (kDense) {
     const int t_begin = split * p.tiles_per_split;
     int t_end = t_begin + p.tiles_per_split;
     t_end = t_end < p.nb ? t_end : p.nb;
-    const int ub_end = t_end < nbfull ? t_end : nbfull;
-    const int nub = ub_end > t_begin ? ub_end - t_begin : 0;
-    int nu = nub;
-    if (has_bias) {
-      nu = p.nvb - t_begin;
-      nu = nu < 0 ? 0 : (nu > nub ? nub : nu);
-    }
-    nU = nu;
-    nBi = nub - nu;
-    nE = nub + ((nbfull < p.nb && p.nb - 1 >= t_begin && p.nb - 1 < t_end) ? 1 : 0);
     d_t0 = t_begin;
-    d_nub = nub;
+    if (self_wg) {
+      // entry e: key block t_begin + e for waves 0-1 (e < lenA) and t_begin
+      // + lenA + e for waves 2-3 (e < lenB); the partial last block and a
+      // missing second tile are general entries, and with the blocks in
+      // ascending order they come last
+      const int n = t_end > t_begin ? t_end - t_begin : 0;
+      d_lenA = (n + 1) / 2;
+      d_lenB = n - d_lenA;
+      const bool part = nbfull < p.nb && p.nb - 1 >= t_begin && p.nb - 1 < t_end;
+      // general entries: lenB-1 when the second tile is the partial block,
+      // lenA-1 (= lenB) when there is no second tile; a one-block range that
+      // is the partial block is only the latter
+      const int ng = (part && d_lenB > 0 ? 1 : 0) + (d_lenA > d_lenB ? 1 : 0);
+      const int nfull = d_lenA - ng;   // entries with two complete tiles
+      int nu = nfull;
+      if (has_bias) {   // biased once the second tile is a sink block
+        nu = p.nvb - t_begin - d_lenA;
+        nu = nu < 0 ? 0 : (nu > nfull ? nfull : nu);
+      }
+      nU = nu;
+      nBi = nfull - nu;
+      nE = d_lenA;
+    } else {
+      const int ub_end = t_end < nbfull ? t_end : nbfull;
+      const int nub = ub_end > t_begin ? ub_end - t_begin : 0;
+      int nu = nub;
+      if (has_bias) {
+        nu = p.nvb - t_begin;
+        nu = nu < 0 ? 0 : (nu > nub ? nub : nu);
+      }
+      nU = nu;
+      nBi = nub - nu;
+      nE = nub + ((nbfull < p.nb && p.nb - 1 >= t_begin && p.nb - 1 < t_end) ? 1 : 0);
+      d_nub = nub;
+    }
     read_q();
     __syncthreads();
   } else {
@@ -580,7 +612,12 @@ void attn_pair_kernel(PairParams p) {
   }
   auto entry = [&](int e, int &a, int &bb) {
     if (kDense) {
-      a = bb = (e < d_nub ? d_t0 + e : p.nb - 1) * kBlock;
+      if (self_wg) {
+        a = (d_t0 + e) * kBlock;
+        bb = e < d_lenB ? (d_t0 + d_lenA + e) * kBlock : T;
+      } else {
+        a = bb = (e < d_nub ? d_t0 + e : p.nb - 1) * kBlock;
+      }
       return;
     }
     if (e - ch_cb >= 64) {
@@ -969,6 +1006,39 @@ void attn_pair_kernel(PairParams p) {
 
   // ---- epilogue -----------------------------------------------------------
   if (!active) return;
+  if (self_wg) {
+    // waves 2-3 hand (max, row-sum share, O) of the second key half to waves
+    // 0-1, which own the same rows in the same lane layout: O in the K ring
+    // (no longer read: the last step computes no S), 16 KiB per wave as
+    // [value][lane], max and sum in the schedule area, unused by the dense
+    // rows
+    float *xo = reinterpret_cast<float *>(smem + kPKOff) + rw * (64 * 64);
+    float *xm = reinterpret_cast<float *>(smem + kPSchOff) + rw * 128;
+    if (blk == 1) {
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xo[(16 * dt + r) * 64 + lane] = o[dt][r];
+      xm[lane] = m_used;
+      xm[64 + lane] = l_run;
+    }
+    __syncthreads();
+    if (blk == 0) {
+      const float mB = xm[lane], lB = xm[64 + lane];
+      const float mN = fmaxf(m_used, mB);
+      const float aA = m_used == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_used - mN);
+      const float aB = mB == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mB - mN);
+      l_run = l_run * aA + lB * aB;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[dt][r] = o[dt][r] * aA + xo[(16 * dt + r) * 64 + lane] * aB;
+      m_used = mN;
+    }
+    // the output staging below reuses the K ring
+    __syncthreads();
+    if (blk == 1) return;
+  }
   const float l_tot = add_with_partner(l_run);
   if (kDense && p.nsplit > 1) {
     if (tq >= T) return;
