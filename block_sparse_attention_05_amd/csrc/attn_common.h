@@ -27,6 +27,7 @@ constexpr int kThreads = 256;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.0f;       // log2 units
+constexpr float kPMax = 4294967296.0f;      // 2^32: largest P a full tile may use before it rescales
 constexpr int kBufferFlags = 0x00020000;    // raw buffer, 32-bit data format
 constexpr int kVmcntZero = 0x0F70;          // s_waitcnt vmcnt(0), other counters untouched
 // sched_group_barrier instruction classes

@@ -61,13 +61,15 @@
 // its own rows).
 //
 // Math per step and wave (32 rows x 32 keys): S^T = K Q^T on
-// v_mfma_f32_32x32x16_bf16, online softmax in base 2 with lazy rescaling
-// (slack 8), P rounded to bf16, O^T += V^T P^T with V^T from
-// ds_read_b64_tr_b16.  A full-tile step issues its copies, takes the tile
-// max and the rare rescale, then runs one straight block in a fixed order:
-// each of the eight S(j+1) MFMAs is followed by the exponentials of two of
-// the lane's logits of tile j, so that the wave's matrix and vector work
-// overlap, and the eight PV MFMAs close the step.  The same arithmetic as
+// v_mfma_f32_32x32x16_bf16, online softmax in base 2, P rounded to bf16,
+// O^T += V^T P^T with V^T from ds_read_b64_tr_b16.  A full-tile step issues
+// its copies, then runs one straight block in a fixed order: each of the
+// eight S(j+1) MFMAs is followed by the exponentials of two of the lane's
+// logits of tile j, taken against the running max as it stands (no tile
+// max), so that the wave's matrix and vector work overlap; a tile whose P
+// would exceed 2^32 (rare) moves the running max and is taken again, and
+// the eight PV MFMAs close the step.  Masked steps take the tile max first
+// and move the running max when it grows by more than 8.  The same arithmetic as
 // the one-block kernel, with the keys of a 64-key tile accumulated in two
 // sequential steps instead of two waves.
 #include <atomic>
@@ -802,8 +804,9 @@ void attn_pair_kernel(PairParams p) {
       }
     };
     bf16x8 pf[2];
-    // P of keys 16*h .. +15 of this lane's 32 (q4 = 2h, 2h+1) into pf[h]
-    auto exps_half = [&](float m_sub, auto h_c) {
+    // P of keys 16*h .. +15 of this lane's 32 (q4 = 2h, 2h+1) into pf[h],
+    // their sum added to acc
+    auto exps_half = [&](float m_sub, auto h_c, float &acc) {
       constexpr int H0 = 2 * decltype(h_c)::value;
 #pragma unroll
       for (int q4 = H0; q4 < H0 + 2; ++q4) {
@@ -829,12 +832,12 @@ void attn_pair_kernel(PairParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const bf16x2 two = {pf[H0 >> 1][2 * i], pf[H0 >> 1][2 * i + 1]};
-        l_run = __builtin_amdgcn_fdot2_f32_bf16(two, ones, l_run, false);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(two, ones, acc, false);
       }
     };
-    auto exps = [&](float m_sub) {
-      exps_half(m_sub, Int<0>{});
-      exps_half(m_sub, Int<1>{});
+    auto exps = [&](float m_sub, float &acc) {
+      exps_half(m_sub, Int<0>{}, acc);
+      exps_half(m_sub, Int<1>{}, acc);
     };
     // O^T += V^T P^T over the half tile's 32 keys
     auto pv = [&]() {
@@ -856,23 +859,25 @@ void attn_pair_kernel(PairParams p) {
       for (int r = 0; r < 16; ++r)
         if (kbase + 8 * (r >> 2) + (r & 3) >= T) s_cur[r] = -INFINITY;
       rescale(tile_max());
-      exps(m_used == -INFINITY ? 0.f : m_used);
+      exps(m_used == -INFINITY ? 0.f : m_used, l_run);
       pv();
       return;
     }
 
-    // Full tiles.  Copies, the max of tile j and the rare rescale come
-    // first; all of them may branch.  Then one straight block in a fixed
-    // order (sched_barrier fences keep the scheduler from regrouping it):
-    // the K fragments of S(j+1) are read at once, every S(j+1) MFMA is
-    // followed by the exponentials of two of this lane's logits (so that
-    // the matrix and vector units of the wave work side by side), the V
-    // fragments are read half way, and the PV MFMAs end the step.  Every
-    // sum runs in the same order as in the general step above.
+    // Full tiles.  P is taken against the running max as it stands, with no
+    // tile max: the copies come first, then one straight block in a fixed
+    // order (sched_barrier fences keep the scheduler from regrouping it): the
+    // K fragments of S(j+1) are read at once, every S(j+1) MFMA is followed
+    // by the exponentials of two of this lane's logits (so that the matrix
+    // and vector units of the wave work side by side), the V fragments are
+    // read half way.  A P above 2^32 (the running max stale by more than 32,
+    // or not yet set: every P is then +inf) shows in the tile's sum; then,
+    // rarely, the tile max moves the running max, O and the row sum are
+    // rescaled and the tile's P are taken again, so that every P fed to the
+    // PV MFMAs that end the step is at most 2^32: far from fp32 and bf16
+    // overflow, and no loss of relative precision.
     dma_k();
     dma_v();
-    rescale(tile_max());
-    const float m_sub = (m_used == -INFINITY) ? 0.f : m_used;
     __builtin_amdgcn_s_setprio(1);
     bf16x8 kf[8];
     if (DO_QK) {
@@ -881,6 +886,7 @@ void attn_pair_kernel(PairParams p) {
     }
     bf16x8 vf[4], vg[4];
     float4 bq = make_float4(0.f, 0.f, 0.f, 0.f);
+    float l_t = 0.f;   // this lane's share of the tile's row sum
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -896,16 +902,16 @@ void attn_pair_kernel(PairParams p) {
       if (BIASED && (i & 1) == 0) bq = bias4(i >> 1);
       float e0, e1;
       if (BIASED) {
-        e0 = __builtin_fmaf(s_cur[r], c, ((i & 1) ? bq.z : bq.x) - m_sub);
-        e1 = __builtin_fmaf(s_cur[r + 1], c, ((i & 1) ? bq.w : bq.y) - m_sub);
+        e0 = __builtin_fmaf(s_cur[r], c, ((i & 1) ? bq.z : bq.x) - m_used);
+        e1 = __builtin_fmaf(s_cur[r + 1], c, ((i & 1) ? bq.w : bq.y) - m_used);
       } else {
-        e0 = __builtin_fmaf(s_cur[r], c, -m_sub);
-        e1 = __builtin_fmaf(s_cur[r + 1], c, -m_sub);
+        e0 = __builtin_fmaf(s_cur[r], c, -m_used);
+        e1 = __builtin_fmaf(s_cur[r + 1], c, -m_used);
       }
       pf[r >> 3][r & 7] = (__bf16)__builtin_amdgcn_exp2f(e0);
       pf[r >> 3][(r & 7) + 1] = (__bf16)__builtin_amdgcn_exp2f(e1);
       const bf16x2 two = {pf[r >> 3][r & 7], pf[r >> 3][(r & 7) + 1]};
-      l_run = __builtin_amdgcn_fdot2_f32_bf16(two, ones, l_run, false);
+      l_t = __builtin_amdgcn_fdot2_f32_bf16(two, ones, l_t, false);
       // V fragments of keys 0-15 and 16-31, read while the S(j+1) MFMAs
       // run (late enough that few K fragments are still held)
       if (i == 3) {
@@ -918,6 +924,22 @@ void attn_pair_kernel(PairParams p) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    // a sum of non-negative terms is at least its largest term; NaN (from
+    // an infinite logit meeting an infinite max) fails the test too
+    if (__any(!(l_t <= kPMax))) {
+      const float mt = tile_max();
+      const float m_new = fmaxf(m_used, mt);
+      const float alpha = m_new > m_used ? __builtin_amdgcn_exp2f(m_used - m_new) : 1.f;  // 0 from -inf
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+      m_used = m_new;
+      l_t = 0.f;
+      exps(m_used == -INFINITY ? 0.f : m_used, l_t);
+    }
+    l_run += l_t;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[dt], pf[0], o[dt], 0, 0, 0);
 #pragma unroll
