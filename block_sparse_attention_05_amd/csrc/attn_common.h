@@ -62,6 +62,17 @@ __device__ __forceinline__ void lds_dma_b128(const i32x4s &rsrc, uint32_t voffse
                : "v"(voffset), "s"(rsrc), "s"(lds_base), "i"(kOff)
                : "memory", "m0", "scc");
 }
+// The same copy with an immediate offset kImm (< 4096) on the global address:
+// the immediate also moves the LDS address, so M0 takes it off again.  The
+// copy lands at lds_base + kOff and reads voffset + kImm.
+template <int kOff, int kImm>
+__device__ __forceinline__ void lds_dma_b128_imm(const i32x4s &rsrc, uint32_t voffset, uint32_t lds_base) {
+  static_assert(kImm >= 0 && kImm < 4096 && kOff >= kImm, "immediate offset out of range");
+  asm volatile("s_add_u32 m0, %2, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen offset:%4 lds"
+               :
+               : "v"(voffset), "s"(rsrc), "s"(lds_base), "i"(kOff - kImm), "i"(kImm)
+               : "memory", "m0", "scc");
+}
 __device__ __forceinline__ void lds_dma_b32(const i32x4s &rsrc, uint32_t voffset, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
                :

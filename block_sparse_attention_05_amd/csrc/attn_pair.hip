@@ -633,13 +633,10 @@ void attn_pair_kernel(PairParams p) {
     a = __builtin_amdgcn_readlane(ch_a, e - ch_cb);
     bb = __builtin_amdgcn_readlane(ch_b, e - ch_cb);
   };
-  // First key of half tile `half` of the tile whose first key is k0; T (no
-  // tile) for a missing block (k0 = T) or a half that lies past T.
-  auto hkey = [&](int k0, int half) -> int {
-    if (half == 0) return k0;
-    const int k1 = k0 + 32;
-    return k1 < T ? k1 : T;
-  };
+  // First key of half tile `half` of the tile whose first key is k0.  A key
+  // at or past T means no tile: a missing block (k0 = T) or a half that lies
+  // past T; every user below tests ">= T".
+  auto hkey = [&](int k0, int half) -> int { return half == 0 ? k0 : k0 + 32; };
 
   // ---- loads --------------------------------------------------------------
   const i32x4s rk = buffer_rsrc(p.k + bbase, slab);
@@ -647,59 +644,47 @@ void attn_pair_kernel(PairParams p) {
   const float *kbias = has_bias ? p.key_bias + (int64_t)b * T : nullptr;
   const i32x4s rb = buffer_rsrc(kbias ? (const void *)kbias : (const void *)p.k, kbias ? T * 4u : 0u);
   const int sink0 = p.nvb * kBlock;
-  const uint32_t rows8 = (uint32_t)(8 * row_bytes);
   // LDS tile layout: the one-block kernel's.  A 64-key slot is 16 blocks of
   // 1 KiB; block 2*kg + hf holds keys 8*kg .. +7 (kg = 0..7) and bytes
   // 128*hf .. +127 of each key row, in 16-byte pieces (key k' = key%8, chunk
   // c = 0..7) placed with an XOR swizzle:
   //   K: piece (k', c) at 128*k' + 16*(c ^ k' ^ (kg & 1));
   //   V: piece (k', c) at 128*k' + 16*(c ^ 2*(k' & 3)).
-  // Key groups 0-3 hold A's half tile (or the shared one), 4-7 B's.  A
-  // paired step has wave w fetch key groups 2w, 2w+1 (keys 16*(w&1) .. +15
-  // of its block's half tile); a shared step has wave w fetch key group w.
+  // Key groups 0-3 hold A's half tile (or the shared one), 4-7 B's.  Wave w
+  // fetches key group w of A's half tile and, in a paired step, key group w
+  // of B's (keys 8w .. 8w+7 of each), so every wave issues the same copies
+  // whatever the step holds; the second 128 bytes of each key row come from
+  // the same lane offset through the instruction's immediate offset.
   const uint32_t chk = (uint32_t)((lane & 7) ^ (lane >> 3));
-  const uint32_t row_lane = (uint32_t)(lane >> 3) * (uint32_t)row_bytes + (uint32_t)h * 256u;
-  const uint32_t k_lane_p = row_lane + 16u * chk;
-  const uint32_t k_lane_s = row_lane + 16u * (chk ^ (uint32_t)(wave & 1));
+  const uint32_t row_lane = (uint32_t)(lane >> 3) * (uint32_t)row_bytes + (uint32_t)h * 256u +
+                            (uint32_t)(8 * wave) * (uint32_t)row_bytes;
+  const uint32_t k_lane = row_lane + 16u * (chk ^ (uint32_t)(wave & 1));
   const uint32_t v_lane = row_lane + 16u * (uint32_t)((lane & 7) ^ (2 * ((lane >> 3) & 3)));
+  const uint32_t lds_w = lds0 + 2048u * (uint32_t)wave;
   auto issue_k = [&](int kA, int kB, int slot) {
-    const uint32_t lb = lds0 + kPKOff + (uint32_t)(slot * 16384);
-    if (kA != kB) {
-      const int kk = wave < 2 ? kA : kB;
-      if (kk >= T) return;
-      const uint32_t base = (uint32_t)(kk + 16 * (wave & 1)) * (uint32_t)row_bytes + k_lane_p;
-      const uint32_t l = lb + 4096u * (uint32_t)wave;
+    const uint32_t l = lds_w + kPKOff + (uint32_t)(slot * 16384);
+    if (kA < T) {
+      const uint32_t base = (uint32_t)kA * (uint32_t)row_bytes + k_lane;
       lds_dma_b128<0>(rk, base, l);
-      lds_dma_b128<1024>(rk, base + 128, l);
-      // odd key group: chunk parity flipped (the chunk term is the only part
-      // of the offset below 256)
-      lds_dma_b128<2048>(rk, (base ^ 16u) + rows8, l);
-      lds_dma_b128<3072>(rk, (base ^ 16u) + rows8 + 128, l);
-    } else {
-      if (kA >= T) return;
-      const uint32_t base = (uint32_t)(kA + 8 * wave) * (uint32_t)row_bytes + k_lane_s;
-      const uint32_t l = lb + 2048u * (uint32_t)wave;
-      lds_dma_b128<0>(rk, base, l);
-      lds_dma_b128<1024>(rk, base + 128, l);
+      lds_dma_b128_imm<1024, 128>(rk, base, l);
+    }
+    if (kB != kA && kB < T) {
+      const uint32_t base = (uint32_t)kB * (uint32_t)row_bytes + k_lane;
+      lds_dma_b128<8192>(rk, base, l);
+      lds_dma_b128_imm<9216, 128>(rk, base, l);
     }
   };
   auto issue_v = [&](int kA, int kB, int slot, bool with_bias) {
-    const uint32_t lb = lds0 + kPVOff + (uint32_t)(slot * 16384);
-    if (kA != kB) {
-      const int kk = wave < 2 ? kA : kB;
-      if (kk < T) {
-        const uint32_t base = (uint32_t)(kk + 16 * (wave & 1)) * (uint32_t)row_bytes + v_lane;
-        const uint32_t l = lb + 4096u * (uint32_t)wave;
-        lds_dma_b128<0>(rv, base, l);
-        lds_dma_b128<1024>(rv, base + 128, l);
-        lds_dma_b128<2048>(rv, base + rows8, l);
-        lds_dma_b128<3072>(rv, base + rows8 + 128, l);
-      }
-    } else if (kA < T) {
-      const uint32_t base = (uint32_t)(kA + 8 * wave) * (uint32_t)row_bytes + v_lane;
-      const uint32_t l = lb + 2048u * (uint32_t)wave;
+    const uint32_t l = lds_w + kPVOff + (uint32_t)(slot * 16384);
+    if (kA < T) {
+      const uint32_t base = (uint32_t)kA * (uint32_t)row_bytes + v_lane;
       lds_dma_b128<0>(rv, base, l);
-      lds_dma_b128<1024>(rv, base + 128, l);
+      lds_dma_b128_imm<1024, 128>(rv, base, l);
+    }
+    if (kB != kA && kB < T) {
+      const uint32_t base = (uint32_t)kB * (uint32_t)row_bytes + v_lane;
+      lds_dma_b128<8192>(rv, base, l);
+      lds_dma_b128_imm<9216, 128>(rv, base, l);
     }
     // natural-log bias of both half tiles (lanes 0-31: A's keys, 32-63:
     // B's); keys of non-sink blocks and past T read as zero
@@ -734,7 +719,8 @@ void attn_pair_kernel(PairParams p) {
 
   // Half of a slot this wave reads in a step with tiles (kA, kB): its own
   // block's half when the entry is paired, else the first half.
-  auto rhalf = [&](int kA, int kB) -> uint32_t { return (blk != 0 && kA != kB) ? 8192u : 0u; };
+  const uint32_t blk_half = blk != 0 ? 8192u : 0u;
+  auto rhalf = [&](int kA, int kB) -> uint32_t { return kA != kB ? blk_half : 0u; };
 
   // One pipeline step on half tile j (scores in s_cur, V in slot VS, this
   // wave's first key my_key, read half rh) that also computes S(j+1) into
