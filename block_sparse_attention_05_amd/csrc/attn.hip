@@ -38,9 +38,10 @@
 //     fragments resident in registers.  Each lane then owns one query row and
 //     16 keys, so the row reductions are in-lane plus one v_permlane32_swap;
 //   * online softmax in base 2 (scale * log2 e folded into one FMA) with lazy
-//     rescaling: the running max moves only when a row's max grows by more
-//     than 8 (P <= 2^8), the row sum accumulates the bf16-rounded P with
-//     v_dot2;
+//     rescaling: a full tile takes P against the running max as it stands
+//     and moves it only when a P would exceed 2^32 (no tile max); a masked
+//     tile moves it when the tile max grows by more than 8; the row sum
+//     accumulates the bf16-rounded P with v_dot2;
 //   * O^T += V^T P^T: P^T fragments come straight from the S^T registers, V^T
 //     fragments from the row-major V tile through ds_read_b64_tr_b16 (each
 //     16-lane group reads a 4-row block, lane c receives column c).  Keys in a
@@ -451,75 +452,93 @@ void attn_fwd_kernel(Params p) {
       const float4 b4 = *reinterpret_cast<const float4 *>(bs + 32 * kh + 8 * q4 + 4 * g);
       return make_float4(b4.x * kLog2e, b4.y * kLog2e, b4.z * kLog2e, b4.w * kLog2e);
     };
-    float mt;  // tile max of this lane's logits, log2 units
-    if (BIASED) {
-      mt = -INFINITY;
+    // tile max of this lane's logits (log2 units), shared with the lane that
+    // holds the other 16 keys of the row
+    auto tile_max = [&]() -> float {
+      float mt;
+      if (BIASED) {
+        mt = -INFINITY;
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const float4 bq = bias4(q4);
-        mt = fmaxf(mt, __builtin_fmaf(s_cur[4 * q4 + 0], c, bq.x));
-        mt = fmaxf(mt, __builtin_fmaf(s_cur[4 * q4 + 1], c, bq.y));
-        mt = fmaxf(mt, __builtin_fmaf(s_cur[4 * q4 + 2], c, bq.z));
-        mt = fmaxf(mt, __builtin_fmaf(s_cur[4 * q4 + 3], c, bq.w));
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const float4 bq = bias4(q4);
+          mt = fmaxf(mt, __builtin_fmaf(s_cur[4 * q4 + 0], c, bq.x));
+          mt = fmaxf(mt, __builtin_fmaf(s_cur[4 * q4 + 1], c, bq.y));
+          mt = fmaxf(mt, __builtin_fmaf(s_cur[4 * q4 + 2], c, bq.z));
+          mt = fmaxf(mt, __builtin_fmaf(s_cur[4 * q4 + 3], c, bq.w));
+        }
+      } else {
+        float mx = s_cur[0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s_cur[r]);
+        mt = mx * c;
       }
-    } else {
-      float mx = s_cur[0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s_cur[r]);
-      mt = mx * c;
-    }
-    mt = max_with_partner(mt);
-    if (DO_QK) {
-      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 3, 0);
-#pragma unroll
-      for (int i = 0; i < 3; ++i) {
-        __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedVALU, 4, 0);
-      }
-    }
-
-    // -- rare: a row max grew past the slack: rescale --
-    if (__any(mt > m_used + kRescaleSlack)) {
-      const float m_new = fmaxf(m_used, mt);
-      const float alpha = __builtin_amdgcn_exp2f(m_used - m_new);  // 0 when m_used = -inf
+      return max_with_partner(mt);
+    };
+    auto rescale_to = [&](float m_new) {
+      const float alpha = m_new > m_used ? __builtin_amdgcn_exp2f(m_used - m_new) : 1.f;  // 0 from -inf
       l_run *= alpha;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
       m_used = m_new;
+    };
+    // P of tile j against m_sub into pf, their sum added to acc
+    bf16x8 pf[2];
+    auto exps = [&](float m_sub, float &acc) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        float e[4];
+        if (BIASED) {
+          const float4 bq = bias4(q4);
+          e[0] = __builtin_fmaf(s_cur[4 * q4 + 0], c, bq.x - m_sub);
+          e[1] = __builtin_fmaf(s_cur[4 * q4 + 1], c, bq.y - m_sub);
+          e[2] = __builtin_fmaf(s_cur[4 * q4 + 2], c, bq.z - m_sub);
+          e[3] = __builtin_fmaf(s_cur[4 * q4 + 3], c, bq.w - m_sub);
+        } else {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) e[u] = __builtin_fmaf(s_cur[4 * q4 + u], c, -m_sub);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; u += 2) {
+          const int r = 4 * q4 + u;
+          const bf16x2 pk = {(__bf16)__builtin_amdgcn_exp2f(e[u]), (__bf16)__builtin_amdgcn_exp2f(e[u + 1])};
+          acc = __builtin_amdgcn_fdot2_f32_bf16(pk, ones, acc, false);
+          pf[r >> 3][r & 7] = pk[0];
+          pf[r >> 3][(r & 7) + 1] = pk[1];
+        }
+      }
+    };
+    float m_sub = m_used;
+    if (MASKED) {
+      // masked tiles: the tile max first, the running max moved when it
+      // grows by more than the slack
+      const float mt = tile_max();
+      if (DO_QK) {
+        __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 3, 0);
+#pragma unroll
+        for (int i = 0; i < 3; ++i) {
+          __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(kSchedVALU, 4, 0);
+        }
+      }
+      if (__any(mt > m_used + kRescaleSlack)) rescale_to(fmaxf(m_used, mt));
+      m_sub = (m_used == -INFINITY) ? 0.f : m_used;
     }
-    const float m_sub = (m_used == -INFINITY) ? 0.f : m_used;
 
     // -- block B: P of tile j (+ remaining S(j+1) MFMAs) --
+    // Full tiles take P against the running max as it stands (no tile max);
+    // a P above 2^32 (the running max stale by more than 32, or not yet set:
+    // P = +inf) shows in the tile's sum, and then, rarely, the tile max moves
+    // the running max and the tile's P are taken again.
     // The exponential and PV phases run at raised wave priority: when the
     // other workgroup's wave on this SIMD is in its max phase, issuing copies
     // or waiting at its barrier, this wave's VALU and MFMA work goes first.
     __builtin_amdgcn_s_setprio(1);
     if (DO_QK) qk_part(Int<3>{}, Int<8>{});
-    bf16x8 pf[2];
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      float e[4];
-      if (BIASED) {
-        const float4 bq = bias4(q4);
-        e[0] = __builtin_fmaf(s_cur[4 * q4 + 0], c, bq.x - m_sub);
-        e[1] = __builtin_fmaf(s_cur[4 * q4 + 1], c, bq.y - m_sub);
-        e[2] = __builtin_fmaf(s_cur[4 * q4 + 2], c, bq.z - m_sub);
-        e[3] = __builtin_fmaf(s_cur[4 * q4 + 3], c, bq.w - m_sub);
-      } else {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) e[u] = __builtin_fmaf(s_cur[4 * q4 + u], c, -m_sub);
-      }
-#pragma unroll
-      for (int u = 0; u < 4; u += 2) {
-        const int r = 4 * q4 + u;
-        const bf16x2 pk = {(__bf16)__builtin_amdgcn_exp2f(e[u]), (__bf16)__builtin_amdgcn_exp2f(e[u + 1])};
-        l_run = __builtin_amdgcn_fdot2_f32_bf16(pk, ones, l_run, false);
-        pf[r >> 3][r & 7] = pk[0];
-        pf[r >> 3][(r & 7) + 1] = pk[1];
-      }
-    }
+    float l_t = 0.f;   // full tiles: this lane's share of the tile's row sum
+    if (MASKED) exps(m_sub, l_run);
+    else exps(m_used, l_t);
     if (DO_QK) {
       __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 2, 0);
 #pragma unroll
@@ -533,6 +552,16 @@ void attn_fwd_kernel(Params p) {
         __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
         __builtin_amdgcn_sched_group_barrier(kSchedVALU, 8, 0);
       }
+    }
+    if (!MASKED) {
+      // a sum of non-negative terms is at least its largest term; NaN (an
+      // infinite logit meeting an infinite max) fails the test too
+      if (__any(!(l_t <= kPMax))) {
+        rescale_to(fmaxf(m_used, tile_max()));
+        l_t = 0.f;
+        exps(m_used == -INFINITY ? 0.f : m_used, l_t);
+      }
+      l_run += l_t;
     }
 
     // -- block C: O^T += V^T P^T over this wave's 32 keys --
