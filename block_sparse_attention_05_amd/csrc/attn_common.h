@@ -73,6 +73,28 @@ __device__ __forceinline__ void lds_dma_b128_imm(const i32x4s &rsrc, uint32_t vo
                : "v"(voffset), "s"(rsrc), "s"(lds_base), "i"(kOff - kImm), "i"(kImm)
                : "memory", "m0", "scc");
 }
+// Both 128-byte halves of 8 key rows: LDS lds_base + kOff gets the bytes at
+// sbase + vlane (one 16-byte piece per lane), lds_base + kOff + 1024 those
+// 128 bytes further on (through the immediate offset, which moves the LDS
+// address too, so M0 takes it off).  The lane address is formed inside the
+// block, where it also serves as the wait state the first M0 write needs;
+// the second has an s_nop.  The address register is read when each load
+// issues and is free afterwards.
+template <int kOff>
+__device__ __forceinline__ void lds_dma_b128_x2(const i32x4s &rsrc, uint32_t sbase, uint32_t vlane,
+                                                uint32_t lds_base) {
+  uint32_t t;
+  asm volatile(
+      "s_add_u32 m0, %3, %4\n\t"
+      "v_add_u32 %0, %2, %1\n\t"
+      "buffer_load_dwordx4 %0, %5, 0 offen lds\n\t"
+      "s_add_u32 m0, %3, %6\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %0, %5, 0 offen offset:128 lds"
+      : "=&v"(t)
+      : "v"(vlane), "s"(sbase), "s"(lds_base), "i"(kOff), "s"(rsrc), "i"(kOff + 1024 - 128)
+      : "memory", "m0", "scc");
+}
 __device__ __forceinline__ void lds_dma_b32(const i32x4s &rsrc, uint32_t voffset, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
                :

@@ -639,6 +639,8 @@ void attn_pair_kernel(PairParams p) {
   auto hkey = [&](int k0, int half) -> int { return half == 0 ? k0 : k0 + 32; };
 
   // ---- loads --------------------------------------------------------------
+  // entries from this index on carry key_bias on their sink tiles
+  const int bias_from = has_bias ? nU : 0x7fffffff;
   const i32x4s rk = buffer_rsrc(p.k + bbase, slab);
   const i32x4s rv = buffer_rsrc(p.v + bbase, slab);
   const float *kbias = has_bias ? p.key_bias + (int64_t)b * T : nullptr;
@@ -661,34 +663,23 @@ void attn_pair_kernel(PairParams p) {
   const uint32_t k_lane = row_lane + 16u * (chk ^ (uint32_t)(wave & 1));
   const uint32_t v_lane = row_lane + 16u * (uint32_t)((lane & 7) ^ (2 * ((lane >> 3) & 3)));
   const uint32_t lds_w = lds0 + 2048u * (uint32_t)wave;
+  // (B's tile is copied when it is its own: kB != kA)
   auto issue_k = [&](int kA, int kB, int slot) {
     const uint32_t l = lds_w + kPKOff + (uint32_t)(slot * 16384);
-    if (kA < T) {
-      const uint32_t base = (uint32_t)kA * (uint32_t)row_bytes + k_lane;
-      lds_dma_b128<0>(rk, base, l);
-      lds_dma_b128_imm<1024, 128>(rk, base, l);
-    }
-    if (kB != kA && kB < T) {
-      const uint32_t base = (uint32_t)kB * (uint32_t)row_bytes + k_lane;
-      lds_dma_b128<8192>(rk, base, l);
-      lds_dma_b128_imm<9216, 128>(rk, base, l);
-    }
+    const int kb = kB == kA ? T : kB;
+    if (kA < T) lds_dma_b128_x2<0>(rk, (uint32_t)kA * (uint32_t)row_bytes, k_lane, l);
+    if (kb < T) lds_dma_b128_x2<8192>(rk, (uint32_t)kb * (uint32_t)row_bytes, k_lane, l);
   };
-  auto issue_v = [&](int kA, int kB, int slot, bool with_bias) {
+  // e_tile: the entry index of the tile; its bias is loaded when e_tile >=
+  // bias_from (the biased and general phases with key_bias)
+  auto issue_v = [&](int kA, int kB, int slot, int e_tile) {
     const uint32_t l = lds_w + kPVOff + (uint32_t)(slot * 16384);
-    if (kA < T) {
-      const uint32_t base = (uint32_t)kA * (uint32_t)row_bytes + v_lane;
-      lds_dma_b128<0>(rv, base, l);
-      lds_dma_b128_imm<1024, 128>(rv, base, l);
-    }
-    if (kB != kA && kB < T) {
-      const uint32_t base = (uint32_t)kB * (uint32_t)row_bytes + v_lane;
-      lds_dma_b128<8192>(rv, base, l);
-      lds_dma_b128_imm<9216, 128>(rv, base, l);
-    }
+    const int kb = kB == kA ? T : kB;
+    if (kA < T) lds_dma_b128_x2<0>(rv, (uint32_t)kA * (uint32_t)row_bytes, v_lane, l);
+    if (kb < T) lds_dma_b128_x2<8192>(rv, (uint32_t)kb * (uint32_t)row_bytes, v_lane, l);
     // natural-log bias of both half tiles (lanes 0-31: A's keys, 32-63:
     // B's); keys of non-sink blocks and past T read as zero
-    if (with_bias && wave == 0) {
+    if (e_tile >= bias_from && wave == 0) {
       const int k0 = lane < 32 ? kA : kB;
       const int key = k0 + (lane & 31);
       const bool sink = k0 >= sink0 && key < T;
@@ -943,7 +934,7 @@ void attn_pair_kernel(PairParams p) {
   if (nE > 1) entry(1, na, nb2);
   if (nE > 0) {
     issue_k(hkey(ea, 0), hkey(eb, 0), 0);
-    issue_v(hkey(ea, 0), hkey(eb, 0), 0, has_bias && nU == 0);
+    issue_v(hkey(ea, 0), hkey(eb, 0), 0, 0);
     issue_k(hkey(ea, 1), hkey(eb, 1), 1);
   }
   __builtin_amdgcn_s_waitcnt(kVmcntZero);
@@ -967,16 +958,14 @@ void attn_pair_kernel(PairParams p) {
   auto run_entry = [&](auto biased_c, auto masked_c, int e) {
     const int a0 = hkey(ea, 0), b0 = hkey(eb, 0), a1 = hkey(ea, 1), b1 = hkey(eb, 1);
     const int n0a = hkey(na, 0), n0b = hkey(nb2, 0), n1a = hkey(na, 1), n1b = hkey(nb2, 1);
-    const bool nbias = has_bias && e + 1 >= nU;
-    const bool cbias = has_bias && e >= nU;
     // half 0
     step(Int<0>{}, biased_c, masked_c, Bool<true>{}, s0, s1, blk ? b0 : a0, rhalf(a0, b0), rhalf(a1, b1),
-         [&] { issue_k(n0a, n0b, 0); }, [&] { issue_v(a1, b1, 1, cbias); });
+         [&] { issue_k(n0a, n0b, 0); }, [&] { issue_v(a1, b1, 1, e); });
     __builtin_amdgcn_s_waitcnt(kVmcntZero);
     __syncthreads();
     // half 1
     step(Int<1>{}, biased_c, masked_c, Bool<true>{}, s1, s0, blk ? b1 : a1, rhalf(a1, b1), rhalf(n0a, n0b),
-         [&] { issue_k(n1a, n1b, 1); }, [&] { issue_v(n0a, n0b, 0, nbias); });
+         [&] { issue_k(n1a, n1b, 1); }, [&] { issue_v(n0a, n0b, 0, e + 1); });
     __builtin_amdgcn_s_waitcnt(kVmcntZero);
     __syncthreads();
     ea = na;
@@ -986,9 +975,8 @@ void attn_pair_kernel(PairParams p) {
   // The last entry: half 0 computes S of half 1; half 1 ends the walk.
   auto last_entry = [&](auto biased_c, auto masked_c, int e) {
     const int a0 = hkey(ea, 0), b0 = hkey(eb, 0), a1 = hkey(ea, 1), b1 = hkey(eb, 1);
-    const bool cbias = has_bias && e >= nU;
     step(Int<0>{}, biased_c, masked_c, Bool<true>{}, s0, s1, blk ? b0 : a0, rhalf(a0, b0), rhalf(a1, b1),
-         [] {}, [&] { issue_v(a1, b1, 1, cbias); });
+         [] {}, [&] { issue_v(a1, b1, 1, e); });
     __builtin_amdgcn_s_waitcnt(kVmcntZero);
     __syncthreads();
     step(Int<1>{}, biased_c, masked_c, Bool<false>{}, s1, s0, blk ? b1 : a1, rhalf(a1, b1), 0u, [] {}, [] {});
