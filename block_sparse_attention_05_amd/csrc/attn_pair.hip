@@ -395,13 +395,21 @@ void attn_pair_kernel(PairParams p) {
   const int tq = qb * kBlock + rw * 32 + c32;    // this lane's query row
 
   // The lists go first: wave 0 reads A's count and first 64 entries, wave 1
-  // B's, all four loads in flight together ahead of the Q rows.
+  // B's, all in flight together ahead of the Q rows.  The count is a scalar
+  // load; the entries are copied into the bias ring (unused until the first
+  // tiles) by a global-to-LDS copy issued before the wave's eight Q copies,
+  // so that the wait for them (vmcnt(8): loads complete in order) does not
+  // also wait for Q, which then arrives while the schedule is built.
   const int64_t liA = (int64_t)bh * p.nqb + qbiA;
+  const bool list_wave = !kDense && !kFused && wave < 2 && (wave == 0 || hasB);
   int lcnt = 0, lfirst = -1;
-  if (!kDense && !kFused && wave < 2 && (wave == 0 || hasB)) {
+  if (list_wave) {
     const int64_t li = liA + wave;
     lcnt = p.block_cnt[li];
-    if (lane < p.max_sel) lfirst = p.block_idx[li * p.max_sel + lane];
+    // entries past max_sel read as zero; only the first lcnt are used
+    const i32x4s rl = buffer_rsrc(p.block_idx + li * p.max_sel, (uint32_t)p.max_sel * 4u);
+    lds_dma_b32(rl, (uint32_t)lane * 4u, (uint32_t)reinterpret_cast<uintptr_t>(LDS_PTR(unsigned char, smem)) +
+                                             kPBOff + 256u * (uint32_t)wave);
   }
 
   // Q^T fragments of this lane's row (d = 16*dc + 8*g + [0, 8)).  Without
@@ -569,6 +577,11 @@ void attn_pair_kernel(PairParams p) {
         lfirst = lane < p.max_sel ? out[lane] : -1;
         lst = out;
       }
+    }
+    if (list_wave) {
+      // the list copy, not the Q copies issued after it
+      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      lfirst = *reinterpret_cast<const int *>(smem + kPBOff + 256 * wave + 4 * lane);
     }
     if (wave == 0 || (wave == 1 && hasB))
       pair_compact(p, lst, __builtin_amdgcn_readfirstlane(lcnt), lfirst, wave ? LB : LA, cnt + 3 + wave,
