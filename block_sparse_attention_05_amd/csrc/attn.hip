@@ -918,6 +918,7 @@ hipError_t launch_attn_sparse_spark(const AttnArgs &a, hipStream_t stream) {
   if (a.nvq <= 0) return hipSuccess;
   if (a.nvb > kMaxRouteBlocks || a.sum_k == nullptr || a.sum_v == nullptr || a.sum_lm == nullptr)
     return hipErrorInvalidValue;
+  if (a.max_sel <= kMaxPairSparkList) return launch_attn_pair_spark(a, stream);
   Params p = make_params(a, 0, a.nvq);
   p.row_hi = a.rows_end;
   const int total = a.B * a.H * a.nvq;

@@ -105,7 +105,25 @@ constexpr int kPARkOff = kSHOff + kListBytes;
 constexpr int kPBRkOff = kPARkOff + kListBytes;
 constexpr int kSHRkOff = kPBRkOff + kListBytes;
 constexpr int kMrgOff = kSHRkOff + kListBytes;          // kMaxPairEntries x int2
-static_assert(kMrgOff + 8 * kMaxPairEntries <= kPVOff, "build temporaries must fit the K ring");
+// Approximate branch: one byte per video block and query block (A | B),
+// marking the list's blocks while the virtual keys are packed.
+constexpr int kVFlagOff = kMrgOff + 8 * kMaxPairEntries;
+static_assert(kVFlagOff + 2 * kMaxRouteBlocks <= kPVOff, "build temporaries must fit the K ring");
+// Approximate branch: the packed virtual keys of A and B (the video blocks
+// each list skips, ascending), 16-bit block indices after the counts.
+constexpr int kPVrowOff = kPLdsBytes;
+constexpr int kPSparkBytes = 2 * kMaxRouteBlocks * 2;
+// Entry encodings of virtual tiles: virtual tile v of block A is the block
+// kVBlkA + v in the merged list and the first key kVirtA + 64 v in the
+// schedule (B: kVBlkB, kVirtB).  Both key bases lie past every T, so the
+// "key >= T: no exact tile" tests skip them; the virtual key at packed
+// position x of block A has key kVirtA + x.
+constexpr int kVBlkA = 1 << 20, kVBlkB = 1 << 21;
+constexpr int kVirtA = 1 << 29, kVirtB = (1 << 29) + (1 << 27);
+constexpr int kVirtBit = 1 << 29;           // set in every virtual key, clear below kVirtA
+constexpr int kVirtPosMask = (1 << 27) - 1; // packed position of a virtual key
+static_assert(2 * kMaxPairSparkList + kMaxRouteBlocks / kBlock <= kMaxPairEntries,
+              "two disjoint lists and the virtual pairs must fit the schedule");
 
 // Fused route: the two query blocks' pooled means (fp64), their scores and
 // their selected lists, inside the V ring (unused until the first tile
@@ -137,6 +155,10 @@ struct PairParams {
   const float *kbar;
   int budget, radius;
   int32_t *list_out, *cnt_out;
+  // approximate branch: summaries of (b, h) at sum_k/sum_v + bh*nb*128 and
+  // sum_lm + bh*nb
+  const uint16_t *sum_k, *sum_v;
+  const float *sum_lm;
 };
 
 // Lanes below this one whose bit is set in m.
@@ -261,7 +283,7 @@ __device__ __forceinline__ void pair_classify(const int *own, int n_own, const i
 // order (pass 2), then sorted into the three phases, stable in that order.
 // Leftover private entries (one list longer than the other) follow all
 // others; they are general-phase entries anyway.
-__device__ __forceinline__ void pair_emit(const PairParams &p, unsigned char *smem, int lane) {
+__device__ __forceinline__ void pair_emit(const PairParams &p, unsigned char *smem, int lane, bool spark) {
   const int *PA = reinterpret_cast<const int *>(smem + kPAOff);
   const int *PB = reinterpret_cast<const int *>(smem + kPBlOff);
   const int *SH = reinterpret_cast<const int *>(smem + kSHOff);
@@ -278,11 +300,20 @@ __device__ __forceinline__ void pair_emit(const PairParams &p, unsigned char *sm
   const bool biased = p.key_bias != nullptr;
   const int nX = nPA > nPB ? nPA : nPB;
   const int nMin = nPA < nPB ? nPA : nPB;
-  const int nC = nX + nS;
+  const int nC0 = nX + nS;
+  // approximate branch: virtual tiles of A and B (cnt[9], cnt[10] virtual
+  // keys), appended as private pairs after the exact entries
+  const int nvA = spark ? __builtin_amdgcn_readfirstlane(cnt[9]) : 0;
+  const int nvB = spark ? __builtin_amdgcn_readfirstlane(cnt[10]) : 0;
+  const int tA = (nvA + kBlock - 1) / kBlock, tB = (nvB + kBlock - 1) / kBlock;
+  const int nC = nC0 + (tA > tB ? tA : tB);
   const bool unsorted = __builtin_amdgcn_readfirstlane(cnt[8]) != 0;
   for (int cb = 0; cb < nC; cb += 64) {
     const int c = cb + lane;
-    if (c < nC) {
+    if (c >= nC0 && c < nC) {
+      const int v = c - nC0;
+      mrg[c] = make_int2(v < tA ? kVBlkA + v : -1, v < tB ? kVBlkB + v : -1);
+    } else if (c < nC) {
       int a, b, r;
       if (c < nX) {
         a = c < nPA ? PA[c] : -1;
@@ -302,8 +333,18 @@ __device__ __forceinline__ void pair_emit(const PairParams &p, unsigned char *sm
     b = v.y;
   };
   // entries are stored as the first key of each block's tile (T: no tile)
-  auto first_key = [&](int x) -> int { return x < 0 ? p.T : x * kBlock; };
+  auto first_key = [&](int x) -> int {
+    if (x < 0) return p.T;
+    if (x >= kVBlkB) return kVirtB + kBlock * (x - kVBlkB);
+    if (x >= kVBlkA) return kVirtA + kBlock * (x - kVBlkA);
+    return x * kBlock;
+  };
   auto phase = [&](int a, int b) -> int {
+    if (a >= kVBlkA || b >= kVBlkA) {   // virtual: biased by the log-mass
+      const bool fa = a >= kVBlkA && kBlock * (a - kVBlkA + 1) <= nvA;
+      const bool fb = b >= kVBlkB && kBlock * (b - kVBlkB + 1) <= nvB;
+      return fa && fb ? 1 : 2;
+    }
     if (a < 0 || b < 0 || a == partial || b == partial) return 2;
     if (biased && (a >= p.nvb || b >= p.nvb)) return 1;
     return 0;
@@ -356,10 +397,10 @@ __device__ __forceinline__ void pair_emit(const PairParams &p, unsigned char *sm
   }
 }
 
-template <bool kDense, bool kFused>
+template <bool kDense, bool kFused, bool kSpark = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_pair_kernel(PairParams p) {
-  __shared__ __align__(16) unsigned char smem[kPLdsBytes];
+  __shared__ __align__(16) unsigned char smem[kPLdsBytes + (kSpark ? kPSparkBytes : 0)];
 
   const int total = p.B * p.H * p.npair * p.nsplit;
   const int w = kDense ? xcd_remap(blockIdx.x, total) : pair_order(blockIdx.x, total, p.npair, p.slots);
@@ -608,8 +649,36 @@ void attn_pair_kernel(PairParams p) {
                         cnt + 8, lane);
       }
     }
+    if (kSpark && wave < 2) {
+      // Approximate branch: the video blocks this wave's list skips, packed
+      // ascending (a missing block B has none): a byte flag per video block
+      // marks the list's entries, then a ballot per 64-block chunk packs the
+      // unflagged ones.
+      unsigned char *fl = smem + kVFlagOff + wave * kMaxRouteBlocks;
+      uint16_t *vr = reinterpret_cast<uint16_t *>(smem + kPVrowOff) + wave * kMaxRouteBlocks;
+      const int *L = reinterpret_cast<const int *>(smem + (wave ? kLBOff : kLAOff));
+      const int nL = (wave == 0 || hasB) ? __builtin_amdgcn_readfirstlane(cnt[3 + wave]) : 0;
+      for (int x = lane; 4 * x < p.nvb; x += 64) reinterpret_cast<uint32_t *>(fl)[x] = 0u;
+      wave_lds_sync();
+      for (int cb = 0; cb < nL; cb += 64) {
+        const int e = cb + lane < nL ? L[cb + lane] : -1;
+        if (e >= 0 && e < p.nvb) fl[e] = 1;
+      }
+      wave_lds_sync();
+      int nv = 0;
+      if (wave == 0 || hasB) {
+        for (int cb = 0; cb < p.nvb; cb += 64) {
+          const int x = cb + lane;
+          const bool skip = x < p.nvb && fl[x] == 0;
+          const uint64_t m = __ballot(skip);
+          if (skip) vr[nv + lanes_below(m)] = (uint16_t)x;
+          nv += __popcll(m);
+        }
+      }
+      if (lane == 0) cnt[9 + wave] = nv;
+    }
     __syncthreads();
-    if (wave == 0) pair_emit(p, smem, lane);
+    if (wave == 0) pair_emit(p, smem, lane, kSpark);
     read_q();
     // all waves have their Q before the first tile copies refill the V ring
     __syncthreads();
@@ -653,12 +722,23 @@ void attn_pair_kernel(PairParams p) {
 
   // ---- loads --------------------------------------------------------------
   // entries from this index on carry key_bias on their sink tiles
-  const int bias_from = has_bias ? nU : 0x7fffffff;
+  const int bias_from = (has_bias || kSpark) ? nU : 0x7fffffff;
   const i32x4s rk = buffer_rsrc(p.k + bbase, slab);
   const i32x4s rv = buffer_rsrc(p.v + bbase, slab);
   const float *kbias = has_bias ? p.key_bias + (int64_t)b * T : nullptr;
   const i32x4s rb = buffer_rsrc(kbias ? (const void *)kbias : (const void *)p.k, kbias ? T * 4u : 0u);
   const int sink0 = p.nvb * kBlock;
+  // approximate branch: summary rows are 256 B apart in one (b, h) slab of
+  // nb rows; log-masses 4 B apart
+  const int64_t sbase = (int64_t)bh * p.nb;
+  const i32x4s rsk = buffer_rsrc(kSpark ? p.sum_k + sbase * kHeadDim : p.k, kSpark ? (uint32_t)p.nb * 256u : 0u);
+  const i32x4s rsv = buffer_rsrc(kSpark ? p.sum_v + sbase * kHeadDim : p.v, kSpark ? (uint32_t)p.nb * 256u : 0u);
+  const i32x4s rlm = buffer_rsrc(kSpark ? (const void *)(p.sum_lm + sbase) : (const void *)p.k,
+                                 kSpark ? (uint32_t)p.nb * 4u : 0u);
+  const int *cntp = reinterpret_cast<const int *>(smem + kPCntOff);
+  const int nvA = kSpark && !kDense ? __builtin_amdgcn_readfirstlane(cntp[9]) : 0;
+  const int nvB = kSpark && !kDense ? __builtin_amdgcn_readfirstlane(cntp[10]) : 0;
+  const uint16_t *vrow = reinterpret_cast<const uint16_t *>(smem + kPVrowOff);
   // LDS tile layout: the one-block kernel's.  A 64-key slot is 16 blocks of
   // 1 KiB; block 2*kg + hf holds keys 8*kg .. +7 (kg = 0..7) and bytes
   // 128*hf .. +127 of each key row, in 16-byte pieces (key k' = key%8, chunk
@@ -677,8 +757,24 @@ void attn_pair_kernel(PairParams p) {
   const uint32_t v_lane = row_lane + 16u * (uint32_t)((lane & 7) ^ (2 * ((lane >> 3) & 3)));
   const uint32_t lds_w = lds0 + 2048u * (uint32_t)wave;
   // (B's tile is copied when it is its own: kB != kA)
+  // Approximate branch: a virtual half tile gathers the summary rows of its
+  // 32 virtual keys (packed positions key - kVirtX .. +31, past the count:
+  // row 0, masked), key group w by wave w, in the exact tiles' LDS layout.
+  const uint32_t sw_k = 16u * (chk ^ (uint32_t)(wave & 1));
+  const uint32_t sw_v = 16u * (uint32_t)((lane & 7) ^ (2 * ((lane >> 3) & 3)));
+  const int vrow_lane = 8 * wave + (lane >> 3);
+  auto vrow_of = [&](int isB, int key) -> uint32_t {
+    const int pos = (key & kVirtPosMask) + vrow_lane;
+    const int nv = isB ? nvB : nvA;
+    return (uint32_t)vrow[isB * kMaxRouteBlocks + (pos < nv ? pos : 0)];
+  };
   auto issue_k = [&](int kA, int kB, int slot) {
     const uint32_t l = lds_w + kPKOff + (uint32_t)(slot * 16384);
+    if (kSpark && ((kA | kB) & kVirtBit) != 0) {
+      if (kA & kVirtBit) lds_dma_b128_x2<0>(rsk, 0u, vrow_of(0, kA) * 256u + sw_k, l);
+      if (kB & kVirtBit) lds_dma_b128_x2<8192>(rsk, 0u, vrow_of(1, kB) * 256u + sw_k, l);
+      return;
+    }
     const int kb = kB == kA ? T : kB;
     if (kA < T) lds_dma_b128_x2<0>(rk, (uint32_t)kA * (uint32_t)row_bytes, k_lane, l);
     if (kb < T) lds_dma_b128_x2<8192>(rk, (uint32_t)kb * (uint32_t)row_bytes, k_lane, l);
@@ -687,6 +783,22 @@ void attn_pair_kernel(PairParams p) {
   // bias_from (the biased and general phases with key_bias)
   auto issue_v = [&](int kA, int kB, int slot, int e_tile) {
     const uint32_t l = lds_w + kPVOff + (uint32_t)(slot * 16384);
+    if (kSpark && ((kA | kB) & kVirtBit) != 0) {
+      if (kA & kVirtBit) lds_dma_b128_x2<0>(rsv, 0u, vrow_of(0, kA) * 256u + sw_v, l);
+      if (kB & kVirtBit) lds_dma_b128_x2<8192>(rsv, 0u, vrow_of(1, kB) * 256u + sw_v, l);
+      // log-masses of both half tiles (lanes 0-31: A's keys, 32-63: B's);
+      // past a block's count or for a missing block they read as zero (the
+      // masked step sets those logits to -inf)
+      if (wave == 0) {
+        const int isB = lane >> 5;
+        const int k0 = isB ? kB : kA;
+        const int pos = (k0 & kVirtPosMask) + (lane & 31);
+        const bool ok = (k0 & kVirtBit) != 0 && pos < (isB ? nvB : nvA);
+        const uint32_t idx = vrow[isB * kMaxRouteBlocks + (ok ? pos : 0)];
+        lds_dma_b32(rlm, ok ? idx * 4u : (uint32_t)p.nb * 4u, lds0 + kPBOff + (uint32_t)(slot * 256));
+      }
+      return;
+    }
     const int kb = kB == kA ? T : kB;
     if (kA < T) lds_dma_b128_x2<0>(rv, (uint32_t)kA * (uint32_t)row_bytes, v_lane, l);
     if (kb < T) lds_dma_b128_x2<8192>(rv, (uint32_t)kb * (uint32_t)row_bytes, v_lane, l);
@@ -843,11 +955,14 @@ void attn_pair_kernel(PairParams p) {
       dma_k();
       dma_v();
       if (DO_QK) qk();
-      if (my_key >= T) return;     // this wave's block has no tile in this step
+      // a virtual tile's keys end at its block's virtual key count
+      const bool virt = kSpark && my_key >= kVirtA;
+      if (!virt && my_key >= T) return;     // this wave's block has no tile in this step
+      const int lim = !virt ? T : my_key >= kVirtB ? kVirtB + nvB : kVirtA + nvA;
       const int kbase = my_key + 4 * g;   // key of s[r] = kbase + 8*(r/4) + r%4
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        if (kbase + 8 * (r >> 2) + (r & 3) >= T) s_cur[r] = -INFINITY;
+        if (kbase + 8 * (r >> 2) + (r & 3) >= lim) s_cur[r] = -INFINITY;
       rescale(tile_max());
       exps(m_used == -INFINITY ? 0.f : m_used, l_run);
       pv();
@@ -1001,7 +1116,7 @@ void attn_pair_kernel(PairParams p) {
   const int nUB = nU + nBi;
   for (; e < nU && e + 1 < nE; ++e) run_entry(Bool<false>{}, Bool<false>{}, e);
   for (; e < nUB && e + 1 < nE; ++e) run_entry(Bool<true>{}, Bool<false>{}, e);
-  if (has_bias) {
+  if (has_bias || kSpark) {
     for (; e + 1 < nE; ++e) run_entry(Bool<true>{}, Bool<true>{}, e);
   } else {
     for (; e + 1 < nE; ++e) run_entry(Bool<false>{}, Bool<true>{}, e);
@@ -1009,7 +1124,7 @@ void attn_pair_kernel(PairParams p) {
   if (e < nE) {
     if (e < nU) last_entry(Bool<false>{}, Bool<false>{}, e);
     else if (e < nUB) last_entry(Bool<true>{}, Bool<false>{}, e);
-    else if (has_bias) last_entry(Bool<true>{}, Bool<true>{}, e);
+    else if (has_bias || kSpark) last_entry(Bool<true>{}, Bool<true>{}, e);
     else last_entry(Bool<false>{}, Bool<true>{}, e);
   }
 
@@ -1181,6 +1296,22 @@ hipError_t launch_attn_pair_sparse(const AttnArgs &a, hipStream_t stream) {
   p.slots = pair_slots_per_xcd();
   const int total = a.B * a.H * p.npair;
   hipLaunchKernelGGL((attn_pair_kernel<false, false>), dim3(total), dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_pair_spark(const AttnArgs &a, hipStream_t stream) {
+  if (a.nvq <= 0) return hipSuccess;
+  if (a.max_sel > kMaxPairSparkList || a.nvb > kMaxRouteBlocks || a.sum_k == nullptr || a.sum_v == nullptr ||
+      a.sum_lm == nullptr)
+    return hipErrorInvalidValue;
+  PairParams p = make_pair_params(a, 0, a.nvq);
+  p.row_hi = a.rows_end;
+  p.slots = pair_slots_per_xcd();
+  p.sum_k = static_cast<const uint16_t *>(a.sum_k);
+  p.sum_v = static_cast<const uint16_t *>(a.sum_v);
+  p.sum_lm = a.sum_lm;
+  const int total = a.B * a.H * p.npair;
+  hipLaunchKernelGGL((attn_pair_kernel<false, false, true>), dim3(total), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

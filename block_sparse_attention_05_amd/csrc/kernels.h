@@ -25,6 +25,10 @@ constexpr int kMaxRouteBlocks = 1024;  // widest per-row sort in the route kerne
 // Longest list (max_sel) the paired-block attention kernel serves; longer
 // lists take the one-block kernel.
 constexpr int kMaxPairList = 512;
+// Largest lists the paired kernel takes with the approximate branch: two
+// fully disjoint lists plus one virtual pair per 64 video blocks fit its
+// schedule of 2 * kMaxPairList entries.
+constexpr int kMaxPairSparkList = kMaxPairList - kMaxRouteBlocks / 128;
 
 // Means of the routed blocks: Q blocks [0, nvq) over rows below q_end (a
 // split last block only over its real rows), K blocks [0, nvb), in the route
@@ -87,6 +91,10 @@ hipError_t launch_attn_pair_sparse(const AttnArgs &a, hipStream_t stream);
 // kMaxRouteBlocks): every workgroup scores both query blocks against the
 // pooled key means and selects their lists (the route kernel's rule).
 hipError_t launch_attn_pair_fused(const AttnArgs &a, hipStream_t stream);
+// The approximate branch on paired query blocks (needs max_sel <=
+// kMaxPairSparkList, nvb <= kMaxRouteBlocks): the virtual tiles of A and B
+// run as private pairs after the exact tiles.
+hipError_t launch_attn_pair_spark(const AttnArgs &a, hipStream_t stream);
 hipError_t launch_attn_pair_dense(const AttnArgs &a, float *part_o, float *part_ml, int nsplit,
                                   hipStream_t stream);
 int dense_pair_splits(int B, int H, int nb, int nvb);

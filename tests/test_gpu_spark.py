@@ -164,12 +164,10 @@ def test_spark_no_bias_split_block():
 
 
 def test_spark_ratio_one_equals_exact():
-    """Nothing skipped: every virtual key is masked, so the result is the
-    exact path's up to the summation order of the tiles and the points where
-    the running max is rescaled (the approximate branch serves one query
-    block per workgroup, sparse_attn_fwd two), within the oracle tolerance.
-    One leaked virtual key would carry about a block's worth of mass and move
-    LSE and outputs by several hundredths."""
+    """Nothing skipped: no virtual tile, so the approximate branch walks the
+    exact path's tiles in the same order on the same paired kernel and
+    gives the same bits.  One leaked virtual key would carry about a
+    block's worth of mass and move LSE and outputs by several hundredths."""
     import block_sparse_attention_05_amd as sa
     q, k, v, ss = _split_case(seed=12)
     qc, kc, vc = q.cuda(), k.cuda(), v.cuda()
@@ -185,7 +183,41 @@ def test_spark_ratio_one_equals_exact():
     d = (a[:, :rows].float() - b[:, :rows].float()).abs().max().item()
     dl = (lse_a[:, :, :rows] - lse_b[:, :, :rows]).abs().max().item()
     log(f"[spark ratio 1] vs exact path: out max_abs={d:.3e} lse max_abs={dl:.3e}")
-    assert d <= 1e-2 and dl <= 1e-2
+    assert torch.equal(a[:, :rows], b[:, :rows]) and torch.equal(lse_a[:, :, :rows], lse_b[:, :, :rows])
+
+
+def test_spark_one_block_kernel_wide_lists():
+    """Lists wider than the paired kernel takes with the approximate branch
+    (the same entries, -1 up to 512 per list) run on the one-block kernel:
+    every output and LSE element of the sparse rows against the oracle, and
+    within the tolerance of the paired kernel's."""
+    import block_sparse_attention_05_amd as sa
+    from gpu_helpers import pad_lists
+    q, k, v, ss = _split_case(seed=31)
+    bias = workloads.sink_key_bias(1, q.shape[1], ss, seed=32)
+    qc, kc, vc, kb = q.cuda(), k.cuda(), v.cuda(), bias.cuda()
+    ratio, radius = 0.2, 1
+    pair_out, pair_lse, parts = sa.routed_attention_spark(qc, kc, vc, ss, ratio, radius, key_bias=kb,
+                                                         return_lse=True, return_parts=True)
+    idx, cnt, summ = parts["block_idx"], parts["block_cnt"], parts["summaries"]
+    wide, wcnt = pad_lists(idx, cnt, [], [], 512)
+    lse = torch.zeros_like(pair_lse)
+    out = sa.sparse_attn_fwd_spark(qc, kc, vc, ss, wide, wcnt, summ, key_bias=kb, lse=lse)
+    torch.cuda.synchronize()
+    rows = 64 * (ss // 64)
+    qn, kn, vn = to_np(q), to_np(k), to_np(v)
+    rt = ora.route(qn, kn, ss, ratio, radius)
+    adopt_lists(idx.cpu(), cnt.cpu(), rt)
+    ak, av, lm = (x.cpu() for x in summ)
+    want, want_lse, _ = osp.routed_attention_spark(qn, kn, vn, ss, ratio, radius,
+                                                   (to_np(ak), to_np(av), lm.numpy().astype(np.float64)),
+                                                   key_bias=bias.numpy(), rt=rt)
+    mx, mean = err_stats(to_np(out)[:, :rows], want[:, :rows])
+    lmx, _ = err_stats(lse.cpu().numpy()[:, :, :rows], want_lse[:, :, :rows])
+    d = (out[:, :rows].float() - pair_out[:, :rows].float()).abs().max().item()
+    log(f"[spark one-block] out max_abs={mx:.3e} mean_abs={mean:.3e} lse max_abs={lmx:.3e}; "
+        f"vs paired kernel max_abs={d:.3e}")
+    assert mx <= MAX_ABS and mean <= MEAN_ABS and lmx <= 1e-2 and d <= MAX_ABS
 
 
 def test_spark_h3_full():
