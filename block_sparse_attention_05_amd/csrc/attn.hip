@@ -1,7 +1,9 @@
 // Block-sparse flash attention on gfx950 bf16 MFMA, one query block per
-// workgroup.  It serves the approximate branch (virtual summary keys) and
-// block lists longer than the paired kernel (attn_pair.hip) takes; the plain
-// sparse rows, the dense rows and the fused route run on the paired kernel.
+// workgroup.  It serves block lists longer than the paired kernel
+// (attn_pair.hip) takes (over 512 entries, or over 504 with the approximate
+// branch of virtual summary keys); the plain sparse rows, the dense rows,
+// the fused route and the approximate branch otherwise run on the paired
+// kernel.
 // This file also holds the combine kernel of the split-KV dense rows and the
 // launch dispatch between the two kernels.
 //

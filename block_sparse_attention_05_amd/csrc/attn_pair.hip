@@ -8,6 +8,15 @@
 // Contract: the natural-log key bias is converted to log2 units and consumed
 // only by the exact branch (sink keys).
 //
+// Approximate branch (the Spark page's virtual summaries merged into the
+// same accumulator, kSpark): each of the two blocks packs the video blocks
+// its list skips, ascending, into virtual tiles of 64 keys whose K and V
+// rows are the summaries ak, av of those blocks (gathered by block index)
+// and whose logits carry the log-mass lm as a natural-log bias.  Virtual
+// tiles run as private pairs (A's tile v with B's tile v) after the exact
+// tiles: full pairs with the biased tiles, a partial tile or a tile without
+// a partner with the general ones, masked at the block's virtual key count.
+//
 // Why pairs.  A 64-row query block does 2.1 MFLOP per 64-key tile against
 // 32 KiB of K/V copied from L2 into LDS, 64 FLOP per byte: at the MFMA rate
 // of a CU that is the whole global-to-LDS copy bandwidth of the CU.
