@@ -835,21 +835,52 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(Params p) {
   const int tq = (p.qb0 + qbi) * kBlock + row;
   if (tq < p.row_lo || tq >= p.row_hi) return;
   const int64_t prow0 = (int64_t)wq * p.nsplit * kBlock + row;   // split s: prow0 + s * kBlock
+  // Up to kCombineRegs splits are loaded at once (one memory round trip),
+  // then merged in split order; more splits take a second pass per group.
+  constexpr int kCombineRegs = 4;
   float m = -INFINITY;
-  for (int s = 0; s < p.nsplit; ++s) m = fmaxf(m, p.part_ml[2 * (prow0 + (int64_t)s * kBlock)]);
-  const float msub = (m == -INFINITY) ? 0.f : m;
   float l = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s = 0; s < p.nsplit; ++s) {
-    const int64_t prow = prow0 + (int64_t)s * kBlock;
-    const float2 ml = *reinterpret_cast<const float2 *>(p.part_ml + 2 * prow);
-    const float4 po = *reinterpret_cast<const float4 *>(p.part_o + prow * kHeadDim + d0);
-    const float wgt = __builtin_amdgcn_exp2f(ml.x - msub);
-    l += wgt * ml.y;
-    acc.x += wgt * po.x;
-    acc.y += wgt * po.y;
-    acc.z += wgt * po.z;
-    acc.w += wgt * po.w;
+  if (p.nsplit <= kCombineRegs) {
+    float2 ml[kCombineRegs];
+    float4 po[kCombineRegs];
+#pragma unroll
+    for (int s = 0; s < kCombineRegs; ++s) {
+      if (s < p.nsplit) {
+        const int64_t prow = prow0 + (int64_t)s * kBlock;
+        ml[s] = *reinterpret_cast<const float2 *>(p.part_ml + 2 * prow);
+        po[s] = *reinterpret_cast<const float4 *>(p.part_o + prow * kHeadDim + d0);
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < kCombineRegs; ++s)
+      if (s < p.nsplit) m = fmaxf(m, ml[s].x);
+    const float msub = (m == -INFINITY) ? 0.f : m;
+#pragma unroll
+    for (int s = 0; s < kCombineRegs; ++s) {
+      if (s < p.nsplit) {
+        const float wgt = __builtin_amdgcn_exp2f(ml[s].x - msub);
+        l += wgt * ml[s].y;
+        acc.x += wgt * po[s].x;
+        acc.y += wgt * po[s].y;
+        acc.z += wgt * po[s].z;
+        acc.w += wgt * po[s].w;
+      }
+    }
+  } else {
+    for (int s = 0; s < p.nsplit; ++s) m = fmaxf(m, p.part_ml[2 * (prow0 + (int64_t)s * kBlock)]);
+    const float msub = (m == -INFINITY) ? 0.f : m;
+    for (int s = 0; s < p.nsplit; ++s) {
+      const int64_t prow = prow0 + (int64_t)s * kBlock;
+      const float2 ml = *reinterpret_cast<const float2 *>(p.part_ml + 2 * prow);
+      const float4 po = *reinterpret_cast<const float4 *>(p.part_o + prow * kHeadDim + d0);
+      const float wgt = __builtin_amdgcn_exp2f(ml.x - msub);
+      l += wgt * ml.y;
+      acc.x += wgt * po.x;
+      acc.y += wgt * po.y;
+      acc.z += wgt * po.z;
+      acc.w += wgt * po.w;
+    }
   }
   const float inv = l > 0.f ? 1.f / l : 0.f;
   uint16_t *op = p.out + (int64_t)b * T * rs + (int64_t)tq * rs + h * kHeadDim + d0;
