@@ -52,7 +52,7 @@ HBM_PEAK_GBPS = 8000.0
 METRIC = "ms/call and effective TFLOP/s (frac of bf16 peak), B1 H56 T9505 D128 top-k 0.1"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_pair_sparse_h3_traffic.json")
 ATTN_SRC = os.path.join(ROOT, "block_sparse_attention_05_amd", "csrc", "attn_pair.hip")
-SPARSE_KERNEL = "attn_pair_kernel<false, false>"
+SPARSE_KERNEL = "attn_pair_kernel<false, false, false>"
 
 
 def effective_flops_from_lists(cnt, idx, T, nvb, H, B):
