@@ -220,7 +220,7 @@ def cpu_baseline(wl, heads):
     flops = ora.effective_flops(T, heads, 1, rt.lists(), rt.nvb)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"oracle routed_attention (pool+route+sparse+dense, float64 arithmetic, "
-                      f"stricter than the fp32 the path is judged against) on heads 0..{heads - 1} "
+                      f"stricter than the fp32 the tolerances are stated for) on heads 0..{heads - 1} "
                       f"of the same workload ({flops / 1e9:.1f} effective GFLOP in {dt:.1f} s)",
             "blas_threads": int(threads), "os_cpu_count": os.cpu_count(),
             "torch_threads": torch.get_num_threads(), "seconds": dt}
